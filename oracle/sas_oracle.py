@@ -1,0 +1,488 @@
+"""Plain, slow, fp64 CPU oracle for SAS gated block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with the
+HIP library and imports nothing from it.
+
+What it computes, and where the pages define it (page titles, then section /
+equation):
+
+  [picx]  picx.dev summary of "SAS: Simple Attention Sparsification" --
+          'Theoretical Foundation' Eq. 1-3, 'Key Idea: Differentiable Continuous
+          Gating' Eq. 4 and 9, 'Gradient Analysis' Eq. 5 and 6, 'Kernel Design'.
+  [daiwk] "SAS: End-to-end learning of sparse attention rankings from
+          language-model loss" (reproduction README) -- 'Core equations',
+          'Background and main changes' (flowchart), 'Scope'.
+  [evolve] "SAS: Simple Attention Sparsification via End-to-End Optimization of
+          Context Ranking" (evolve.pub review) -- 'Summary', FAQ.
+
+Per row r = (batch b, KV head kv, query block t), with valid history length C_t:
+  1. scores s_m for history blocks m < C_t (given, or the mean-pool stand-in:
+     pooled query block . pooled key block / sqrt(d));
+  2. gate normaliser lse_s = log sum_{m<C_t} exp(s_m); log g_m = s_m - lse_s
+     ([picx] Eq. 6; the current block keeps g0 = 1, i.e. bias 0, Eq. 4);
+  3. I = Top-K(s): the min(K, C_t) history blocks of largest s, equal scores
+     going to the lower block index, emitted in ascending order ([picx] Eq. 3);
+  4. keys J_i = union of the selected blocks and the causal prefix of the
+     current block; bias log g_m on block m, 0 on the current block;
+  5. o_i = softmax_j(q_i . k_j * scale + bias_j) v_j, scale = 1/sqrt(d)
+     ([daiwk] 'Core equations'; [picx] Eq. 9);
+  6. gradients of L = sum dO . o: dq, dk, dv, d(log g) summed per selected block
+     ([picx] Eq. 5, inner gating), and ds through the gate softmax of step 2;
+  7. decode: the same for a single query token at position L - 1.
+
+Readings taken where the pages leave a step open are listed in the design doc of
+the repository (all-history softmax domain, token-causal current block, one
+selection per KV head shared by its query heads, decode position L - 1, ...).
+
+Arithmetic: float64 throughout, except where a floating-point value decides an
+integer (the Top-K ranking): that decision is taken on fp32 scores, the
+precision the scores are stored in, exactly as the device library takes it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+import torch
+
+
+# --------------------------------------------------------------------------- helpers
+
+def _np64(x) -> np.ndarray:
+    """Any torch tensor (incl. bf16) or array-like -> float64 numpy array."""
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _rows(x, J: np.ndarray) -> np.ndarray:
+    """x[J] along the first axis as float64 (x a torch tensor or an array)."""
+    if isinstance(x, torch.Tensor):
+        return _np64(x[torch.from_numpy(np.asarray(J, dtype=np.int64))])
+    return _np64(np.asarray(x)[J])
+
+
+def _npint(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        return x.detach().cpu().numpy().astype(np.int64)
+    return np.asarray(x, dtype=np.int64)
+
+
+def n_blocks(n: int, bs: int) -> int:
+    return -(-n // bs)
+
+
+def block_span(m: int, bs: int, n: int):
+    """Token range [lo, hi) of block B_m; the last block may be partial."""
+    return m * bs, min((m + 1) * bs, n)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def to_f32(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to fp32 (round to nearest even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> torch.Tensor:
+    """fp32 -> bf16 with round to nearest even (torch's conversion)."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------- (1) scores
+
+def pool_keys(k, bs: int) -> np.ndarray:
+    """kbar[b,kv,m] = mean of k over the valid tokens of block B_m (float64).
+
+    Stand-in for the pages' "pooling-based block summaries" ([evolve] FAQ)."""
+    k = _np64(k)
+    b, hkv, n, d = k.shape
+    out = np.empty((b, hkv, n_blocks(n, bs), d))
+    for m in range(out.shape[2]):
+        lo, hi = block_span(m, bs, n)
+        out[:, :, m] = k[:, :, lo:hi].mean(axis=2)
+    return out
+
+
+def pool_queries(q, hkv: int, bs: int) -> np.ndarray:
+    """qbar[b,kv,t] = mean of q over the G query heads of KV head kv and over the
+    valid tokens of query block t (float64)."""
+    q = _np64(q)
+    b, hq, n, d = q.shape
+    g = hq // hkv
+    out = np.empty((b, hkv, n_blocks(n, bs), d))
+    for kv in range(hkv):
+        heads = q[:, kv * g:(kv + 1) * g]
+        for t in range(out.shape[2]):
+            lo, hi = block_span(t, bs, n)
+            out[:, kv, t] = heads[:, :, lo:hi].mean(axis=(1, 2))
+    return out
+
+
+def history_len(t: int, row_offset: int, C: int) -> int:
+    """Valid history length of row t: C_t = min(t + row_offset, C)."""
+    return min(t + row_offset, C)
+
+
+def standin_scores(qbar32: np.ndarray, kbar32: np.ndarray, scale: float,
+                   C: int, row_offset: int = 0) -> np.ndarray:
+    """s[b,kv,t,m] = (qbar . kbar) * scale for m < C_t, rounded to fp32; 0 elsewhere.
+
+    qbar32 [b,kv,T,d] and kbar32 [b,kv,>=C,d] are the fp32 pooled summaries; the
+    dot product is evaluated in float64 and rounded once to fp32."""
+    qb = np.asarray(qbar32, dtype=np.float64)
+    kb = np.asarray(kbar32, dtype=np.float64)[:, :, :C]
+    b, hkv, T, _ = qb.shape
+    s = np.zeros((b, hkv, T, C), dtype=np.float32)
+    for t in range(T):
+        ct = history_len(t, row_offset, C)
+        if ct == 0:
+            continue
+        dots = np.einsum("bkd,bkmd->bkm", qb[:, :, t], kb[:, :, :ct])
+        s[:, :, t, :ct] = to_f32(dots * scale)
+    return s
+
+
+# --------------------------------------------------------------------------- (2)+(3) gates, Top-K
+
+def gate_normaliser(s_row: np.ndarray) -> float:
+    """lse_s = log sum_m exp(s_m) over the valid history, shifted by the max."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    if s_row.size == 0:
+        return -math.inf
+    if not np.all(np.isfinite(s_row)):
+        raise ValueError("selector scores must be finite on the valid history")
+    mx = s_row.max()
+    return float(mx + math.log(np.exp(s_row - mx).sum()))
+
+
+def topk_history(s_row32: np.ndarray, K: int) -> np.ndarray:
+    """Indices of the min(K, C) largest scores, ranked by (score descending,
+    index ascending), returned in ascending index order.
+
+    The comparison is on the fp32 values (equal fp32 values tie; -0.0 == +0.0)."""
+    s_row = np.asarray(s_row32, dtype=np.float32).astype(np.float64)
+    C = s_row.size
+    if C == 0 or K <= 0:
+        return np.zeros(0, dtype=np.int64)
+    # lexsort: last key is primary.  -s ascending == s descending; ties -> index.
+    order = np.lexsort((np.arange(C), -s_row))
+    return np.sort(order[:min(K, C)])
+
+
+def select_topk(s, K: int, row_offset: int = 0, C: Optional[int] = None):
+    """Selection for every row of s [b,kv,T,>=C] (fp32 values).
+
+    Returns idx int64 [b,kv,T,K] (ascending, -1 padded), logg float64
+    [b,kv,T,K] (0 on pads) and lse_s float64 [b,kv,T] (-inf when C_t = 0)."""
+    s = np.asarray(s.detach().cpu().numpy() if isinstance(s, torch.Tensor) else s,
+                   dtype=np.float32)
+    b, hkv, T = s.shape[:3]
+    C = s.shape[3] if C is None else C
+    idx = np.full((b, hkv, T, K), -1, dtype=np.int64)
+    logg = np.zeros((b, hkv, T, K))
+    lse_s = np.full((b, hkv, T), -math.inf)
+    for bb in range(b):
+        for kv in range(hkv):
+            for t in range(T):
+                ct = history_len(t, row_offset, C)
+                if ct == 0:
+                    continue
+                row = s[bb, kv, t, :ct]
+                lse = gate_normaliser(row)
+                sel = topk_history(row, K)
+                lse_s[bb, kv, t] = lse
+                idx[bb, kv, t, :sel.size] = sel
+                logg[bb, kv, t, :sel.size] = row[sel].astype(np.float64) - lse
+    return idx, logg, lse_s
+
+
+# --------------------------------------------------------------------------- (4)+(5) forward
+
+def key_set(t: int, idx_row, logg_row, bs: int, n: int, last_pos: Optional[int] = None):
+    """Key positions, biases and causal limits seen by query block t.
+
+    Returns (J, bias, slot, cur) where J are token positions (selected history
+    blocks in ascending block order, then the current block B_t), bias is the
+    log-gate of each key (0 on the current block, and 0 everywhere when
+    logg_row is None), slot[j] is the Top-K slot of the key's block (-1 for the
+    current block) and cur marks keys of the current block (to be causally
+    masked against the query position)."""
+    J, bias, slot, cur = [], [], [], []
+    for sl, m in enumerate(np.asarray(idx_row).tolist()):
+        if m < 0:
+            continue
+        if m >= t:
+            raise ValueError(f"selected block {m} is not history of block {t}")
+        lo, hi = block_span(m, bs, n)
+        J.extend(range(lo, hi))
+        bias.extend([0.0 if logg_row is None else float(logg_row[sl])] * (hi - lo))
+        slot.extend([sl] * (hi - lo))
+        cur.extend([False] * (hi - lo))
+    lo, hi = block_span(t, bs, n)
+    if last_pos is not None:
+        hi = min(hi, last_pos + 1)
+    J.extend(range(lo, hi))
+    bias.extend([0.0] * (hi - lo))
+    slot.extend([-1] * (hi - lo))
+    cur.extend([True] * (hi - lo))
+    return (np.asarray(J, dtype=np.int64), np.asarray(bias), np.asarray(slot, dtype=np.int64),
+            np.asarray(cur, dtype=bool))
+
+
+def _logits(qrows, pos, kj, J, bias, cur, scale):
+    """z[i, j] = q_i . k_j * scale + bias_j, -inf where a current-block key lies
+    after the query position."""
+    z = (qrows @ kj.T) * scale + bias[None, :]
+    future = cur[None, :] & (J[None, :] > pos[:, None])
+    return np.where(future, -np.inf, z)
+
+
+def _softmax_stats(z):
+    mx = z.max(axis=1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.exp(z - mx).sum(axis=1))
+    p = np.exp(z - lse[:, None])
+    return p, lse
+
+
+def fwd_row_block(q, k, v, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int):
+    """Forward of one row block: (o [G,rows,d], lse [G,rows], P list, J data)."""
+    hq, n = q.shape[1], q.shape[2]
+    g = hq // k.shape[1]
+    idx_row = _npint(idx[bb, kv, t])
+    logg_row = None if logg is None else _np64(logg[bb, kv, t])
+    J, bias, slot, cur = key_set(t, idx_row, logg_row, bs, n)
+    kj = _rows(k[bb, kv], J)
+    vj = _rows(v[bb, kv], J)
+    lo, hi = block_span(t, bs, n)
+    pos = np.arange(lo, hi)
+    os_, lses, ps = [], [], []
+    for h in range(kv * g, (kv + 1) * g):
+        z = _logits(_np64(q[bb, h, lo:hi]), pos, kj, J, bias, cur, scale)
+        p, lse = _softmax_stats(z)
+        os_.append(p @ vj)
+        lses.append(lse)
+        ps.append(p)
+    return np.stack(os_), np.stack(lses), ps, (J, bias, slot, cur, kj, vj)
+
+
+def attn_fwd(q, k, v, idx, logg, bs: int, scale: Optional[float] = None):
+    """o [b,hq,N,d] and LSE [b,hq,N] (float64) of gated block-sparse attention."""
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    o = np.zeros((b, hq, n, d))
+    lse = np.zeros((b, hq, n))
+    for bb in range(b):
+        for kv in range(hkv):
+            for t in range(n_blocks(n, bs)):
+                lo, hi = block_span(t, bs, n)
+                ob, lb, _, _ = fwd_row_block(q, k, v, idx, logg, bs, scale, bb, kv, t)
+                o[bb, kv * g:(kv + 1) * g, lo:hi] = ob
+                lse[bb, kv * g:(kv + 1) * g, lo:hi] = lb
+    return o, lse
+
+
+def attn_fwd_dense(q, k, v, idx, logg, bs: int, scale: Optional[float] = None):
+    """Second formulation for small inputs: materialise the whole N x N logit
+    matrix, put log g on selected history blocks, 0 on the causal part of the
+    current block and -inf everywhere else, then take a row softmax
+    ([picx] 'Kernel Design': masking non-selected blocks; [daiwk] 'Scope':
+    a dense-materialised reference)."""
+    q, k, v = _np64(q), _np64(k), _np64(v)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    idx = _npint(idx)
+    logg = None if logg is None else _np64(logg)
+    T = n_blocks(n, bs)
+    o = np.zeros_like(q)
+    lse = np.zeros((b, hq, n))
+    for bb in range(b):
+        for kv in range(hkv):
+            bias = np.full((n, n), -np.inf)
+            for t in range(T):
+                lo, hi = block_span(t, bs, n)
+                for sl in range(idx.shape[3]):
+                    m = idx[bb, kv, t, sl]
+                    if m < 0:
+                        continue
+                    mlo, mhi = block_span(m, bs, n)
+                    bias[lo:hi, mlo:mhi] = 0.0 if logg is None else logg[bb, kv, t, sl]
+                for i in range(lo, hi):
+                    bias[i, lo:i + 1] = 0.0
+            for h in range(kv * g, (kv + 1) * g):
+                z = q[bb, h] @ k[bb, kv].T * scale + bias
+                p, l = _softmax_stats(z)
+                o[bb, h] = p @ v[bb, kv]
+                lse[bb, h] = l
+    return o, lse
+
+
+# --------------------------------------------------------------------------- (6) backward
+
+def bwd_row_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int):
+    """Backward of one row block for L = sum dO . o.
+
+    Returns dq [G,rows,d], dlogg [K] (sum of dS over each selected block, all G
+    heads and all rows of the block), and the key-side contributions
+    (J, dk_J, dv_J) to be summed over row blocks."""
+    o, lse, ps, (J, bias, slot, cur, kj, vj) = fwd_row_block(q, k, v, idx, logg, bs, scale,
+                                                             bb, kv, t)
+    hq, n = q.shape[1], q.shape[2]
+    g = hq // k.shape[1]
+    K = idx.shape[3]
+    lo, hi = block_span(t, bs, n)
+    dq = np.zeros((g, hi - lo, kj.shape[1]))
+    dk_j = np.zeros_like(kj)
+    dv_j = np.zeros_like(vj)
+    dlogg = np.zeros(K)
+    for gi, h in enumerate(range(kv * g, (kv + 1) * g)):
+        p = ps[gi]
+        do = _np64(dout[bb, h, lo:hi])
+        qh = _np64(q[bb, h, lo:hi])
+        D = (do * o[gi]).sum(axis=1)                  # D_i = dO_i . o_i
+        dp = do @ vj.T                                # dP_ij = dO_i . v_j
+        ds_ = p * (dp - D[:, None])                   # dS_ij = p_ij (dP_ij - D_i)
+        dq[gi] = (ds_ @ kj) * scale
+        dk_j += (ds_.T @ qh) * scale
+        dv_j += p.T @ do
+        col = ds_.sum(axis=0)
+        for sl in range(K):
+            dlogg[sl] += col[slot == sl].sum()
+    return dq, dlogg, (J, dk_j, dv_j)
+
+
+def ds_row(s_row, lse_s: float, idx_row, dlogg_row) -> np.ndarray:
+    """Selector gradient over the whole valid history of a row:
+    ds_m = 1[m in I] dlogg_m - g_m * sum_{m' in I} dlogg_{m'}, g_m = exp(s_m - lse_s)
+    (derivative of log g_m = s_m - LSE(s), [picx] Eq. 6; Top-K carries none,
+    [picx] 'Theoretical Foundation')."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    gates = np.exp(s_row - lse_s)
+    ds = np.zeros_like(s_row)
+    total = 0.0
+    for sl, m in enumerate(np.asarray(idx_row).tolist()):
+        if m < 0:
+            continue
+        ds[m] += dlogg_row[sl]
+        total += dlogg_row[sl]
+    return ds - gates * total
+
+
+def attn_bwd(q, k, v, dout, idx, logg, s, lse_s, bs: int, scale: Optional[float] = None,
+             row_offset: int = 0):
+    """All gradients: dq [b,hq,N,d], dk/dv [b,hkv,N,d], dlogg [b,kv,T,K],
+    ds [b,kv,T,C] (0 where m >= C_t)."""
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    T = n_blocks(n, bs)
+    K = idx.shape[3]
+    s32 = np.asarray(s.detach().cpu().numpy() if isinstance(s, torch.Tensor) else s,
+                     dtype=np.float32)
+    C = s32.shape[3]
+    lse_s = _np64(lse_s)
+    dq = np.zeros((b, hq, n, d))
+    dk = np.zeros((b, hkv, n, d))
+    dv = np.zeros((b, hkv, n, d))
+    dlogg = np.zeros((b, hkv, T, K))
+    ds = np.zeros((b, hkv, T, C))
+    for bb in range(b):
+        for kv in range(hkv):
+            for t in range(T):
+                lo, hi = block_span(t, bs, n)
+                dqb, dl, (J, dkj, dvj) = bwd_row_block(q, k, v, dout, idx, logg, bs, scale,
+                                                       bb, kv, t)
+                dq[bb, kv * g:(kv + 1) * g, lo:hi] = dqb
+                dk[bb, kv, J] += dkj
+                dv[bb, kv, J] += dvj
+                dlogg[bb, kv, t] = dl
+                ct = history_len(t, row_offset, C)
+                if ct > 0:
+                    ds[bb, kv, t, :ct] = ds_row(s32[bb, kv, t, :ct], lse_s[bb, kv, t],
+                                                _npint(idx[bb, kv, t]), dl)
+    return {"dq": dq, "dk": dk, "dv": dv, "dlogg": dlogg, "ds": ds}
+
+
+def bwd_key_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, m: int):
+    """dk, dv on the tokens of key block B_m only: the sum over every row block
+    whose key set contains B_m (the blocks that selected m, and m itself)."""
+    n = q.shape[2]
+    T = n_blocks(n, bs)
+    lo, hi = block_span(m, bs, n)
+    idx_np = _npint(idx[bb, kv])
+    dk = np.zeros((hi - lo, q.shape[3]))
+    dv = np.zeros_like(dk)
+    for t in range(m, T):
+        if t != m and m not in idx_np[t].tolist():
+            continue
+        _, _, (J, dkj, dvj) = bwd_row_block(q, k, v, dout, idx, logg, bs, scale, bb, kv, t)
+        sel = (J >= lo) & (J < hi)
+        dk[J[sel] - lo] += dkj[sel]
+        dv[J[sel] - lo] += dvj[sel]
+    return dk, dv
+
+
+# --------------------------------------------------------------------------- (7) decode
+
+def decode(q, kcache, vcache, L: int, idx, logg, bs: int, scale: Optional[float] = None):
+    """Single-token attention at position L - 1 over the selected history blocks
+    and the current block's prefix.  logg None -> ungated ([picx] Eq. 2, the
+    deployed form in [evolve] 'Summary').  q [b,hq,d] -> o [b,hq,d], lse [b,hq]."""
+    b, hq, d = q.shape
+    hkv = kcache.shape[1]
+    g = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    c = (L - 1) // bs
+    o = np.zeros((b, hq, d))
+    lse = np.zeros((b, hq))
+    for bb in range(b):
+        for kv in range(hkv):
+            idx_row = _npint(idx[bb, kv])
+            logg_row = None if logg is None else _np64(logg[bb, kv])
+            J, bias, _, _ = key_set(c, idx_row, logg_row, bs, L, last_pos=L - 1)
+            kj = _rows(kcache[bb, kv], J)
+            vj = _rows(vcache[bb, kv], J)
+            for h in range(kv * g, (kv + 1) * g):
+                z = (_np64(q[bb, h]) @ kj.T) * scale + bias
+                p, l = _softmax_stats(z[None, :])
+                o[bb, h] = (p @ vj)[0]
+                lse[bb, h] = l[0]
+    return o, lse
+
+
+def decode_qbar(q, hkv: int) -> np.ndarray:
+    """Decode-mode pooled query: mean over the G query heads of each KV head,
+    shaped [b,kv,1,d] (float64)."""
+    q = _np64(q)
+    b, hq, d = q.shape
+    g = hq // hkv
+    return q.reshape(b, hkv, g, d).mean(axis=2)[:, :, None, :]
+
+
+# --------------------------------------------------------------------------- work counts
+
+def selected_pairs(idx, n: int, bs: int, g: int) -> int:
+    """Number of (query head, query row, key) pairs attended: selected history
+    blocks count fully, the current block causally."""
+    idx = _npint(idx)
+    b, hkv, T, _ = idx.shape
+    total = 0
+    for t in range(T):
+        lo, hi = block_span(t, bs, n)
+        rows = hi - lo
+        hist = 0
+        for m in idx[:, :, t].reshape(-1).tolist():
+            if m >= 0:
+                mlo, mhi = block_span(m, bs, n)
+                hist += mhi - mlo
+        total += hist * rows + b * hkv * rows * (rows + 1) // 2
+    return total * g

@@ -1,0 +1,90 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that a pin fails.
+
+Each mutation is applied with monkeypatch to the oracle module, one at a time;
+the pins of test_oracle_pins are then run and at least one must fail."""
+import numpy as np
+import pytest
+
+from oracle import sas_oracle as O
+import tests.test_oracle_pins as pins
+
+
+def _ds_row_no_softmax_term(s_row, lse_s, idx_row, dlogg_row):
+    ds = np.zeros(len(s_row))
+    for sl, m in enumerate(np.asarray(idx_row).tolist()):
+        if m >= 0:
+            ds[m] += dlogg_row[sl]
+    return ds
+
+
+def _topk_ties_high_index(s_row32, K):
+    s = np.asarray(s_row32, dtype=np.float32).astype(np.float64)
+    C = s.size
+    if C == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((-np.arange(C), -s))
+    return np.sort(order[:min(K, C)])
+
+
+def _gate_normaliser_selected_only(s_row):
+    # softmax over the top-K only would change lse; emulate with max only
+    s_row = np.asarray(s_row, dtype=np.float64)
+    return float(s_row.max()) if s_row.size else -np.inf
+
+
+_orig_logits = O._logits
+
+
+def _logits_no_causal(qrows, pos, kj, J, bias, cur, scale):
+    return (qrows @ kj.T) * scale + bias[None, :]
+
+
+def _logits_bias_sign(qrows, pos, kj, J, bias, cur, scale):
+    return _orig_logits(qrows, pos, kj, J, -bias, cur, scale)
+
+
+def _logits_no_scale(qrows, pos, kj, J, bias, cur, scale):
+    return _orig_logits(qrows, pos, kj, J, bias, cur, 1.0)
+
+
+_orig_bwd_row = O.bwd_row_block
+
+
+def _bwd_row_dk_unscaled(*a, **k):
+    dq, dl, (J, dkj, dvj) = _orig_bwd_row(*a, **k)
+    return dq, dl, (J, dkj / a[7], dvj)
+
+
+MUTATIONS = [
+    ("ds_row", _ds_row_no_softmax_term),
+    ("topk_history", _topk_ties_high_index),
+    ("gate_normaliser", _gate_normaliser_selected_only),
+    ("_logits", _logits_no_causal),
+    ("_logits", _logits_bias_sign),
+    ("_logits", _logits_no_scale),
+    ("bwd_row_block", _bwd_row_dk_unscaled),
+]
+
+PINS = [
+    pins.test_p2_score_shift_invariance,
+    pins.test_p3_ds_sums_to_zero,
+    pins.test_p5_topk_bruteforce_with_ties,
+    pins.test_p7_inner_gate_gradient_closed_form,
+    pins.test_p9_dominant_gate_limit,
+    pins.test_p10_gather_equals_dense_and_rows_normalise,
+    lambda: pins.test_p1_single_history_block_is_dense_causal(2, 1),
+    pins.test_p4_dense_scope_matches_library_softmax_and_autograd,
+    pins.test_p6_finite_differences,
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    failures = 0
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {fn.__name__}"
