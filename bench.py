@@ -1,0 +1,281 @@
+"""Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the training hot path over the Qwen3-4B-shaped 8K
+workload (batch 1, 8192 tokens, 32 query / 8 KV heads, head_dim 128, bf16,
+block 64, Top-31 + current block, stand-in selector): block pooling of q and k,
+stand-in scores, gate normalisation + Top-K, fused gated forward, and the
+backward returning dq/dk/dv, the per-block gate gradient and the selector
+gradient ds.  `value` is selected-attention TFLOP/s: 12*d FLOP per attended
+(query head, query, key) pair (4d forward, 8d backward), divided by the step
+time.  The decode part of the path (batch 8 x 64K and batch 1 x 512K contexts)
+is measured in the same run and reported under "decode" in GB/s of selected
+K/V bytes.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def selected_pairs_device(idx, n, bs, g):
+    """Attended (query head, query, key) pairs, counted on the device from idx:
+    selected history blocks count fully, the current block causally."""
+    import torch
+    b, hkv, T, K = idx.shape
+    valid = (idx >= 0).sum().item()
+    hist = valid * bs * bs                       # all blocks here are full (n % bs == 0)
+    cur = b * hkv * T * bs * (bs + 1) // 2
+    return (hist + cur) * g
+
+
+def train_step_fn(w, x, ws):
+    import torch
+    from gated_block_sparse_scores_amd import ops
+    T = w.nblocks
+
+    def step():
+        qb = ops.block_pool(x["q"], w.block, w.group)
+        kb = ops.block_pool(x["k"], w.block, 1)
+        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, w.topk, qbar=qb, kbar=kb)
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block)
+        gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s,
+                          w.block, workspace=ws)
+        return idx, gr
+    return step
+
+
+def kernel_flops(name, pairs, d):
+    """Algorithmic FLOPs of one launch of a kernel (selected pairs only)."""
+    if name.startswith("fwd"):
+        return 4 * d * pairs
+    if name.startswith("bwd_dkdv"):
+        return 6 * d * pairs       # dP, dV, dK
+    if name.startswith("bwd_dq"):
+        return 2 * d * pairs       # dQ
+    return None
+
+
+def bench_train(args):
+    import torch
+    import synth
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+
+    w = synth.workload(2)
+    dev = "cuda"
+    x = synth.train_inputs(w, device=dev)
+    sh = ops.shape_of(x["q"], x["k"], w.block)
+    ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
+    step = train_step_fn(w, x, ws)
+    for _ in range(args.warmup):
+        idx, _ = step()
+    torch.cuda.synchronize()
+    pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
+    flops = 12 * w.head_dim * pairs
+
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.sas_profiler_enable(False)
+    kt = L.sas_profiler_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    # dominant kernel
+    name, (n, tot) = max(kt.items(), key=lambda kv: kv[1][1])
+    avg_ms = tot / n
+    kf = kernel_flops(name, pairs, w.head_dim)
+    mfma = "mfma" in name
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
+    roof = None
+    if kf is not None:
+        ach = kf / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma" if mfma else "alu", "kernel": name, "achieved": round(ach, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 4)}
+    kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
+    return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
+                kernels=kernels, x=x, idx=idx)
+
+
+def bench_decode(wl, steps, layers=8):
+    """Decode of one new token per sequence over `layers` independent
+    selections (distinct queries), so consecutive calls read different blocks."""
+    import torch
+    import synth
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+
+    w = synth.workload(wl)
+    dev = "cuda"
+    x = synth.decode_inputs(w, device=dev)
+    Lc = w.seqlen
+    C = (Lc - 1) // w.block
+    kb = ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(1000 + wl)
+    qs = [torch.randn(x["q"].shape, generator=gen, device=dev).to(torch.bfloat16)
+          for _ in range(layers)]
+    sh = ops.shape_of(qs[0], x["kcache"], w.block, seqlen=Lc)
+    ws = torch.empty(L.sas_decode_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
+
+    def one(q):
+        qb = ops.block_pool(q.unsqueeze(2), w.block, w.group)
+        idx, logg, _, _ = ops.select_topk(w.batch, w.hkv, 1, C, w.topk, row_offset=C, qbar=qb,
+                                          kbar=kb)
+        return ops.decode(q, x["kcache"], x["vcache"], Lc, idx[:, :, 0], logg[:, :, 0],
+                          w.block, workspace=ws)
+
+    for q in qs:
+        one(q)
+    torch.cuda.synchronize()
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    t0 = time.perf_counter()
+    for it in range(steps):
+        for q in qs:
+            one(q)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.sas_profiler_enable(False)
+    kt = L.sas_profiler_read()
+    calls = steps * layers
+    us_step = (t1 - t0) * 1e6 / calls
+    sel_bytes = w.batch * w.hkv * (w.topk + 1) * w.block * w.head_dim * 2 * 2
+    kbar_bytes = w.batch * w.hkv * C * w.head_dim * 2
+    dsplit = kt.get("decode_split", (1, 0.0))
+    dmerge = kt.get("decode_merge", (1, 0.0))
+    split_us = dsplit[1] / dsplit[0] * 1e3
+    merge_us = dmerge[1] / dmerge[0] * 1e3
+    dec_gbs = sel_bytes / (split_us * 1e-6) / 1e9
+    kernels = {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)} for k, v in kt.items()}
+    return {
+        "workload": w.name, "batch": w.batch, "context": Lc, "hq": w.hq, "hkv": w.hkv,
+        "topk": w.topk, "selected_kv_bytes": sel_bytes, "pooled_key_bytes": kbar_bytes,
+        "decode_GBps": round(dec_gbs, 1),
+        "decode_plus_merge_us": round(split_us + merge_us, 2),
+        "step_us": round(us_step, 2),
+        "step_GBps": round((sel_bytes + kbar_bytes) / (us_step * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(dec_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(split_us, 2)},
+        "kernels": kernels,
+    }
+
+
+def cpu_baseline(res, budget_s=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    its own selection over every row, then forward + backward of sampled
+    (KV head, query block) rows until the time budget is spent."""
+    import numpy as np
+    import torch
+    from oracle import sas_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = res["w"]
+    x = {k: res["x"][k].cpu() for k in ("q", "k", "v", "dout")}
+    t0 = time.perf_counter()
+    qb = O.to_f32(O.pool_queries(x["q"], w.hkv, w.block))
+    kb = O.to_f32(O.pool_keys(x["k"], w.block))
+    T = w.nblocks
+    s = O.standin_scores(qb, kb, O.default_scale(w.head_dim), T)
+    idx, logg, lse_s = O.select_topk(s, w.topk)
+    t_sel = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    scale = O.default_scale(w.head_dim)
+    done, flops, t_rows = 0, 0, 0.0
+    order = rng.permutation(w.hkv * T)
+    while t_rows < budget_s and done < len(order):
+        kv, t = divmod(int(order[done]), T)
+        a = time.perf_counter()
+        O.bwd_row_block(x["q"], x["k"], x["v"], x["dout"], idx, logg, w.block, scale, 0, kv, t)
+        t_rows += time.perf_counter() - a
+        nsel = int((idx[0, kv, t] >= 0).sum())
+        pairs = (nsel * w.block * w.block + w.block * (w.block + 1) // 2) * w.group
+        flops += 12 * w.head_dim * pairs
+        done += 1
+    return {"value": round(flops / t_rows / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle: selection over all {w.hkv * T} rows "
+                      f"({t_sel:.1f} s), then forward+backward of {done} of the "
+                      f"{w.hkv * T} (KV head, query block) rows ({t_rows:.1f} s); value = "
+                      f"12*d FLOP per attended pair of those rows / their time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path is single-GPU by design "
+              "(sharding across GPUs is not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log("training workload ...")
+    res = bench_train(args)
+    out = {
+        "metric": "gated sparse attn fwd+bwd TFLOP/s, decode GB/s; % of MI355X roofline",
+        "value": round(res["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": res["w"].name, "batch": 1, "seq_len": res["w"].seqlen,
+                   "hq": 32, "hkv": 8, "head_dim": 128, "block": 64, "topk": res["w"].topk,
+                   "selector": "mean-pooled stand-in", "parallelism": "none"},
+        "selected_pairs": int(res["pairs"]),
+        "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
+        "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "roofline": res["roofline"],
+        "kernels": res["kernels"],
+    }
+    if not args.no_decode:
+        log("decode workloads ...")
+        out["decode"] = [bench_decode(4, steps=10), bench_decode(5, steps=25)]
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(res)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,647 @@
+// Gated block-sparse attention, portable kernels with fp32 arithmetic.
+//
+// These serve every supported shape and dtype (fp32 tensors in particular);
+// the bf16 MFMA kernels in attn_mfma_*.hip take over where they apply.
+//
+// picx.dev summary of SAS, 'Key Idea' Eq. 9: o = softmax(qK_S^T/sqrt(d) +
+// log g_S) V_S over the selected history blocks plus the current block (log
+// g0 = 0); 'Kernel Design': tile-level logits with the log gates added,
+// non-selected blocks skipped, online softmax, no attention matrix stored.
+// 'Gradient Analysis' Eq. 5 (inner gating) for the gate gradient and Eq. 6
+// for the selector gradient through the gate softmax.
+//
+// Thread layout (forward and dq pass): P = head_dim / 32 adjacent lanes own
+// one query row; lane p holds the float4 groups p, p+P, p+2P, ... of the row
+// (32 values).  Dot products are reduced across the P lanes with shuffles.
+// K/V tiles are staged in LDS as fp32, KC keys at a time.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace sas {
+
+namespace {
+
+constexpr int kRowsPerWG = 128;  // query rows (all heads) per forward / dq workgroup
+
+__device__ __forceinline__ void decode_tile(int tile, const Dims& dm, int nchunk, int* b,
+                                            int* kv, int* t, int* chunk) {
+  *chunk = tile % nchunk;
+  tile /= nchunk;
+  *t = tile % dm.T;
+  tile /= dm.T;
+  *kv = tile % dm.hkv;
+  *b = tile / dm.hkv;
+}
+
+// Loads 32 values of row `row` (head_dim D) owned by lane p into r[].
+template <typename T, int D>
+__device__ __forceinline__ void load_row_slice(const T* __restrict__ base, int p, float* r) {
+  constexpr int P = D / 32;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 4 * (p + P * e);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[4 * e + u] = Elem<T>::load(base, c + u);
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_row_slice(T* __restrict__ base, int p, const float* r,
+                                                float mul) {
+  constexpr int P = D / 32;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 4 * (p + P * e);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Elem<T>::store(base, c + u, r[4 * e + u] * mul);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float dot_slice(const float* r, const float* lds_row, int p) {
+  constexpr int P = D / 32;
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float4 x = *reinterpret_cast<const float4*>(lds_row + 4 * (p + P * e));
+    acc += r[4 * e] * x.x + r[4 * e + 1] * x.y + r[4 * e + 2] * x.z + r[4 * e + 3] * x.w;
+  }
+  return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void axpy_slice(float* acc, float a, const float* lds_row, int p) {
+  constexpr int P = D / 32;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float4 x = *reinterpret_cast<const float4*>(lds_row + 4 * (p + P * e));
+    acc[4 * e] += a * x.x;
+    acc[4 * e + 1] += a * x.y;
+    acc[4 * e + 2] += a * x.z;
+    acc[4 * e + 3] += a * x.w;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float reduce_p(float v) {
+  constexpr int P = D / 32;
+#pragma unroll
+  for (int o = 1; o < P; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Copies rows [lo, lo+nk) of a [*, D] tensor (type T) into LDS as fp32.
+template <typename T, int D, int KC>
+__device__ __forceinline__ void stage_rows(float (*dst)[D], const T* __restrict__ src, int nk) {
+  for (int e = threadIdx.x; e < KC * D; e += blockDim.x) {
+    const int r = e / D, c = e % D;
+    dst[r][c] = r < nk ? Elem<T>::load(src, (size_t)r * D + c) : 0.0f;
+  }
+}
+
+// Builds the list of key blocks of row (b, kv, t): valid selected blocks in
+// slot order (with their slot and log-gate), then the current block t.
+__device__ __forceinline__ int build_block_list(const int32_t* __restrict__ idx_row,
+                                                const float* __restrict__ logg_row, int K,
+                                                int t, int* blist, int* bslot, float* bbias) {
+  int cnt = 0;
+  for (int s = 0; s < K; ++s) {
+    const int m = idx_row[s];
+    if (m >= 0 && m < t) {
+      blist[cnt] = m;
+      bslot[cnt] = s;
+      bbias[cnt] = logg_row ? logg_row[s] : 0.0f;
+      ++cnt;
+    }
+  }
+  blist[cnt] = t;
+  bslot[cnt] = -1;
+  bbias[cnt] = 0.0f;
+  return cnt + 1;
+}
+
+// ---------------------------------------------------------------- forward
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(512) fwd_generic_kernel(
+    Dims dm, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, T* __restrict__ o,
+    float* __restrict__ lse, int hpw, int nchunk) {
+  constexpr int P = D / 32;
+  constexpr int KC = BS < 32 ? BS : 32;
+  __shared__ __align__(16) float Ks[KC][D];
+  __shared__ __align__(16) float Vs[KC][D];
+  __shared__ int blist[65], bslot[65];
+  __shared__ float bbias[65];
+  __shared__ int nblk;
+
+  int b, kv, t, chunk;
+  decode_tile(blockIdx.x, dm, nchunk, &b, &kv, &t, &chunk);
+  const int p = threadIdx.x % P;
+  const int rr = threadIdx.x / P;
+  const int r = rr % BS, hh = chunk * hpw + rr / BS;
+  const int h = kv * dm.g + hh;
+  const int i = t * BS + r;
+  const bool active = rr / BS < hpw && hh < dm.g && i < dm.n;
+
+  const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
+  if (threadIdx.x == 0)
+    nblk = build_block_list(idx + rowbk * dm.K, logg ? logg + rowbk * dm.K : nullptr, dm.K, t,
+                            blist, bslot, bbias);
+  float qv[32], acc[32];
+  const size_t qoff = (((size_t)b * dm.hq + h) * dm.n + i) * D;
+  if (active)
+    load_row_slice<T, D>(q + qoff, p, qv);
+  else
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qv[e] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
+  float mrun = -INFINITY, lrun = 0.0f;
+  __syncthreads();
+
+  const T* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
+  const T* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
+  const int nb = nblk;
+  for (int bi = 0; bi < nb; ++bi) {
+    const int m = blist[bi];
+    const float bias = bbias[bi];
+    for (int c0 = 0; c0 < BS; c0 += KC) {
+      const int lo = m * BS + c0;
+      const int nk = min(KC, dm.n - lo);
+      if (nk <= 0) break;
+      stage_rows<T, D, KC>(Ks, kbase + (size_t)lo * D, nk);
+      stage_rows<T, D, KC>(Vs, vbase + (size_t)lo * D, nk);
+      __syncthreads();
+      float sc[KC];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float z = reduce_p<D>(dot_slice<D>(qv, Ks[j], p)) * dm.scale + bias;
+        const bool valid = j < nk && (m != t || lo + j <= i);
+        sc[j] = valid ? z : -INFINITY;
+        cmax = fmaxf(cmax, sc[j]);
+      }
+      const float mnew = fmaxf(mrun, cmax);
+      const float alpha = mrun == -INFINITY ? 0.0f : expf(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float pj = sc[j] == -INFINITY ? 0.0f : expf(sc[j] - mnew);
+        lrun += pj;
+        axpy_slice<D>(acc, pj, Vs[j], p);
+      }
+      mrun = mnew;
+      __syncthreads();
+    }
+  }
+  if (active) {
+    store_row_slice<T, D>(o + qoff, p, acc, 1.0f / lrun);
+    if (p == 0) lse[((size_t)b * dm.hq + h) * dm.n + i] = mrun + logf(lrun);
+  }
+}
+
+int heads_per_wg(const Dims& dm) {
+  int hpw = kRowsPerWG / dm.bs;
+  if (hpw > dm.g) hpw = dm.g;
+  if (hpw < 1) hpw = 1;
+  return hpw;
+}
+
+template <typename T, int D, int BS>
+hipError_t fwd_generic_typed(const Dims& dm, const void* q, const void* k, const void* v,
+                             const int32_t* idx, const float* logg, void* o, float* lse,
+                             hipStream_t st) {
+  const int hpw = heads_per_wg(dm);
+  const int nchunk = (dm.g + hpw - 1) / hpw;
+  const int threads = (hpw * BS * (D / 32) + 63) / 64 * 64;
+  const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * nchunk;
+  ProfScope ps("fwd_generic", st);
+  hipLaunchKernelGGL((fwd_generic_kernel<T, D, BS>), dim3((unsigned)tiles), dim3(threads), 0,
+                     st, dm, (const T*)q, (const T*)k, (const T*)v, idx, logg, (T*)o, lse,
+                     hpw, nchunk);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- backward: D and CSR
+// D[b, h, i] = dout_i . o_i (fp32), 16 lanes per row.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ o,
+                                                      const T* __restrict__ dout,
+                                                      float* __restrict__ Dv, size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (row < rows) {
+    for (int e = sub; e < D; e += 16)
+      acc += Elem<T>::load(o, row * D + e) * Elem<T>::load(dout, row * D + e);
+  }
+#pragma unroll
+  for (int s = 8; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
+  if (row < rows && sub == 0) Dv[row] = acc;
+}
+
+// Inverse selection map: for key block m of (b, kv), the query blocks t > m
+// that selected it, ascending in t, as entries (t << 8) | slot.
+__global__ void __launch_bounds__(256) csr_count_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int K, size_t nbk,
+                                                        int* __restrict__ count) {
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= nbk * T) return;
+  const size_t bk = gid / T;
+  const int m = (int)(gid % T);
+  const int32_t* base = idx + bk * (size_t)T * K;
+  int c = 0;
+  for (int t = m + 1; t < T; ++t)
+    for (int s = 0; s < K; ++s) c += base[(size_t)t * K + s] == m;
+  count[gid] = c;
+}
+
+__global__ void __launch_bounds__(256) csr_scan_kernel(const int* __restrict__ count, int T,
+                                                       int K, int* __restrict__ off) {
+  __shared__ int scr[16];
+  const size_t bk = blockIdx.x;
+  int carry = (int)(bk * (size_t)T * K);
+  for (int m0 = 0; m0 < T; m0 += blockDim.x) {
+    const int m = m0 + threadIdx.x;
+    const int c = m < T ? count[bk * T + m] : 0;
+    int total;
+    const int ex = block_excl_scan(c, scr, &total);
+    if (m < T) off[bk * T + m] = carry + ex;
+    carry += total;
+  }
+}
+
+__global__ void __launch_bounds__(256) csr_fill_kernel(const int32_t* __restrict__ idx, int T,
+                                                       int K, size_t nbk,
+                                                       const int* __restrict__ off,
+                                                       int* __restrict__ list) {
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= nbk * T) return;
+  const size_t bk = gid / T;
+  const int m = (int)(gid % T);
+  const int32_t* base = idx + bk * (size_t)T * K;
+  int pos = off[gid];
+  for (int t = m + 1; t < T; ++t)
+    for (int s = 0; s < K; ++s)
+      if (base[(size_t)t * K + s] == m) list[pos++] = (t << 8) | s;
+}
+
+// ---------------------------------------------------------------- backward: dq + dlogg
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
+    Dims dm, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, T* __restrict__ dq,
+    float* __restrict__ dlogg_part, int hpw, int nchunk) {
+  constexpr int P = D / 32;
+  constexpr int KC = BS < 32 ? BS : 32;
+  __shared__ __align__(16) float Ks[KC][D];
+  __shared__ __align__(16) float Vs[KC][D];
+  __shared__ int blist[65], bslot[65];
+  __shared__ float bbias[65];
+  __shared__ float fscr[16];
+  __shared__ int nblk;
+
+  int b, kv, t, chunk;
+  decode_tile(blockIdx.x, dm, nchunk, &b, &kv, &t, &chunk);
+  const int p = threadIdx.x % P;
+  const int rr = threadIdx.x / P;
+  const int r = rr % BS, hh = chunk * hpw + rr / BS;
+  const int h = kv * dm.g + hh;
+  const int i = t * BS + r;
+  const bool active = rr / BS < hpw && hh < dm.g && i < dm.n;
+
+  const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
+  if (threadIdx.x == 0)
+    nblk = build_block_list(idx + rowbk * dm.K, logg ? logg + rowbk * dm.K : nullptr, dm.K, t,
+                            blist, bslot, bbias);
+  float qv[32], dov[32], acc[32];
+  const size_t row = ((size_t)b * dm.hq + h) * dm.n + i;
+  float lse_i = 0.0f, D_i = 0.0f;
+  if (active) {
+    load_row_slice<T, D>(q + row * D, p, qv);
+    load_row_slice<T, D>(dout + row * D, p, dov);
+    lse_i = lse[row];
+    D_i = Dv[row];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qv[e] = dov[e] = 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
+  __syncthreads();
+
+  float* dpart = dlogg_part + (rowbk * nchunk + chunk) * dm.K;
+  const T* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
+  const T* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
+  const int nb = nblk;
+  // slots without a valid block get 0
+  if (threadIdx.x < dm.K) {
+    bool used = false;
+    for (int bi = 0; bi + 1 < nb; ++bi) used |= bslot[bi] == (int)threadIdx.x;
+    if (!used) dpart[threadIdx.x] = 0.0f;
+  }
+  for (int bi = 0; bi < nb; ++bi) {
+    const int m = blist[bi];
+    const float bias = bbias[bi];
+    float bsum = 0.0f;
+    for (int c0 = 0; c0 < BS; c0 += KC) {
+      const int lo = m * BS + c0;
+      const int nk = min(KC, dm.n - lo);
+      if (nk <= 0) break;
+      stage_rows<T, D, KC>(Ks, kbase + (size_t)lo * D, nk);
+      stage_rows<T, D, KC>(Vs, vbase + (size_t)lo * D, nk);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float z = reduce_p<D>(dot_slice<D>(qv, Ks[j], p)) * dm.scale + bias;
+        const float dp = reduce_p<D>(dot_slice<D>(dov, Vs[j], p));
+        const bool valid = active && j < nk && (m != t || lo + j <= i);
+        const float pj = valid ? expf(z - lse_i) : 0.0f;
+        const float ds = pj * (dp - D_i);
+        axpy_slice<D>(acc, ds, Ks[j], p);
+        bsum += ds;
+      }
+      __syncthreads();
+    }
+    if (bslot[bi] >= 0) {
+      const float tot = block_sum(p == 0 ? bsum : 0.0f, fscr);
+      if (threadIdx.x == 0) dpart[bslot[bi]] = tot;
+    }
+  }
+  if (active) store_row_slice<T, D>(dq + row * D, p, acc, dm.scale);
+}
+
+// ---------------------------------------------------------------- backward: dk, dv
+// One workgroup per key block (b, kv, m); BS keys x P lanes.  Visits the
+// diagonal query block t = m, then every query block that selected m, for all
+// G heads, staging KC query rows of q and dout at a time.
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
+    Dims dm, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    const float* __restrict__ logg, const int* __restrict__ csr_count,
+    const int* __restrict__ csr_off, const int* __restrict__ csr_list, T* __restrict__ dk,
+    T* __restrict__ dv) {
+  constexpr int P = D / 32;
+  constexpr int KC = BS < 32 ? BS : 32;
+  __shared__ __align__(16) float Qs[KC][D];
+  __shared__ __align__(16) float Os[KC][D];
+  __shared__ float Ls[KC], Dl[KC];
+
+  const int m = blockIdx.x % dm.T;
+  const size_t bk = blockIdx.x / dm.T;
+  const int kv = (int)(bk % dm.hkv), b = (int)(bk / dm.hkv);
+  const int p = threadIdx.x % P;
+  const int jr = threadIdx.x / P;
+  const int j = m * BS + jr;
+  const bool kact = j < dm.n;
+
+  float kvk[32], kvv[32], adk[32], adv[32];
+  const size_t kvrow = ((size_t)b * dm.hkv + kv) * dm.n + j;
+  if (kact) {
+    load_row_slice<T, D>(k + kvrow * D, p, kvk);
+    load_row_slice<T, D>(v + kvrow * D, p, kvv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) kvk[e] = kvv[e] = 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) adk[e] = adv[e] = 0.0f;
+
+  const int ncsr = csr_count[bk * dm.T + m];
+  const int off = csr_off[bk * dm.T + m];
+  for (int ei = -1; ei < ncsr; ++ei) {
+    int t, slot;
+    if (ei < 0) {
+      t = m;
+      slot = -1;
+    } else {
+      const int e = csr_list[off + ei];
+      t = e >> 8;
+      slot = e & 255;
+    }
+    const float bias =
+        (slot >= 0 && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] : 0.0f;
+    for (int hh = 0; hh < dm.g; ++hh) {
+      const int h = kv * dm.g + hh;
+      const size_t rbase = ((size_t)b * dm.hq + h) * dm.n;
+      for (int c0 = 0; c0 < BS; c0 += KC) {
+        const int lo = t * BS + c0;
+        const int nr = min(KC, dm.n - lo);
+        if (nr <= 0) break;
+        stage_rows<T, D, KC>(Qs, q + (rbase + lo) * D, nr);
+        stage_rows<T, D, KC>(Os, dout + (rbase + lo) * D, nr);
+        for (int e = threadIdx.x; e < KC; e += blockDim.x) {
+          Ls[e] = e < nr ? lse[rbase + lo + e] : 0.0f;
+          Dl[e] = e < nr ? Dv[rbase + lo + e] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int ii = 0; ii < KC; ++ii) {
+          const float z = reduce_p<D>(dot_slice<D>(kvk, Qs[ii], p)) * dm.scale + bias;
+          const float dp = reduce_p<D>(dot_slice<D>(kvv, Os[ii], p));
+          const bool valid = kact && ii < nr && (t != m || j <= lo + ii);
+          const float pj = valid ? expf(z - Ls[ii]) : 0.0f;
+          const float ds = pj * (dp - Dl[ii]);
+          axpy_slice<D>(adv, pj, Os[ii], p);
+          axpy_slice<D>(adk, ds, Qs[ii], p);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (kact) {
+    store_row_slice<T, D>(dk + kvrow * D, p, adk, dm.scale);
+    store_row_slice<T, D>(dv + kvrow * D, p, adv, 1.0f);
+  }
+}
+
+// ---------------------------------------------------------------- backward: ds
+// Per row (b, kv, t): dlogg = sum of the per-chunk partials (fixed order),
+// ds_m = [m in I] dlogg_slot(m) - exp(s_m - lse_s) * sum(dlogg) for m < t,
+// 0 for m >= t.
+__global__ void __launch_bounds__(256) bwd_ds_kernel(
+    int T, int K, const int32_t* __restrict__ idx, const float* __restrict__ s,
+    const float* __restrict__ lse_s, const float* __restrict__ dlogg_part, int nchunk,
+    float* __restrict__ dlogg, float* __restrict__ ds) {
+  __shared__ float dl[64];
+  __shared__ int im[64];
+  __shared__ float tot;
+  const size_t row = blockIdx.x;
+  const int t = (int)(row % T);
+  if (threadIdx.x < K) {
+    float a = 0.0f;
+    for (int c = 0; c < nchunk; ++c) a += dlogg_part[(row * nchunk + c) * K + threadIdx.x];
+    const int m = idx[row * K + threadIdx.x];
+    const bool ok = m >= 0 && m < t;
+    dl[threadIdx.x] = ok ? a : 0.0f;
+    im[threadIdx.x] = ok ? m : -1;
+    if (dlogg) dlogg[row * K + threadIdx.x] = ok ? a : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = 0.0f;
+    for (int sl = 0; sl < K; ++sl) a += dl[sl];
+    tot = a;
+  }
+  __syncthreads();
+  if (!ds) return;
+  const float ls = lse_s ? lse_s[row] : 0.0f;
+  for (int m = threadIdx.x; m < T; m += blockDim.x) {
+    float val = 0.0f;
+    if (m < t) {
+      float own = 0.0f;
+      for (int sl = 0; sl < K; ++sl)
+        if (im[sl] == m) own = dl[sl];
+      val = own - expf(s[row * T + m] - ls) * tot;
+    }
+    ds[row * T + m] = val;
+  }
+}
+
+template <typename T, int D, int BS>
+hipError_t bwd_generic_typed(const Dims& dm, const void* q, const void* k, const void* v,
+                             const void* dout, const float* lse, const int32_t* idx,
+                             const float* logg, void* dq, void* dk, void* dv,
+                             const BwdWorkspace& ws, int* nchunk_out, hipStream_t st) {
+  const int hpw = heads_per_wg(dm);
+  const int nchunk = (dm.g + hpw - 1) / hpw;
+  *nchunk_out = nchunk;
+  {
+    const int threads = (hpw * BS * (D / 32) + 63) / 64 * 64;
+    const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * nchunk;
+    ProfScope ps("bwd_dq_generic", st);
+    hipLaunchKernelGGL((bwd_dq_generic_kernel<T, D, BS>), dim3((unsigned)tiles), dim3(threads),
+                       0, st, dm, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse,
+                       ws.D, idx, logg, (T*)dq, ws.dlogg_part, hpw, nchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
+    ProfScope ps("bwd_dkdv_generic", st);
+    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D, BS>), dim3((unsigned)wgs),
+                       dim3(BS * (D / 32)), 0, st, dm, (const T*)q, (const T*)k, (const T*)v,
+                       (const T*)dout, lse, ws.D, logg, ws.csr_count, ws.csr_off, ws.csr_list,
+                       (T*)dk, (T*)dv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
+                              const int32_t* idx, const float* logg, void* o, float* lse,
+                              hipStream_t st) {
+#define SAS_FWD(T_, D_, BS_)                                                         \
+  if ((dm.bf16 == std::is_same<T_, bf16_t>::value) && dm.d == D_ && dm.bs == BS_) \
+    return fwd_generic_typed<T_, D_, BS_>(dm, q, k, v, idx, logg, o, lse, st);
+  SAS_FWD(float, 64, 16) SAS_FWD(float, 64, 32) SAS_FWD(float, 64, 64)
+  SAS_FWD(float, 128, 16) SAS_FWD(float, 128, 32) SAS_FWD(float, 128, 64)
+  SAS_FWD(bf16_t, 64, 16) SAS_FWD(bf16_t, 64, 32) SAS_FWD(bf16_t, 64, 64)
+  SAS_FWD(bf16_t, 128, 16) SAS_FWD(bf16_t, 128, 32) SAS_FWD(bf16_t, 128, 64)
+#undef SAS_FWD
+  return hipErrorInvalidValue;
+}
+
+int bwd_dlogg_chunks(const Dims& dm) {
+  const int hpw = heads_per_wg(dm);
+  return (dm.g + hpw - 1) / hpw;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base) {
+  BwdWorkspace w{};
+  char* p = (char*)base;
+  size_t off = 0;
+  const size_t rows = (size_t)dm.b * dm.hkv * dm.T;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.D = (float*)take((size_t)dm.b * dm.hq * dm.n * sizeof(float));
+  w.csr_count = (int*)take(rows * sizeof(int));
+  w.csr_off = (int*)take(rows * sizeof(int));
+  w.csr_list = (int*)take(rows * (size_t)dm.K * sizeof(int));
+  w.dlogg_part = (float*)take(rows * (size_t)bwd_dlogg_chunks(dm) * dm.K * sizeof(float));
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, const int32_t* idx,
+                           const BwdWorkspace& ws, hipStream_t st) {
+  const size_t rows = (size_t)dm.b * dm.hq * dm.n;
+  {
+    ProfScope ps("bwd_dot", st);
+    const unsigned grid = (unsigned)((rows + 15) / 16);
+    if (dm.bf16 && dm.d == 128)
+      hipLaunchKernelGGL((bwd_dot_kernel<bf16_t, 128>), dim3(grid), dim3(256), 0, st,
+                         (const bf16_t*)o, (const bf16_t*)dout, ws.D, rows);
+    else if (dm.bf16)
+      hipLaunchKernelGGL((bwd_dot_kernel<bf16_t, 64>), dim3(grid), dim3(256), 0, st,
+                         (const bf16_t*)o, (const bf16_t*)dout, ws.D, rows);
+    else if (dm.d == 128)
+      hipLaunchKernelGGL((bwd_dot_kernel<float, 128>), dim3(grid), dim3(256), 0, st,
+                         (const float*)o, (const float*)dout, ws.D, rows);
+    else
+      hipLaunchKernelGGL((bwd_dot_kernel<float, 64>), dim3(grid), dim3(256), 0, st,
+                         (const float*)o, (const float*)dout, ws.D, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t nbk = (size_t)dm.b * dm.hkv;
+  const unsigned g = (unsigned)((nbk * dm.T + 255) / 256);
+  {
+    ProfScope ps("csr_count", st);
+    hipLaunchKernelGGL(csr_count_kernel, dim3(g), dim3(256), 0, st, idx, dm.T, dm.K, nbk,
+                       ws.csr_count);
+  }
+  {
+    ProfScope ps("csr_scan", st);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)nbk), dim3(256), 0, st, ws.csr_count,
+                       dm.T, dm.K, ws.csr_off);
+  }
+  {
+    ProfScope ps("csr_fill", st);
+    hipLaunchKernelGGL(csr_fill_kernel, dim3(g), dim3(256), 0, st, idx, dm.T, dm.K, nbk,
+                       ws.csr_off, ws.csr_list);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const int32_t* idx,
+                              const float* logg, void* dq, void* dk, void* dv,
+                              const BwdWorkspace& ws, int* nchunk_out, hipStream_t st) {
+#define SAS_BWD(T_, D_, BS_)                                                           \
+  if ((dm.bf16 == std::is_same<T_, bf16_t>::value) && dm.d == D_ && dm.bs == BS_)   \
+    return bwd_generic_typed<T_, D_, BS_>(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws, \
+                                          nchunk_out, st);
+  SAS_BWD(float, 64, 16) SAS_BWD(float, 64, 32) SAS_BWD(float, 64, 64)
+  SAS_BWD(float, 128, 16) SAS_BWD(float, 128, 32) SAS_BWD(float, 128, 64)
+  SAS_BWD(bf16_t, 64, 16) SAS_BWD(bf16_t, 64, 32) SAS_BWD(bf16_t, 64, 64)
+  SAS_BWD(bf16_t, 128, 16) SAS_BWD(bf16_t, 128, 32) SAS_BWD(bf16_t, 128, 64)
+#undef SAS_BWD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_ds(const Dims& dm, const int32_t* idx, const float* s, const float* lse_s,
+                         const float* dlogg_part, int nchunk, float* dlogg, float* ds,
+                         hipStream_t st) {
+  const size_t rows = (size_t)dm.b * dm.hkv * dm.T;
+  ProfScope ps("bwd_ds", st);
+  hipLaunchKernelGGL(bwd_ds_kernel, dim3((unsigned)rows), dim3(256), 0, st, dm.T, dm.K, idx, s,
+                     lse_s, dlogg_part, nchunk, dlogg, ds);
+  return hipGetLastError();
+}
+
+}  // namespace sas

@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI (sas_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+// Brackets one kernel launch with timing events when the profiler is on.
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t stream);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+
+struct Dims {
+  int b, hq, hkv, g, n, d, bs, T, K;
+  float scale;
+  bool bf16;
+};
+
+// ---- selection (select.hip)
+hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, int group,
+                             int n, int d, int bs, bool out_bf16, void* out, hipStream_t st);
+hipError_t launch_standin_scores(const float* qbar, const void* kbar, bool kbar_bf16,
+                                 int kbar_ld, int rows_bk, int T, int C, int row_offset,
+                                 int d, double scale, float* s_out, hipStream_t st);
+hipError_t launch_topk(const float* s, int rows_bk, int T, int C, int row_offset, int K,
+                       int32_t* idx, float* logg, float* lse_s, hipStream_t st);
+
+// ---- attention, portable fp32-arithmetic kernels (attn_generic.hip)
+hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
+                              const int32_t* idx, const float* logg, void* o, float* lse,
+                              hipStream_t st);
+// Workspace layout helpers for the backward.
+struct BwdWorkspace {
+  float* D;          // [b, hq, n]
+  int* csr_count;    // [b*hkv*T]
+  int* csr_off;      // [b*hkv*T]
+  int* csr_list;     // [b*hkv*T*K]  entries (t << 8) | slot
+  float* dlogg_part; // [b*hkv*T, nchunk, K]
+  size_t bytes;
+};
+BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base);
+hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, const int32_t* idx,
+                           const BwdWorkspace& ws, hipStream_t st);
+hipError_t launch_bwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const int32_t* idx,
+                              const float* logg, void* dq, void* dk, void* dv,
+                              const BwdWorkspace& ws, int* nchunk_out, hipStream_t st);
+hipError_t launch_bwd_ds(const Dims& dm, const int32_t* idx, const float* s, const float* lse_s,
+                         const float* dlogg_part, int nchunk, float* dlogg, float* ds,
+                         hipStream_t st);
+int bwd_dlogg_chunks(const Dims& dm);
+
+// ---- decode (decode.hip)
+int decode_blocks_per_split(const Dims& dm);
+size_t decode_workspace_bytes(const Dims& dm);
+hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
+                         const void* vc, const int32_t* idx, const float* logg, void* o,
+                         float* lse, void* ws, hipStream_t st);
+
+}  // namespace sas

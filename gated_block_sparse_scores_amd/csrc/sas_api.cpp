@@ -1,0 +1,334 @@
+// C ABI of the SAS gated block-sparse attention library: argument checks on
+// the host, workspace layout, kernel dispatch and the optional kernel timer.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/sas.h"
+#include "internal.h"
+
+namespace sas {
+// MFMA paths (attn_mfma_fwd.hip / attn_mfma_bwd.hip); return false when the
+// shape is not one they handle.
+bool mfma_fwd_supported(const Dims& dm);
+hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const float* logg, void* o, float* lse,
+                           hipStream_t st);
+bool mfma_bwd_supported(const Dims& dm);
+hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const int32_t* idx,
+                           const float* logg, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& ws, int* nchunk_out, hipStream_t st);
+}  // namespace sas
+
+namespace {
+
+// ------------------------------------------------------------------ profiler
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRecord> pending;
+  std::map<std::string, std::pair<long long, double>> totals;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain() {
+    for (auto& r : pending) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(r.stop) == hipSuccess &&
+          hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+        auto& t = totals[r.name];
+        t.first += 1;
+        t.second += ms;
+      }
+      pool.push_back(r.start);
+      pool.push_back(r.stop);
+    }
+    pending.clear();
+  }
+};
+
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+thread_local std::vector<ProfRecord> open_records;
+
+}  // namespace
+
+namespace sas {
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.on) return;
+  ProfRecord r{name, p.take(), p.take()};
+  if (!r.start || !r.stop) return;
+  (void)hipEventRecord(r.start, s);
+  open_records.push_back(r);
+  slot = (int)open_records.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  ProfRecord r = open_records[slot];
+  open_records.pop_back();
+  (void)hipEventRecord(r.stop, stream);
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.pending.push_back(r);
+}
+
+}  // namespace sas
+
+using sas::Dims;
+
+namespace {
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+sas_status check_shape(const sas_shape* s, bool need_seq = true) {
+  if (!s) return SAS_ERR_INVALID_ARG;
+  if (s->batch <= 0 || s->hq <= 0 || s->hkv <= 0 || s->head_dim <= 0 || s->block <= 0)
+    return SAS_ERR_INVALID_ARG;
+  if (need_seq && s->seqlen <= 0) return SAS_ERR_INVALID_ARG;
+  if (s->hq % s->hkv != 0) return SAS_ERR_INVALID_ARG;
+  if (s->dtype != SAS_DTYPE_F32 && s->dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
+  if (!(s->scale >= 0.0f) || isinf(s->scale)) return SAS_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return SAS_ERR_UNSUPPORTED;
+  if (s->block != 16 && s->block != 32 && s->block != 64) return SAS_ERR_UNSUPPORTED;
+  return SAS_OK;
+}
+
+Dims make_dims(const sas_shape* s, int K) {
+  Dims d{};
+  d.b = s->batch;
+  d.hq = s->hq;
+  d.hkv = s->hkv;
+  d.g = s->hq / s->hkv;
+  d.n = s->seqlen;
+  d.d = s->head_dim;
+  d.bs = s->block;
+  d.T = (s->seqlen + s->block - 1) / s->block;
+  d.K = K;
+  d.scale = s->scale > 0.0f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
+  d.bf16 = s->dtype == SAS_DTYPE_BF16;
+  return d;
+}
+
+sas_status launch_status(hipError_t e) { return e == hipSuccess ? SAS_OK : SAS_ERR_LAUNCH; }
+
+#define SAS_TRY(expr)                       \
+  do {                                      \
+    sas_status st_ = (expr);                \
+    if (st_ != SAS_OK) return st_;          \
+  } while (0)
+
+#define SAS_LAUNCH(expr)                                \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return SAS_ERR_LAUNCH;        \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* sas_status_string(sas_status status) {
+  switch (status) {
+    case SAS_OK: return "ok";
+    case SAS_ERR_INVALID_ARG: return "invalid argument";
+    case SAS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case SAS_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int sas_version(void) { return 100; }
+
+sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int group,
+                          sas_dtype out_dtype, void* out, void* stream) {
+  if (!shape) return SAS_ERR_INVALID_ARG;
+  if (shape->batch <= 0 || shape->seqlen <= 0 || shape->head_dim <= 0 || shape->block <= 0)
+    return SAS_ERR_INVALID_ARG;
+  if (heads <= 0 || group <= 0 || heads % group != 0) return SAS_ERR_INVALID_ARG;
+  if (!x || !out) return SAS_ERR_INVALID_ARG;
+  if (shape->dtype != SAS_DTYPE_F32 && shape->dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
+  if (out_dtype != SAS_DTYPE_F32 && out_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
+  if (shape->head_dim != 64 && shape->head_dim != 128) return SAS_ERR_UNSUPPORTED;
+  if (shape->block > 4096) return SAS_ERR_UNSUPPORTED;
+  return launch_status(sas::launch_block_pool(
+      x, shape->dtype == SAS_DTYPE_BF16, shape->batch, heads, group, shape->seqlen,
+      shape->head_dim, shape->block, out_dtype == SAS_DTYPE_BF16, out, (hipStream_t)stream));
+}
+
+sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset, int K,
+                           const float* s, const float* qbar, const void* kbar,
+                           sas_dtype kbar_dtype, int kbar_ld, float* s_out, int32_t* idx,
+                           float* logg, float* lse_s, void* stream) {
+  if (!shape || shape->batch <= 0 || shape->hkv <= 0) return SAS_ERR_INVALID_ARG;
+  if (T <= 0 || C < 0 || row_offset < 0 || K <= 0) return SAS_ERR_INVALID_ARG;
+  if (!idx || !logg || !lse_s) return SAS_ERR_INVALID_ARG;
+  if (K > 64 || C > 16384) return SAS_ERR_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  const int rows_bk = shape->batch * shape->hkv;
+  const float* scores = s;
+  if (!s) {
+    if (!qbar || !kbar || !s_out) return SAS_ERR_INVALID_ARG;
+    if (kbar_dtype != SAS_DTYPE_F32 && kbar_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
+    if (kbar_ld < C) return SAS_ERR_INVALID_ARG;
+    if (shape->head_dim <= 0) return SAS_ERR_INVALID_ARG;
+    if (shape->head_dim > 128) return SAS_ERR_UNSUPPORTED;
+    if (!(shape->scale >= 0.0f)) return SAS_ERR_INVALID_ARG;
+    const double scale =
+        shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
+    if (C > 0)
+      SAS_LAUNCH(sas::launch_standin_scores(qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
+                                            rows_bk, T, C, row_offset, shape->head_dim, scale,
+                                            s_out, st));
+    scores = s_out;
+  }
+  return launch_status(
+      sas::launch_topk(scores, rows_bk, T, C, row_offset, K, idx, logg, lse_s, st));
+}
+
+size_t sas_attn_fwd_workspace_size(const sas_shape* shape, int K) {
+  (void)shape;
+  (void)K;
+  return 0;
+}
+
+sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void* k,
+                        const void* v, const int32_t* idx, const float* logg, void* o,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  SAS_TRY(check_shape(shape));
+  if (K <= 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !idx || !o || !lse) return SAS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return SAS_ERR_INVALID_ARG;
+  const Dims dm = make_dims(shape, K);
+  const hipStream_t st = (hipStream_t)stream;
+  if (sas::mfma_fwd_supported(dm))
+    return launch_status(sas::launch_fwd_mfma(dm, q, k, v, idx, logg, o, lse, st));
+  return launch_status(sas::launch_fwd_generic(dm, q, k, v, idx, logg, o, lse, st));
+}
+
+size_t sas_attn_bwd_workspace_size(const sas_shape* shape, int K) {
+  if (check_shape(shape) != SAS_OK || K <= 0 || K > 64) return 0;
+  const Dims dm = make_dims(shape, K);
+  return sas::bwd_workspace_layout(dm, nullptr).bytes;
+}
+
+sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        const int32_t* idx, const float* logg, const float* s,
+                        const float* lse_s, void* dq, void* dk, void* dv, float* dlogg,
+                        float* ds, void* workspace, size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !dout || !lse || !idx || !dq || !dk || !dv)
+    return SAS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SAS_ERR_INVALID_ARG;
+  if (!logg && (dlogg || ds || s || lse_s)) return SAS_ERR_INVALID_ARG;
+  if (ds && (!s || !lse_s)) return SAS_ERR_INVALID_ARG;
+  const Dims dm = make_dims(shape, K);
+  const sas::BwdWorkspace ws = sas::bwd_workspace_layout(dm, workspace);
+  if (!workspace || ws_bytes < ws.bytes) return SAS_ERR_WORKSPACE;
+  const hipStream_t st = (hipStream_t)stream;
+  SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, st));
+  int nchunk = 0;
+  if (sas::mfma_bwd_supported(dm))
+    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws, &nchunk,
+                                    st));
+  else
+    SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws,
+                                       &nchunk, st));
+  if (dlogg || ds)
+    SAS_LAUNCH(sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, nchunk, dlogg, ds, st));
+  return SAS_OK;
+}
+
+size_t sas_decode_workspace_size(const sas_shape* shape, int K) {
+  if (check_shape(shape) != SAS_OK || K <= 0 || K > 64) return 0;
+  return sas::decode_workspace_bytes(make_dims(shape, K));
+}
+
+sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* q,
+                      const void* kcache, const void* vcache, const int32_t* idx,
+                      const float* logg, void* o, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0 || cache_len < 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  const int L = shape->seqlen;
+  const int cl = cache_len == 0 ? L : cache_len;
+  if (cl < L) return SAS_ERR_INVALID_ARG;
+  if (!q || !kcache || !vcache || !idx || !o || !lse) return SAS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o))
+    return SAS_ERR_INVALID_ARG;
+  if (shape->hq / shape->hkv > 8) return SAS_ERR_UNSUPPORTED;
+  const Dims dm = make_dims(shape, K);
+  const size_t need = sas::decode_workspace_bytes(dm);
+  if (!workspace || ws_bytes < need) return SAS_ERR_WORKSPACE;
+  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx, logg, o, lse,
+                                          workspace, (hipStream_t)stream));
+}
+
+void sas_profiler_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+}
+
+void sas_profiler_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.drain();
+  p.totals.clear();
+}
+
+int sas_profiler_read(sas_kernel_time* out, int max_entries) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.drain();
+  int i = 0;
+  for (auto& kvp : p.totals) {
+    if (out && i < max_entries) {
+      memset(out[i].name, 0, sizeof(out[i].name));
+      strncpy(out[i].name, kvp.first.c_str(), sizeof(out[i].name) - 1);
+      out[i].launches = kvp.second.first;
+      out[i].total_ms = kvp.second.second;
+    }
+    ++i;
+  }
+  return i;
+}
+
+}  // extern "C"

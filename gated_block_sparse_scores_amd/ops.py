@@ -1,0 +1,113 @@
+"""Allocating wrappers over the C ABI (torch supplies device memory and streams).
+
+Each function allocates its outputs (and workspace) with torch on the inputs'
+device and calls the matching libsas entry point; nothing is computed here.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import Shape
+
+
+def _i32(shape, dev):
+    return torch.empty(shape, dtype=torch.int32, device=dev)
+
+
+def _f32(shape, dev):
+    return torch.empty(shape, dtype=torch.float32, device=dev)
+
+
+def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, scale: float = 0.0,
+             seqlen: Optional[int] = None) -> Shape:
+    """Shape of a training call (q [b,hq,N,d], k [b,hkv,N,d]) or, with q of
+    rank 3, of a decode call (seqlen = valid cache length)."""
+    if q.dim() == 4:
+        b, hq, n, d = q.shape
+    else:
+        b, hq, d = q.shape
+        n = seqlen
+    return Shape(b, hq, k.shape[1], n if seqlen is None else seqlen, d, block,
+                 L.dtype_code(q.dtype), scale)
+
+
+def block_pool(x: torch.Tensor, block: int, group: int = 1,
+               out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """Mean of x [b,H,N,d] over each block's tokens and over groups of `group`
+    heads -> [b, H/group, ceil(N/block), d]."""
+    b, H, n, d = x.shape
+    T = -(-n // block)
+    out = torch.empty((b, H // group, T, d), dtype=out_dtype, device=x.device)
+    sh = Shape(b, H, H, n, d, block, L.dtype_code(x.dtype))
+    L.sas_block_pool(sh, x, H, group, L.dtype_code(out_dtype), out, stream)
+    return out
+
+
+def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int = 0,
+                s: Optional[torch.Tensor] = None, qbar: Optional[torch.Tensor] = None,
+                kbar: Optional[torch.Tensor] = None, head_dim: int = 0, scale: float = 0.0,
+                stream=None, device=None):
+    """Returns (idx, logg, lse_s, s_used).  With s None the stand-in score from
+    qbar/kbar is formed on the device and returned as s_used."""
+    dev = device or (s.device if s is not None else qbar.device)
+    idx = _i32((batch, hkv, T, K), dev)
+    logg = _f32((batch, hkv, T, K), dev)
+    lse_s = _f32((batch, hkv, T), dev)
+    s_out = None
+    kdt, kld = L.SAS_DTYPE_F32, 0
+    if s is None:
+        s_out = _f32((batch, hkv, T, C), dev)
+        kdt = L.dtype_code(kbar.dtype)
+        kld = kbar.shape[2]
+        head_dim = qbar.shape[-1]
+    sh = Shape(batch, hkv, hkv, 1, head_dim or 1, 1, L.SAS_DTYPE_F32, scale)
+    L.sas_select_topk(sh, T, C, row_offset, K, s, qbar, kbar, kdt, kld, s_out, idx, logg, lse_s,
+                      stream)
+    return idx, logg, lse_s, (s if s is not None else s_out)
+
+
+def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None):
+    sh = shape_of(q, k, block, scale)
+    K = idx.shape[-1]
+    o = torch.empty_like(q)
+    lse = _f32(q.shape[:3], q.device)
+    ws_n = L.sas_attn_fwd_workspace_size(sh, K)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_attn_fwd(sh, K, q, k, v, idx, logg, o, lse, ws, ws_n, stream)
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, idx, logg, s, lse_s, block: int, scale: float = 0.0,
+             want_ds: bool = True, stream=None, workspace: Optional[torch.Tensor] = None):
+    sh = shape_of(q, k, block, scale)
+    K = idx.shape[-1]
+    T = idx.shape[2]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dlogg = _f32(idx.shape, q.device) if logg is not None else None
+    ds = _f32((q.shape[0], k.shape[1], T, T), q.device) if (want_ds and logg is not None) else None
+    ws_n = L.sas_attn_bwd_workspace_size(sh, K)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_attn_bwd(sh, K, q, k, v, o, dout, lse, idx, logg, s if ds is not None else None,
+                   lse_s if ds is not None else None, dq, dk, dv, dlogg, ds, workspace, ws_n,
+                   stream)
+    return {"dq": dq, "dk": dk, "dv": dv, "dlogg": dlogg, "ds": ds}
+
+
+def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0,
+           stream=None, workspace: Optional[torch.Tensor] = None):
+    """q [b,hq,d]; caches [b,hkv,cache_len,d]; idx/logg [b,hkv,K]."""
+    sh = shape_of(q, kcache, block, scale, seqlen=L_)
+    K = idx.shape[-1]
+    o = torch.empty_like(q)
+    lse = _f32(q.shape[:2], q.device)
+    ws_n = L.sas_decode_workspace_size(sh, K)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_decode(sh, kcache.shape[2], K, q, kcache, vcache, idx, logg, o, lse, workspace, ws_n,
+                 stream)
+    return o, lse

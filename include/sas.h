@@ -1,0 +1,205 @@
+/*
+ * sas.h -- C ABI of the MI355X (gfx950) library for SAS gated block-sparse
+ * causal attention.
+ *
+ * The method (page titles of the sources, then section / equation):
+ *   picx.dev summary of "SAS: Simple Attention Sparsification":
+ *     'Theoretical Foundation' Eq. 2-3 (block-sparse attention over a Top-K set
+ *     of history blocks), 'Key Idea: Differentiable Continuous Gating' Eq. 4
+ *     (positive gates, g0 = 1 on the always-kept current block) and Eq. 9 (log
+ *     gates added inside the attention softmax), 'Gradient Analysis' Eq. 5
+ *     (inner-gate gradient) and Eq. 6 (softmax gates: log g_m = s_m - LSE(s)),
+ *     'Kernel Design' (fused flash-style kernel, no attention matrix).
+ *   "SAS: End-to-end learning of sparse attention rankings from language-model
+ *     loss" (reproduction README): 'Core equations' (the 1/sqrt(d) scale and
+ *     g = softmax(s) over the history blocks before Top-K).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains them; scratch comes from a caller
+ *     workspace whose size the matching *_workspace_size call returns.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream) and returns without waiting.
+ *   - Argument errors (null pointers, bad sizes, unsupported shapes, short
+ *     workspace) are detected on the host before anything is launched and
+ *     returned synchronously; nothing is enqueued then.  SAS_ERR_LAUNCH
+ *     reports a failed enqueue (hipGetLastError after the launch).
+ *   - Layouts are dense row-major with head_dim innermost:
+ *       q, o, dout, dq      [batch, hq,  seqlen, head_dim]
+ *       k, v, dk, dv        [batch, hkv, seqlen, head_dim]
+ *       scores s, ds        [batch, hkv, T, C]        fp32
+ *       idx, logg           [batch, hkv, T, K]        int32 / fp32
+ *     with T = ceil(seqlen / block) query blocks.  Query head h reads KV head
+ *     h / (hq / hkv); all query heads of one KV head share one selection.
+ *   - Block B_m holds tokens [m*block, min((m+1)*block, seqlen)); the query
+ *     block of row i is B_t, t = i / block.  Row i attends to the tokens of
+ *     the selected history blocks (fully) and to tokens j <= i of B_t.
+ *   - idx entries are ascending block indices, -1 for unused slots.  Entries
+ *     outside [0, t) of their row are ignored by the attention kernels (they
+ *     can never make a kernel read outside the tensors).
+ *   - Supported: head_dim in {64, 128}; block in {16, 32, 64}; dtype fp32
+ *     (all tensors fp32) or bf16 (q, k, v, o, dout, dq, dk, dv bf16; scores,
+ *     gates, LSE, ds fp32); 1 <= K <= 64; hq a multiple of hkv.  Anything
+ *     else returns SAS_ERR_UNSUPPORTED.
+ *   - Calls are thread-safe.  Calls that share output buffers must not
+ *     overlap.
+ */
+#ifndef SAS_H
+#define SAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAS_OK = 0,
+  SAS_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, inconsistent shape */
+  SAS_ERR_UNSUPPORTED = 2,  /* valid, but outside the supported shapes above */
+  SAS_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than required */
+  SAS_ERR_LAUNCH = 4        /* the HIP runtime refused a launch */
+} sas_status;
+
+typedef enum { SAS_DTYPE_F32 = 0, SAS_DTYPE_BF16 = 1 } sas_dtype;
+
+typedef struct {
+  int batch;
+  int hq;        /* query heads */
+  int hkv;       /* key/value heads; hq % hkv == 0, G = hq / hkv */
+  int seqlen;    /* training: N tokens; decode: valid cache length L (incl. new token) */
+  int head_dim;  /* d */
+  int block;     /* tokens per block */
+  sas_dtype dtype;
+  float scale;   /* logit scale; 0 selects 1/sqrt(head_dim) */
+} sas_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* sas_status_string(sas_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int sas_version(void);
+
+/* ------------------------------------------------------------------------
+ * Block summaries for the stand-in selector (evolve.pub review of SAS, FAQ:
+ * pooling-based block summaries).
+ *
+ * out[b, h / group, t, :] = mean of x[b, h', i, :] over the `group` heads
+ * h' of that group and the valid tokens i of block B_t, accumulated in fp64
+ * and rounded to fp32 (out_dtype F32) or, for out_dtype BF16, rounded to fp32
+ * and then to bf16 (both round-to-nearest-even).
+ *   x   : [batch, heads, seqlen, head_dim] in shape->dtype
+ *   out : [batch, heads / group, ceil(seqlen / block), head_dim] in out_dtype
+ * Uses shape->batch, seqlen, head_dim, block, dtype.  heads % group == 0.
+ * ---------------------------------------------------------------------- */
+sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int group,
+                          sas_dtype out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gate normalisation and hard Top-K (picx Eq. 3, Eq. 4, Eq. 6).
+ *
+ * Rows r = (b, kv, t), t < T.  Row t ranks the history blocks m < C_t with
+ *   C_t = min(t + row_offset, C)
+ * (training: T = C = number of blocks, row_offset = 0; decode: T = 1,
+ * C = (L - 1) / block, row_offset = C).
+ *
+ * Scores: either s != NULL (fp32 [b, hkv, T, C]; only m < C_t is read, and
+ * those entries must be finite), or s == NULL and the stand-in score
+ *   s[r, m] = fp32( (qbar[r] . kbar[b, kv, m]) * scale )
+ * is formed from qbar (fp32 [b, hkv, T, head_dim]) and kbar ([b, hkv,
+ * kbar_ld, head_dim] in kbar_dtype, kbar_ld >= C), the dot product and the
+ * scaling in fp64 (scale = shape->scale, 0 -> 1/sqrt(head_dim)).  The scores
+ * are then written to s_out (fp32 [b, hkv, T, C]; 0 for m >= C_t).
+ *
+ * Outputs, per row:
+ *   lse_s[r]  = log sum_{m < C_t} exp(s_m)             (-inf when C_t = 0)
+ *   idx[r, :] = the min(K, C_t) blocks of largest s, equal scores resolved
+ *               to the lower block index (-0.0 equals +0.0), ascending,
+ *               -1 padded
+ *   logg[r,:] = s_idx - lse_s (fp32; 0 on padded slots)
+ * Uses shape->batch, hkv, head_dim, scale.  C <= 16384.
+ * ---------------------------------------------------------------------- */
+sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset, int K,
+                           const float* s, const float* qbar, const void* kbar,
+                           sas_dtype kbar_dtype, int kbar_ld, float* s_out,
+                           int32_t* idx, float* logg, float* lse_s, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused gated block-sparse forward (picx Eq. 9, 'Kernel Design'):
+ *   o_i = sum_j softmax_j( q_i . k_j * scale + bias_j ) v_j,
+ *   lse[b, h, i] = log sum_j exp( q_i . k_j * scale + bias_j ),
+ * over the keys j of the selected history blocks (bias = logg of the block's
+ * slot) and the causal prefix of the current block (bias 0 = log g0).
+ * logg == NULL computes the ungated form (picx Eq. 2).
+ *   q [b,hq,N,d], k/v [b,hkv,N,d] (shape->dtype); idx/logg [b,hkv,T,K];
+ *   o [b,hq,N,d] (shape->dtype); lse fp32 [b,hq,N].
+ * ---------------------------------------------------------------------- */
+size_t sas_attn_fwd_workspace_size(const sas_shape* shape, int K);
+sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void* k,
+                        const void* v, const int32_t* idx, const float* logg, void* o,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of L = sum dout . o (picx Eq. 5 inner gating; Eq. 6 for ds).
+ *   dq, dk, dv      : gradients of q, k, v (shape->dtype; fp32 accumulation)
+ *   dlogg (optional): fp32 [b,hkv,T,K], sum over the block's keys, all rows of
+ *                     the query block and all G heads of dS_ij; 0 on pads
+ *   ds (optional)   : fp32 [b,hkv,T,T], the selector gradient through the
+ *                     gate softmax over ALL history blocks of the row,
+ *                     ds_m = [m in I] dlogg_m - g_m * sum_{m' in I} dlogg_m',
+ *                     g_m = exp(s_m - lse_s); 0 for m >= t.
+ *                     Needs s [b,hkv,T,T] and lse_s [b,hkv,T] from
+ *                     sas_select_topk.
+ * o and lse are the forward's outputs.  With logg == NULL (ungated) dlogg,
+ * ds, s and lse_s must be NULL.  dq/dk/dv are overwritten.
+ * ---------------------------------------------------------------------- */
+size_t sas_attn_bwd_workspace_size(const sas_shape* shape, int K);
+sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        const int32_t* idx, const float* logg, const float* s,
+                        const float* lse_s, void* dq, void* dk, void* dv, float* dlogg,
+                        float* ds, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Single-token decode (picx Eq. 9 with one query; Eq. 2 when logg == NULL,
+ * the deployed form without gates, evolve.pub review 'Summary').
+ * The new token sits at position L - 1 = shape->seqlen - 1; its current block
+ * is c = (L - 1) / block and the history blocks are m < c.
+ *   q      [b, hq, d]                       (shape->dtype)
+ *   kcache [b, hkv, cache_len, d], vcache the same; cache_len >= L
+ *          (cache_len = 0 means L)
+ *   idx    [b, hkv, K] int32 (ascending, -1 padded, entries >= c ignored)
+ *   logg   [b, hkv, K] fp32 or NULL
+ *   o      [b, hq, d] (shape->dtype);  lse fp32 [b, hq]
+ * Split-K over the selected blocks with an LSE merge; the partials live in
+ * the workspace.
+ * ---------------------------------------------------------------------- */
+size_t sas_decode_workspace_size(const sas_shape* shape, int K);
+sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* q,
+                      const void* kcache, const void* vcache, const int32_t* idx,
+                      const float* logg, void* o, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (not part of the method).  When enabled, every kernel the
+ * library enqueues is bracketed by a pair of HIP events recorded on the same
+ * stream; sas_profiler_read synchronises those events and returns, per kernel
+ * name, the launch count and the summed duration.  Process-global state.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  char name[48];
+  long long launches;
+  double total_ms;
+} sas_kernel_time;
+
+void sas_profiler_enable(int on);
+void sas_profiler_reset(void);
+/* Writes up to max_entries entries, returns the number of distinct kernels. */
+int sas_profiler_read(sas_kernel_time* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H */

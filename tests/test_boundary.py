@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/sas.h declares, and rejects bad arguments before
+launching anything (these calls return from the host-side checks)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from gated_block_sparse_scores_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "sas.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert "sas_select_topk" in names and "sas_decode" in names
+    lib = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert L.sas_version() >= 100
+    assert L.status_string(L.SAS_OK) == "ok"
+    assert "workspace" in L.status_string(L.SAS_ERR_WORKSPACE)
+
+
+def shape(**kw):
+    base = dict(batch=1, hq=4, hkv=2, seqlen=256, head_dim=128, block=64,
+                dtype=L.SAS_DTYPE_BF16, scale=0.0)
+    base.update(kw)
+    return L.sas_shape(*base.values())
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails its host-side checks
+
+
+def fwd(sh, K=4, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, logg=FAKE, o=FAKE, lse=FAKE)
+    p.update(ptrs)
+    return L.lib().sas_attn_fwd(C.byref(sh), K, p["q"], p["k"], p["v"], p["idx"], p["logg"],
+                                p["o"], p["lse"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), L.SAS_ERR_INVALID_ARG),
+    (dict(batch=0), L.SAS_ERR_INVALID_ARG),
+    (dict(seqlen=-1), L.SAS_ERR_INVALID_ARG),
+    (dict(head_dim=96), L.SAS_ERR_UNSUPPORTED),
+    (dict(block=48), L.SAS_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.SAS_ERR_INVALID_ARG),
+    (dict(scale=-1.0), L.SAS_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_bad_shapes(kw, status):
+    assert fwd(shape(**kw), q=None) in (status, L.SAS_ERR_INVALID_ARG)
+    assert fwd(shape(**kw)) == status
+
+
+def test_fwd_rejects_null_and_misaligned_pointers_and_bad_K():
+    sh = shape()
+    for name in ("q", "k", "v", "idx", "o", "lse"):
+        assert fwd(sh, **{name: None}) == L.SAS_ERR_INVALID_ARG
+    assert fwd(sh, q=FAKE + 2) == L.SAS_ERR_INVALID_ARG
+    assert fwd(sh, K=0) == L.SAS_ERR_INVALID_ARG
+    assert fwd(sh, K=65) == L.SAS_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_query_and_checks():
+    sh = shape(seqlen=8192, hq=32, hkv=8)
+    n = L.lib().sas_attn_bwd_workspace_size(C.byref(sh), 31)
+    # D (b*hq*N fp32) dominates; CSR and dlogg partials are small
+    assert n >= 32 * 8192 * 4
+    assert n < 32 * 8192 * 4 + (1 << 21)
+    args = [FAKE] * 16
+    # missing workspace
+    st = L.lib().sas_attn_bwd(C.byref(sh), 31, *args[:13], None, None, None, 0, None)
+    assert st == L.SAS_ERR_WORKSPACE
+    # too small workspace
+    st = L.lib().sas_attn_bwd(C.byref(sh), 31, *args[:13], None, None, FAKE, n - 1, None)
+    assert st == L.SAS_ERR_WORKSPACE
+    # ds without s
+    a = list(args)
+    a[8] = None  # s
+    st = L.lib().sas_attn_bwd(C.byref(sh), 31, *a[:13], None, FAKE, FAKE, n, None)
+    assert st == L.SAS_ERR_INVALID_ARG
+    # ungated with selector outputs requested
+    a = list(args)
+    a[7] = None  # logg
+    st = L.lib().sas_attn_bwd(C.byref(sh), 31, *a[:13], FAKE, FAKE, FAKE, n, None)
+    assert st == L.SAS_ERR_INVALID_ARG
+
+
+def test_select_checks():
+    sh = shape()
+    lib = L.lib()
+    # no scores and no stand-in inputs
+    assert lib.sas_select_topk(C.byref(sh), 4, 4, 0, 2, None, None, None, 0, 4, None, FAKE,
+                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+    # kbar_ld smaller than C
+    assert lib.sas_select_topk(C.byref(sh), 1, 8, 8, 2, None, FAKE, FAKE, 0, 7, FAKE, FAKE,
+                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+    assert lib.sas_select_topk(C.byref(sh), 4, 20000, 0, 2, FAKE, None, None, 0, 0, None, FAKE,
+                               FAKE, FAKE, None) == L.SAS_ERR_UNSUPPORTED
+    assert lib.sas_select_topk(C.byref(sh), 4, 4, 0, 0, FAKE, None, None, 0, 0, None, FAKE,
+                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+
+
+def test_decode_checks():
+    sh = shape(seqlen=1000, hq=32, hkv=8)
+    lib = L.lib()
+    need = lib.sas_decode_workspace_size(C.byref(sh), 31)
+    assert need > 0
+    call = lambda sh_, cl, ws, n: lib.sas_decode(C.byref(sh_), cl, 31, FAKE, FAKE, FAKE, FAKE,
+                                                 FAKE, FAKE, FAKE, ws, n, None)
+    assert call(sh, 999, FAKE, need) == L.SAS_ERR_INVALID_ARG        # cache shorter than L
+    assert call(sh, 0, FAKE, need - 4) == L.SAS_ERR_WORKSPACE
+    assert call(shape(seqlen=1000, hq=36, hkv=4), 0, FAKE, 1 << 30) == L.SAS_ERR_UNSUPPORTED
+
+
+def test_pool_checks():
+    sh = shape()
+    lib = L.lib()
+    assert lib.sas_block_pool(C.byref(sh), FAKE, 6, 4, 0, FAKE, None) == L.SAS_ERR_INVALID_ARG
+    assert lib.sas_block_pool(C.byref(sh), None, 4, 4, 0, FAKE, None) == L.SAS_ERR_INVALID_ARG
+    assert lib.sas_block_pool(C.byref(shape(head_dim=80)), FAKE, 4, 4, 0, FAKE,
+                              None) == L.SAS_ERR_UNSUPPORTED
+
+
+def test_profiler_is_inert_when_off():
+    L.sas_profiler_enable(False)
+    L.sas_profiler_reset()
+    assert L.sas_profiler_read() == {}

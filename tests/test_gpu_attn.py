@@ -1,0 +1,210 @@
+"""GPU parity of the fused gated block-sparse forward and backward (C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import sas_oracle as O
+from tests._gpu_helpers import (GATE_ATOL, max_abs, np64, rel_l2, say, tols)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_gpu(x, K, bs, gated=True, s_for_ds=True):
+    """Select (given s) + forward + backward on the device."""
+    from gated_block_sparse_scores_amd import ops
+    g = {k_: (v_.to(DEV) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in x.items()}
+    b, hkv = g["k"].shape[:2]
+    T = g["s"].shape[2]
+    idx, logg, lse_s, _ = ops.select_topk(b, hkv, T, T, K, s=g["s"])
+    lg = logg if gated else None
+    o, lse = ops.attn_fwd(g["q"], g["k"], g["v"], idx, lg, bs)
+    gr = ops.attn_bwd(g["q"], g["k"], g["v"], o, g["dout"], lse, idx, lg,
+                      g["s"] if gated else None, lse_s if gated else None, bs,
+                      want_ds=gated and s_for_ds)
+    torch.cuda.synchronize()
+    return dict(idx=idx, logg=logg, lse_s=lse_s, o=o, lse=lse, **gr)
+
+
+def small_inputs(seed, b, hq, hkv, n, d, bs, K, dtype, std=1.0):
+    w = synth.workload(1, batch=b, hq=hq, hkv=hkv, seqlen=n, head_dim=d, block=bs, topk=K,
+                       dtype="f32" if dtype == torch.float32 else "bf16", qkv_std=std)
+    x = synth.train_inputs(w, seed=seed, poison_invalid_scores=False)
+    T = O.n_blocks(n, bs)
+    s = synth.random_scores((b, hkv, T, T), seed=seed + 7)
+    s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
+    x["s"] = s
+    return x
+
+
+def compare_full(x, r, K, bs, dtype, gated=True):
+    atol, rtol = tols(dtype)
+    idx_o, logg_o, lse_s_o = O.select_topk(x["s"], K)
+    np.testing.assert_array_equal(r["idx"].cpu().numpy(), idx_o)
+    lg = logg_o if gated else None
+    o, lse = O.attn_fwd(x["q"], x["k"], x["v"], idx_o, lg, bs)
+    eo, el = max_abs(r["o"].cpu(), o), max_abs(r["lse"].cpu(), lse)
+    gr = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], idx_o, lg if gated else None,
+                    x["s"], lse_s_o, bs) if gated else None
+    if not gated:
+        gr = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], idx_o, None, x["s"], lse_s_o, bs)
+    errs = {"o": eo, "lse": el}
+    for key in ("dq", "dk", "dv"):
+        errs[key] = rel_l2(np64(r[key].cpu()), gr[key])
+    if gated:
+        errs["dlogg"] = rel_l2(np64(r["dlogg"].cpu()), gr["dlogg"])
+        errs["ds"] = rel_l2(np64(r["ds"].cpu()), gr["ds"])
+    say("  errors: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+    assert eo <= atol and el <= atol
+    for key in ("dq", "dk", "dv", "dlogg", "ds"):
+        if key in errs:
+            assert errs[key] <= rtol, key
+    return errs
+
+
+CASES = [
+    # b, hq, hkv, n,   d,  bs, K
+    (1, 1, 1, 256, 64, 16, 4),
+    (1, 4, 2, 200, 64, 16, 3),
+    (2, 4, 1, 130, 128, 32, 2),
+    (1, 8, 2, 300, 128, 64, 3),
+    (1, 5, 1, 257, 128, 64, 2),
+    (1, 4, 4, 64, 128, 64, 1),
+    (1, 2, 1, 1000, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_fwd_bwd_small(case, dtype):
+    b, hq, hkv, n, d, bs, K = case
+    say(f"fwd+bwd {case} {dtype}")
+    x = small_inputs(sum(case), b, hq, hkv, n, d, bs, K, dtype)
+    r = run_gpu(x, K, bs)
+    compare_full(x, r, K, bs, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_ungated_is_block_sparse_attention(dtype):
+    """logg NULL computes picx Eq. 2 (no gates)."""
+    x = small_inputs(3, 1, 4, 2, 192, 128, 64, 2, dtype)
+    r = run_gpu(x, 2, 64, gated=False)
+    compare_full(x, r, 2, 64, dtype, gated=False)
+
+
+def test_tiny_fp32_workload():
+    """seq 256, 1 head, d 64, block 16, K 4, fp32: the whole output and every
+    gradient against the oracle."""
+    w = synth.workload(1)
+    x = synth.train_inputs(w)
+    say("tiny fp32 workload")
+    r = run_gpu(x, w.topk, w.block)
+    compare_full(x, r, w.topk, w.block, torch.float32)
+
+
+def test_repeat_runs_bitwise_equal():
+    x = small_inputs(11, 1, 8, 2, 512, 128, 64, 3, torch.bfloat16)
+    a = run_gpu(x, 3, 64)
+    b_ = run_gpu(x, 3, 64)
+    for key in ("o", "lse", "dq", "dk", "dv", "dlogg", "ds"):
+        assert torch.equal(a[key], b_[key]), key
+
+
+def test_ds_rows_sum_to_zero_and_empty_first_row():
+    x = small_inputs(13, 1, 4, 2, 640, 128, 64, 3, torch.bfloat16)
+    r = run_gpu(x, 3, 64)
+    ds = np64(r["ds"].cpu())
+    scale = np.abs(ds).max()
+    assert np.abs(ds.sum(-1)).max() <= 1e-5 * scale
+    assert np.all(ds[..., 0, :] == 0)
+    T = ds.shape[-1]
+    assert np.all(ds[..., np.triu(np.ones((T, T), dtype=bool))] == 0)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+def run_workload(wl):
+    from gated_block_sparse_scores_amd import ops
+    w = synth.workload(wl)
+    x = synth.train_inputs(w, device=DEV)
+    T = w.nblocks
+    if w.scores == "standin":
+        qb = ops.block_pool(x["q"], w.block, w.group)
+        kb = ops.block_pool(x["k"], w.block, 1)
+        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, w.topk, qbar=qb, kbar=kb)
+    else:
+        s = x["s"]
+        idx, logg, lse_s, _ = ops.select_topk(w.batch, w.hkv, T, T, w.topk, s=s)
+    o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block)
+    gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s, w.block)
+    torch.cuda.synchronize()
+    return w, x, dict(idx=idx, logg=logg, lse_s=lse_s, s=s, o=o, lse=lse, **gr)
+
+
+@pytest.mark.parametrize("wl", [2, 3])
+def test_training_workload_sampled(wl):
+    """Full-size training workloads (8K tokens / 32K tokens, 32/8 heads, d 128,
+    block 64).  The oracle recomputes sampled query blocks (o, LSE, dq, dlogg,
+    ds) and sampled key blocks (dk, dv) on the device's selection, which is
+    itself checked against the oracle's Top-K of the same fp32 scores."""
+    say(f"training workload {wl}")
+    w, x, r = run_workload(wl)
+    T = w.nblocks
+    s = r["s"].cpu()
+    s_np = s.numpy()
+    oi, ol, ols = O.select_topk(s_np, w.topk)
+    np.testing.assert_array_equal(r["idx"].cpu().numpy(), oi)
+    assert max_abs(r["logg"].cpu().numpy(), ol) <= GATE_ATOL
+    xc = {k_: x[k_].cpu() for k_ in ("q", "k", "v", "dout")}
+    scale = O.default_scale(w.head_dim)
+    rng = np.random.default_rng(wl)
+    tsamp = sorted({0, 1, T // 2, T - 1, *rng.integers(0, T, 3).tolist()})
+    g = w.group
+    o_gpu, lse_gpu, dq_gpu = r["o"].cpu(), r["lse"].cpu(), r["dq"].cpu()
+    ds_gpu, dl_gpu = r["ds"].cpu().numpy(), r["dlogg"].cpu().numpy()
+    errs = {"o": 0.0, "lse": 0.0}
+    dq_num = dq_den = dl_num = dl_den = ds_num = ds_den = 0.0
+    for kv in (0, w.hkv - 1):
+        for t in tsamp:
+            lo, hi = O.block_span(t, w.block, w.seqlen)
+            ob, lb, _, _ = O.fwd_row_block(xc["q"], xc["k"], xc["v"], oi, ol, w.block, scale, 0,
+                                           kv, t)
+            hs = slice(kv * g, (kv + 1) * g)
+            errs["o"] = max(errs["o"], max_abs(o_gpu[0, hs, lo:hi], ob))
+            errs["lse"] = max(errs["lse"], max_abs(lse_gpu[0, hs, lo:hi], lb))
+            dqb, dlb, _ = O.bwd_row_block(xc["q"], xc["k"], xc["v"], xc["dout"], oi, ol, w.block,
+                                          scale, 0, kv, t)
+            dq_num += np.sum((np64(dq_gpu[0, hs, lo:hi]) - dqb) ** 2)
+            dq_den += np.sum(dqb ** 2)
+            dl_num += np.sum((dl_gpu[0, kv, t] - dlb) ** 2)
+            dl_den += np.sum(dlb ** 2)
+            if t > 0:
+                dsr = O.ds_row(s_np[0, kv, t, :t], ols[0, kv, t], oi[0, kv, t], dlb)
+                ds_num += np.sum((ds_gpu[0, kv, t, :t] - dsr) ** 2)
+                ds_den += np.sum(dsr ** 2)
+    dk_num = dk_den = dv_num = dv_den = 0.0
+    dk_gpu, dv_gpu = r["dk"].cpu(), r["dv"].cpu()
+    for kv in (0, w.hkv - 1):
+        for m in sorted({0, T // 3, T - 2}):
+            dkb, dvb = O.bwd_key_block(xc["q"], xc["k"], xc["v"], xc["dout"], oi, ol, w.block,
+                                       scale, 0, kv, m)
+            lo, hi = O.block_span(m, w.block, w.seqlen)
+            dk_num += np.sum((np64(dk_gpu[0, kv, lo:hi]) - dkb) ** 2)
+            dk_den += np.sum(dkb ** 2)
+            dv_num += np.sum((np64(dv_gpu[0, kv, lo:hi]) - dvb) ** 2)
+            dv_den += np.sum(dvb ** 2)
+    for name, num, den in (("dq", dq_num, dq_den), ("dlogg", dl_num, dl_den),
+                           ("ds", ds_num, ds_den), ("dk", dk_num, dk_den),
+                           ("dv", dv_num, dv_den)):
+        errs[name] = math.sqrt(num / den)
+    say("  sampled errors: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+    assert errs["o"] <= 2e-2 and errs["lse"] <= 2e-2
+    for name in ("dq", "dlogg", "ds", "dk", "dv"):
+        assert errs[name] <= 3e-2, name
+    # invariants over every row
+    ds_all = np64(r["ds"])
+    assert np.abs(ds_all.sum(-1)).max() <= 1e-5 * np.abs(ds_all).max()
+    assert torch.isfinite(r["dq"]).all() and torch.isfinite(r["dk"]).all()
