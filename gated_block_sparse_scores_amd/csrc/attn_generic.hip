@@ -247,49 +247,64 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ o,
 }
 
 // Inverse selection map: for key block m of (b, kv), the query blocks t > m
-// that selected it, ascending in t, as entries (t << 8) | slot.
-__global__ void __launch_bounds__(256) csr_count_kernel(const int32_t* __restrict__ idx, int T,
-                                                        int K, size_t nbk,
-                                                        int* __restrict__ count) {
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= nbk * T) return;
-  const size_t bk = gid / T;
-  const int m = (int)(gid % T);
-  const int32_t* base = idx + bk * (size_t)T * K;
-  int c = 0;
-  for (int t = m + 1; t < T; ++t)
-    for (int s = 0; s < K; ++s) c += base[(size_t)t * K + s] == m;
-  count[gid] = c;
+// that selected it, ascending in t, as entries (t << 8) | slot.  Built in three
+// steps: clear a T x T bitmap per (b, kv); set bit (m, t) for every selection;
+// then, one workgroup per (b, kv), count bits per m, scan, and list the set bits
+// of each m in ascending t (the slot is found in the row's ascending idx).
+__global__ void __launch_bounds__(256) csr_clear_kernel(uint32_t* __restrict__ bm, size_t words) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < words) bm[i] = 0u;
 }
 
-__global__ void __launch_bounds__(256) csr_scan_kernel(const int* __restrict__ count, int T,
-                                                       int K, int* __restrict__ off) {
+__global__ void __launch_bounds__(256) csr_mark_kernel(const int32_t* __restrict__ idx, int T,
+                                                       int K, int W, size_t entries,
+                                                       uint32_t* __restrict__ bm) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= entries) return;
+  const size_t row = i / K;          // (bk, t)
+  const int t = (int)(row % T);
+  const size_t bk = row / T;
+  const int m = idx[i];
+  if (m >= 0 && m < t) atomicOr(&bm[(bk * T + m) * W + (t >> 5)], 1u << (t & 31));
+}
+
+__global__ void __launch_bounds__(256) csr_build_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int K, int W,
+                                                        const uint32_t* __restrict__ bm,
+                                                        int* __restrict__ count,
+                                                        int* __restrict__ off,
+                                                        int* __restrict__ list) {
   __shared__ int scr[16];
   const size_t bk = blockIdx.x;
   int carry = (int)(bk * (size_t)T * K);
   for (int m0 = 0; m0 < T; m0 += blockDim.x) {
     const int m = m0 + threadIdx.x;
-    const int c = m < T ? count[bk * T + m] : 0;
+    const uint32_t* bits = bm + (bk * T + (m < T ? m : 0)) * W;
+    int c = 0;
+    if (m < T)
+      for (int w = 0; w < W; ++w) c += __popc(bits[w]);
     int total;
     const int ex = block_excl_scan(c, scr, &total);
-    if (m < T) off[bk * T + m] = carry + ex;
+    if (m < T) {
+      const int base = carry + ex;
+      count[bk * T + m] = c;
+      off[bk * T + m] = base;
+      int pos = base;
+      for (int w = 0; w < W; ++w) {
+        uint32_t word = bits[w];
+        while (word) {
+          const int bit = __ffs(word) - 1;
+          word &= word - 1u;
+          const int t = w * 32 + bit;
+          const int32_t* ir = idx + (bk * T + t) * (size_t)K;
+          int slot = 0;
+          while (slot < K && ir[slot] != m) ++slot;
+          list[pos++] = (t << 8) | slot;
+        }
+      }
+    }
     carry += total;
   }
-}
-
-__global__ void __launch_bounds__(256) csr_fill_kernel(const int32_t* __restrict__ idx, int T,
-                                                       int K, size_t nbk,
-                                                       const int* __restrict__ off,
-                                                       int* __restrict__ list) {
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= nbk * T) return;
-  const size_t bk = gid / T;
-  const int m = (int)(gid % T);
-  const int32_t* base = idx + bk * (size_t)T * K;
-  int pos = off[gid];
-  for (int t = m + 1; t < T; ++t)
-    for (int s = 0; s < K; ++s)
-      if (base[(size_t)t * K + s] == m) list[pos++] = (t << 8) | s;
 }
 
 // ---------------------------------------------------------------- backward: dq + dlogg
@@ -573,6 +588,8 @@ BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base) {
   w.csr_off = (int*)take(rows * sizeof(int));
   w.csr_list = (int*)take(rows * (size_t)dm.K * sizeof(int));
   w.dlogg_part = (float*)take(rows * (size_t)bwd_dlogg_chunks(dm) * dm.K * sizeof(float));
+  w.csr_words = (size_t)(dm.T + 31) / 32;
+  w.csr_bits = (uint32_t*)take(rows * w.csr_words * sizeof(uint32_t));
   w.bytes = off;
   return w;
 }
@@ -599,21 +616,23 @@ hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, cons
     if (e != hipSuccess) return e;
   }
   const size_t nbk = (size_t)dm.b * dm.hkv;
-  const unsigned g = (unsigned)((nbk * dm.T + 255) / 256);
+  const int W = (int)ws.csr_words;
+  const size_t words = nbk * dm.T * W;
+  const size_t entries = nbk * dm.T * dm.K;
   {
-    ProfScope ps("csr_count", st);
-    hipLaunchKernelGGL(csr_count_kernel, dim3(g), dim3(256), 0, st, idx, dm.T, dm.K, nbk,
-                       ws.csr_count);
+    ProfScope ps("csr_clear", st);
+    hipLaunchKernelGGL(csr_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                       ws.csr_bits, words);
   }
   {
-    ProfScope ps("csr_scan", st);
-    hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)nbk), dim3(256), 0, st, ws.csr_count,
-                       dm.T, dm.K, ws.csr_off);
+    ProfScope ps("csr_mark", st);
+    hipLaunchKernelGGL(csr_mark_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0,
+                       st, idx, dm.T, dm.K, W, entries, ws.csr_bits);
   }
   {
-    ProfScope ps("csr_fill", st);
-    hipLaunchKernelGGL(csr_fill_kernel, dim3(g), dim3(256), 0, st, idx, dm.T, dm.K, nbk,
-                       ws.csr_off, ws.csr_list);
+    ProfScope ps("csr_build", st);
+    hipLaunchKernelGGL(csr_build_kernel, dim3((unsigned)nbk), dim3(256), 0, st, idx, dm.T, dm.K,
+                       W, ws.csr_bits, ws.csr_count, ws.csr_off, ws.csr_list);
   }
   return hipGetLastError();
 }

@@ -1,14 +1,15 @@
 // Fused gated block-sparse forward with bf16 MFMA (gfx950): head_dim 128,
-// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv in {4, 8}.
+// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv a multiple of 4.
 //
 // picx.dev summary of SAS, 'Key Idea' Eq. 9 and 'Kernel Design': logits of
 // the selected blocks get their normalised log gate, the current block gets 0
 // (g0 = 1), unselected blocks are never loaded, the softmax is online and no
 // attention matrix is stored.
 //
-// Work unit: one (batch, KV head, query block) tile = G heads x 64 query rows;
-// every K/V block it needs is gathered once into LDS and serves all G heads
-// (one selection per KV head).  Wave w owns head kv*G + w and its 64 rows.
+// Work unit: one (batch, KV head, query block, 4-head chunk) tile = 4 heads x
+// 64 query rows; every K/V block it needs is gathered once into LDS and serves
+// the 4 heads (one selection per KV head).  Wave w owns head kv*G + 4*chunk + w
+// and its 64 rows.
 //   S^T = K Q^T   (32x32x16 MFMA; A = K rows from LDS, B = Q rows held in
 //                  registers), so each lane holds one query column and the
 //                  softmax max/sum over keys stays inside the lane (plus one
@@ -35,9 +36,10 @@ constexpr int VLD = BS + 4;  // V^T row stride in LDS (bf16 elements): 136 B
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-template <int G>
+constexpr int HPW = 4;  // heads (waves) per workgroup
+
 struct Stage {
-  static constexpr int NT = 64 * G;
+  static constexpr int NT = 64 * HPW;
   static constexpr int KCH = (BS * D / 8) / NT;   // 16-byte K chunks per thread
   static constexpr int VUN = (BS / 2) * (D / 8) / NT;  // (key pair, 8 dims) units per thread
   uint4 kreg[KCH];
@@ -85,8 +87,7 @@ struct Stage {
   }
 };
 
-template <int G>
-__global__ void __launch_bounds__(64 * G) fwd_mfma_kernel(
+__global__ void __launch_bounds__(64 * HPW) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, bf16_t* __restrict__ o, float* __restrict__ lse) {
@@ -96,14 +97,17 @@ __global__ void __launch_bounds__(64 * G) fwd_mfma_kernel(
   __shared__ float bbias[65];
   __shared__ int nblk;
 
+  const int nchunk = dm.g / HPW;
   int tile = blockIdx.x;
   const int kv = tile % dm.hkv;
   tile /= dm.hkv;
+  const int chunk = tile % nchunk;
+  tile /= nchunk;
   const int b = tile % dm.b;
   const int t = dm.T - 1 - tile / dm.b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
-  const int h = kv * G + wave;
+  const int h = kv * dm.g + chunk * HPW + wave;
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
   if (threadIdx.x == 0) {
@@ -147,7 +151,7 @@ __global__ void __launch_bounds__(64 * G) fwd_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  Stage<G> st;
+  Stage st;
   st.load(kbase + (size_t)blist[0] * BS * D, vbase + (size_t)blist[0] * BS * D);
 
   for (int bi = 0; bi < nb; ++bi) {
@@ -255,22 +259,17 @@ __global__ void __launch_bounds__(64 * G) fwd_mfma_kernel(
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& dm) {
-  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && (dm.g == 4 || dm.g == 8);
+  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0;
 }
 
 hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const int32_t* idx, const float* logg, void* o, float* lse,
                            hipStream_t st) {
-  const size_t tiles = (size_t)dm.b * dm.hkv * dm.T;
+  const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
   ProfScope ps("fwd_mfma", st);
-  if (dm.g == 4)
-    hipLaunchKernelGGL(fwd_mfma_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, st, dm,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
-                       (bf16_t*)o, lse);
-  else
-    hipLaunchKernelGGL(fwd_mfma_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, st, dm,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
-                       (bf16_t*)o, lse);
+  hipLaunchKernelGGL(fwd_mfma_kernel, dim3((unsigned)tiles), dim3(64 * HPW), 0, st, dm,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
+                     (bf16_t*)o, lse);
   return hipGetLastError();
 }
 

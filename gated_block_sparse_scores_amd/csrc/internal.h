@@ -41,6 +41,8 @@ struct BwdWorkspace {
   int* csr_off;      // [b*hkv*T]
   int* csr_list;     // [b*hkv*T*K]  entries (t << 8) | slot
   float* dlogg_part; // [b*hkv*T, nchunk, K]
+  uint32_t* csr_bits;  // [b*hkv*T, csr_words] bitmap (key block m, query block t)
+  size_t csr_words;
   size_t bytes;
 };
 BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base);

@@ -74,6 +74,11 @@ CASES = [
     (1, 5, 1, 257, 128, 64, 2),
     (1, 4, 4, 64, 128, 64, 1),
     (1, 2, 1, 1000, 64, 64, 64),
+    # shapes served by the bf16 MFMA kernels (G % 4 == 0, d 128, block 64, N % 64 == 0)
+    (1, 4, 1, 64, 128, 64, 2),
+    (1, 8, 2, 512, 128, 64, 3),
+    (2, 8, 1, 640, 128, 64, 5),
+    (1, 16, 4, 1024, 128, 64, 16),
 ]
 
 
