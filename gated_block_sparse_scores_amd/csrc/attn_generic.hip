@@ -246,65 +246,24 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ o,
   if (row < rows && sub == 0) Dv[row] = acc;
 }
 
-// Inverse selection map: for key block m of (b, kv), the query blocks t > m
-// that selected it, ascending in t, as entries (t << 8) | slot.  Built in three
-// steps: clear a T x T bitmap per (b, kv); set bit (m, t) for every selection;
-// then, one workgroup per (b, kv), count bits per m, scan, and list the set bits
-// of each m in ascending t (the slot is found in the row's ascending idx).
-__global__ void __launch_bounds__(256) csr_clear_kernel(uint32_t* __restrict__ bm, size_t words) {
+// Inverse selection map: slot[b, kv][m][t] = the Top-K slot of block m in
+// the selection of query block t (0xFF when t did not select m).  Cleared and
+// then marked from idx; the key-major kernels read the row of their key block.
+__global__ void __launch_bounds__(256) slotmap_clear_kernel(uint4* __restrict__ sm, size_t n16) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < words) bm[i] = 0u;
+  if (i < n16) sm[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
 }
 
-__global__ void __launch_bounds__(256) csr_mark_kernel(const int32_t* __restrict__ idx, int T,
-                                                       int K, int W, size_t entries,
-                                                       uint32_t* __restrict__ bm) {
+__global__ void __launch_bounds__(256) slotmap_mark_kernel(const int32_t* __restrict__ idx,
+                                                           int T, int K, size_t entries,
+                                                           uint8_t* __restrict__ sm) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= entries) return;
   const size_t row = i / K;          // (bk, t)
   const int t = (int)(row % T);
   const size_t bk = row / T;
   const int m = idx[i];
-  if (m >= 0 && m < t) atomicOr(&bm[(bk * T + m) * W + (t >> 5)], 1u << (t & 31));
-}
-
-__global__ void __launch_bounds__(256) csr_build_kernel(const int32_t* __restrict__ idx, int T,
-                                                        int K, int W,
-                                                        const uint32_t* __restrict__ bm,
-                                                        int* __restrict__ count,
-                                                        int* __restrict__ off,
-                                                        int* __restrict__ list) {
-  __shared__ int scr[16];
-  const size_t bk = blockIdx.x;
-  int carry = (int)(bk * (size_t)T * K);
-  for (int m0 = 0; m0 < T; m0 += blockDim.x) {
-    const int m = m0 + threadIdx.x;
-    const uint32_t* bits = bm + (bk * T + (m < T ? m : 0)) * W;
-    int c = 0;
-    if (m < T)
-      for (int w = 0; w < W; ++w) c += __popc(bits[w]);
-    int total;
-    const int ex = block_excl_scan(c, scr, &total);
-    if (m < T) {
-      const int base = carry + ex;
-      count[bk * T + m] = c;
-      off[bk * T + m] = base;
-      int pos = base;
-      for (int w = 0; w < W; ++w) {
-        uint32_t word = bits[w];
-        while (word) {
-          const int bit = __ffs(word) - 1;
-          word &= word - 1u;
-          const int t = w * 32 + bit;
-          const int32_t* ir = idx + (bk * T + t) * (size_t)K;
-          int slot = 0;
-          while (slot < K && ir[slot] != m) ++slot;
-          list[pos++] = (t << 8) | slot;
-        }
-      }
-    }
-    carry += total;
-  }
+  if (m >= 0 && m < t) sm[(bk * T + m) * (size_t)T + t] = (uint8_t)(i % K);
 }
 
 // ---------------------------------------------------------------- backward: dq + dlogg
@@ -401,14 +360,16 @@ template <typename T, int D, int BS>
 __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
     Dims dm, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
-    const float* __restrict__ logg, const int* __restrict__ csr_count,
-    const int* __restrict__ csr_off, const int* __restrict__ csr_list, T* __restrict__ dk,
+    const float* __restrict__ logg, const uint8_t* __restrict__ slotmap, T* __restrict__ dk,
     T* __restrict__ dv) {
   constexpr int P = D / 32;
   constexpr int KC = BS < 32 ? BS : 32;
   __shared__ __align__(16) float Qs[KC][D];
   __shared__ __align__(16) float Os[KC][D];
   __shared__ float Ls[KC], Dl[KC];
+  __shared__ int lst[256];
+  __shared__ int scan_scr[16];
+  __shared__ int lst_n;
 
   const int m = blockIdx.x % dm.T;
   const size_t bk = blockIdx.x / dm.T;
@@ -416,7 +377,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
   const int p = threadIdx.x % P;
   const int jr = threadIdx.x / P;
   const int j = m * BS + jr;
-  const bool kact = j < dm.n;
+  const bool kact = jr < BS && j < dm.n;
 
   float kvk[32], kvv[32], adk[32], adv[32];
   const size_t kvrow = ((size_t)b * dm.hkv + kv) * dm.n + j;
@@ -430,18 +391,26 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
 #pragma unroll
   for (int e = 0; e < 32; ++e) adk[e] = adv[e] = 0.0f;
 
-  const int ncsr = csr_count[bk * dm.T + m];
-  const int off = csr_off[bk * dm.T + m];
-  for (int ei = -1; ei < ncsr; ++ei) {
-    int t, slot;
-    if (ei < 0) {
-      t = m;
-      slot = -1;
-    } else {
-      const int e = csr_list[off + ei];
-      t = e >> 8;
-      slot = e & 255;
+  const uint8_t* srow = slotmap + (bk * dm.T + m) * (size_t)dm.T;
+  // Query blocks attending to block m: t = m (diagonal), then every t > m
+  // whose selection holds m, compacted NTH at a time into LDS.
+  for (int t0 = m; t0 < dm.T; t0 += blockDim.x) {
+    {
+      const int tt = t0 + (int)threadIdx.x;
+      int sl = 0xFF;
+      if (tt == m) sl = 0xFE;
+      else if (tt < dm.T) sl = srow[tt];
+      const int flag = sl != 0xFF;
+      int cnt;
+      const int pos = block_excl_scan(flag, scan_scr, &cnt);
+      if (flag) lst[pos] = (tt << 8) | sl;
+      if (threadIdx.x == 0) lst_n = cnt;
+      __syncthreads();
     }
+    const int ne = lst_n;
+  for (int ei = 0; ei < ne; ++ei) {
+    const int t = lst[ei] >> 8;
+    const int slot = (lst[ei] & 255) == 0xFE ? -1 : (lst[ei] & 255);
     const float bias =
         (slot >= 0 && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] : 0.0f;
     for (int hh = 0; hh < dm.g; ++hh) {
@@ -471,6 +440,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
         __syncthreads();
       }
     }
+  }
   }
   if (kact) {
     store_row_slice<T, D>(dk + kvrow * D, p, adk, dm.scale);
@@ -542,10 +512,10 @@ hipError_t bwd_generic_typed(const Dims& dm, const void* q, const void* k, const
   {
     const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
     ProfScope ps("bwd_dkdv_generic", st);
-    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D, BS>), dim3((unsigned)wgs),
-                       dim3(BS * (D / 32)), 0, st, dm, (const T*)q, (const T*)k, (const T*)v,
-                       (const T*)dout, lse, ws.D, logg, ws.csr_count, ws.csr_off, ws.csr_list,
-                       (T*)dk, (T*)dv);
+    const int threads = BS * (D / 32) < 64 ? 64 : BS * (D / 32);
+    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D, BS>), dim3((unsigned)wgs), dim3(threads),
+                       0, st, dm, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse,
+                       ws.D, logg, ws.slotmap, (T*)dk, (T*)dv);
   }
   return hipGetLastError();
 }
@@ -584,12 +554,9 @@ BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base) {
     return r;
   };
   w.D = (float*)take((size_t)dm.b * dm.hq * dm.n * sizeof(float));
-  w.csr_count = (int*)take(rows * sizeof(int));
-  w.csr_off = (int*)take(rows * sizeof(int));
-  w.csr_list = (int*)take(rows * (size_t)dm.K * sizeof(int));
   w.dlogg_part = (float*)take(rows * (size_t)bwd_dlogg_chunks(dm) * dm.K * sizeof(float));
-  w.csr_words = (size_t)(dm.T + 31) / 32;
-  w.csr_bits = (uint32_t*)take(rows * w.csr_words * sizeof(uint32_t));
+  w.slotmap_bytes = align256(rows * (size_t)dm.T);
+  w.slotmap = (uint8_t*)take(w.slotmap_bytes);
   w.bytes = off;
   return w;
 }
@@ -615,24 +582,17 @@ hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t nbk = (size_t)dm.b * dm.hkv;
-  const int W = (int)ws.csr_words;
-  const size_t words = nbk * dm.T * W;
-  const size_t entries = nbk * dm.T * dm.K;
+  const size_t entries = (size_t)dm.b * dm.hkv * dm.T * dm.K;
   {
-    ProfScope ps("csr_clear", st);
-    hipLaunchKernelGGL(csr_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
-                       ws.csr_bits, words);
+    ProfScope ps("slotmap_clear", st);
+    const size_t n16 = ws.slotmap_bytes / 16;
+    hipLaunchKernelGGL(slotmap_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0,
+                       st, (uint4*)ws.slotmap, n16);
   }
   {
-    ProfScope ps("csr_mark", st);
-    hipLaunchKernelGGL(csr_mark_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0,
-                       st, idx, dm.T, dm.K, W, entries, ws.csr_bits);
-  }
-  {
-    ProfScope ps("csr_build", st);
-    hipLaunchKernelGGL(csr_build_kernel, dim3((unsigned)nbk), dim3(256), 0, st, idx, dm.T, dm.K,
-                       W, ws.csr_bits, ws.csr_count, ws.csr_off, ws.csr_list);
+    ProfScope ps("slotmap_mark", st);
+    hipLaunchKernelGGL(slotmap_mark_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256),
+                       0, st, idx, dm.T, dm.K, entries, ws.slotmap);
   }
   return hipGetLastError();
 }

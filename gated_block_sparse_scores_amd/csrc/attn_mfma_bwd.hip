@@ -7,20 +7,21 @@
 // recomputed from the saved LSE instead of being stored ('Kernel Design').
 //
 // Two kernels, no floating-point atomics (results are bitwise reproducible):
-//  * dK/dV (key-major): one workgroup of two waves per (batch, KV head, key
-//    block m); wave w owns keys 32w..32w+31 of the block with K, V held in
-//    registers and dK^T, dV^T accumulated in registers.  It visits the
-//    diagonal query block t = m and then every query block that selected m
-//    (inverse selection list, ascending t), for each of the G heads, staging
-//    that head's 64 rows of q and dout in LDS twice: row-major (A operand of
-//    S = Q K^T and dP = dO V^T) and transposed (A operand of dK^T = Q^T dS and
-//    dV^T = dO^T P).  Since block m is the only owner of the (t, slot) pairs
-//    that selected it, it also writes dlogg[t][slot] (sum over G heads, 64
-//    rows and 64 keys) directly.
-//  * dQ (query-major): the forward's tiling (4 heads x 64 rows per
-//    workgroup), recomputing S^T = K Q^T and dP^T = V dO^T per selected block
-//    and accumulating dQ^T += K^T dS^T, with K staged row-major and
-//    transposed and V row-major in LDS.
+//  * dK/dV (key-major): one workgroup of four waves per (batch, KV head, key
+//    block m).  Wave w owns keys 32*(w%2)..+32 of the block (K, V fragments in
+//    registers) and query rows 32*(w/2)..+32 of every visited query tile; its
+//    partial dK^T, dV^T stay in registers and the two query halves are summed
+//    through LDS at the end.  The workgroup visits the diagonal query block
+//    t = m and every later query block whose selection holds m (read from the
+//    slot map, compacted 256 at a time), for each of the G heads, staging that
+//    head's 64 rows of q and dout in LDS row-major (A operand of S = Q K^T and
+//    dP = dO V^T) and transposed (A operand of dK^T = Q^T dS, dV^T = dO^T P).
+//    Block m is the only owner of the (t, slot) pairs that selected it, so it
+//    also writes dlogg[t][slot] (sum over G heads, 64 rows, 64 keys) directly.
+//  * dQ (query-major): the forward's tiling (4 heads x 64 rows per workgroup,
+//    eight waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
+//    selected block and accumulating dQ^T += K^T dS^T, with K staged row-major
+//    and transposed and V row-major in LDS.
 #include <math.h>
 
 #include "common.h"
@@ -86,6 +87,44 @@ __device__ __forceinline__ void stage_rows(const bf16_t* __restrict__ src, bf16_
   }
 }
 
+// Register-staged copy of 64 rows x 128 dims (row pairs x 8-dim groups),
+// loaded from global memory ahead of use and written to LDS later, both
+// row-major (stride RLD) and, optionally, transposed (stride TLD).
+template <int NT>
+struct RowPairs {
+  static constexpr int UN = (BS / 2) * (D / 8) / NT;
+  uint4 ra[UN], rb[UN];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ src) {
+#pragma unroll
+    for (int i = 0; i < UN; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int dg = u & 15, rp = u >> 4;
+      ra[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp) * D + dg * 8);
+      rb[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp + 1) * D + dg * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* rowm, bf16_t* trans) const {
+#pragma unroll
+    for (int i = 0; i < UN; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int dg = u & 15, rp = u >> 4;
+      *reinterpret_cast<uint4*>(rowm + (2 * rp) * RLD + dg * 8) = ra[i];
+      *reinterpret_cast<uint4*>(rowm + (2 * rp + 1) * RLD + dg * 8) = rb[i];
+      if (trans) {
+        const uint32_t a[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+        const uint32_t b[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
+          const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+          *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w) * TLD + 2 * rp) = lo;
+          *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w + 1) * TLD + 2 * rp) = hi;
+        }
+      }
+    }
+  }
+};
+
 __device__ __forceinline__ bf16x8 lds8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -98,21 +137,27 @@ __device__ __forceinline__ bf16x8 trans_frag(const bf16_t* tile, int row, int ch
 }
 
 // ---------------------------------------------------------------- dK / dV
-constexpr int DKV_NT = 128;
+constexpr int DKV_NT = 256;
+constexpr int DKV_MAXT = 8192;  // longest inverse list (query blocks) held in LDS
+constexpr int TILE_BYTES_R = BS * RLD * 2;   // one row-major 64 x 128 tile
+constexpr int TILE_BYTES_T = D * TLD * 2;    // one transposed 128 x 64 tile
+constexpr int DKV_SMEM = 2 * TILE_BYTES_R + 2 * TILE_BYTES_T;
 
 __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ Dv,
-    const float* __restrict__ logg, const int* __restrict__ csr_count,
-    const int* __restrict__ csr_off, const int* __restrict__ csr_list,
+    const float* __restrict__ logg, const uint8_t* __restrict__ slotmap,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg) {
-  __shared__ __align__(16) bf16_t Qs[BS * RLD];
-  __shared__ __align__(16) bf16_t Os[BS * RLD];
-  __shared__ __align__(16) bf16_t Qt[D * TLD];
-  __shared__ __align__(16) bf16_t Ot[D * TLD];
+  __shared__ __align__(16) unsigned char smem[DKV_SMEM];
+  bf16_t* Qs = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* Os = reinterpret_cast<bf16_t*>(smem + TILE_BYTES_R);
+  bf16_t* Qt = reinterpret_cast<bf16_t*>(smem + 2 * TILE_BYTES_R);
+  bf16_t* Ot = reinterpret_cast<bf16_t*>(smem + 2 * TILE_BYTES_R + TILE_BYTES_T);
   __shared__ float Ls[BS], Dl[BS];
-  __shared__ float red[2];
+  __shared__ float red[4];
+  __shared__ int lst[DKV_MAXT];
+  __shared__ int scan_scr[16];
 
   // key blocks ascending (low blocks are selected by the most query blocks, so
   // the longest inverse lists go first), KV head fastest
@@ -124,7 +169,8 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
   const size_t bk = (size_t)b * dm.hkv + kv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
-  const int key = wave * 32 + c;  // key within the block owned by this lane's column
+  const int kt = wave & 1, qh = wave >> 1;
+  const int key = kt * 32 + c;  // key within the block (this lane's column)
 
   // K, V of the wave's 32 keys as B operands (column = key, k = dims).
   const size_t kvrow = (bk * dm.n + (size_t)m * BS + key) * D;
@@ -141,106 +187,153 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.0f;
 
   const float sc2 = dm.scale * LOG2E;
-  const int ncsr = csr_count[bk * dm.T + m];
-  const int off = csr_off[bk * dm.T + m];
-  for (int ei = -1; ei < ncsr; ++ei) {
-    int t, slot;
-    if (ei < 0) {
-      t = m;
-      slot = -1;
-    } else {
-      const int e = csr_list[off + ei];
-      t = e >> 8;
-      slot = e & 255;
-    }
-    const bool diag = slot < 0;
-    const float bias2 = (!diag && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] * LOG2E
-                                        : 0.0f;
-    float dlsum = 0.0f;
-    for (int hh = 0; hh < dm.g; ++hh) {
-      const int h = kv * dm.g + hh;
-      const size_t rbase = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
-      __syncthreads();
-      stage_both<DKV_NT>(q + rbase * D, Qs, Qt);
-      stage_both<DKV_NT>(dout + rbase * D, Os, Ot);
-      if (threadIdx.x < BS) {
-        Ls[threadIdx.x] = lse[rbase + threadIdx.x] * LOG2E;
-        Dl[threadIdx.x] = Dv[rbase + threadIdx.x];
-      }
-      __syncthreads();
+  // Query blocks attending to block m, in ascending t: the diagonal t = m,
+  // then every t > m whose selection holds m (slot map row, compacted into
+  // LDS 256 entries per pass).
+  const uint8_t* srow = slotmap + (bk * dm.T + m) * (size_t)dm.T;
+  int ne = 0;
+  for (int t0 = m; t0 < dm.T; t0 += DKV_NT) {
+    const int tt = t0 + (int)threadIdx.x;
+    int sl = 0xFF;
+    if (tt == m)
+      sl = 0xFE;
+    else if (tt < dm.T)
+      sl = srow[tt];
+    const int flag = sl != 0xFF;
+    int cnt;
+    const int pos = block_excl_scan(flag, scan_scr, &cnt);
+    if (flag) lst[ne + pos] = (tt << 8) | sl;
+    ne += cnt;
+  }
+  __syncthreads();
 
-      // S[q][key] and dP[q][key] for the 64 query rows (two 32-row tiles).
-      f32x16 sa[2], pa[2];
+  // Flat loop over (entry, head); the next tile's q / dout rows are loaded
+  // into registers while the current one is computed.
+  const int items = ne * dm.g;
+  RowPairs<DKV_NT> pq, po;
+  float pls = 0.0f, pdl = 0.0f;
+  auto tile_base = [&](int it) {
+    const int t = lst[it / dm.g] >> 8;
+    const int h = kv * dm.g + it % dm.g;
+    return ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
+  };
+  auto prefetch = [&](int it) {
+    const size_t rb = tile_base(it);
+    pq.load(q + rb * D);
+    po.load(dout + rb * D);
+    if (threadIdx.x < BS) {
+      pls = lse[rb + threadIdx.x] * LOG2E;
+      pdl = Dv[rb + threadIdx.x];
+    }
+  };
+  if (items > 0) prefetch(0);
+  float dlsum = 0.0f;
+  for (int it = 0; it < items; ++it) {
+    const int e = it / dm.g;
+    const int t = lst[e] >> 8;
+    const int slot = (lst[e] & 255) == 0xFE ? -1 : (lst[e] & 255);
+    const bool diag = slot < 0;
+    const float bias2 =
+        (!diag && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] * LOG2E : 0.0f;
+    __syncthreads();
+    pq.store(Qs, Qt);
+    po.store(Os, Ot);
+    if (threadIdx.x < BS) {
+      Ls[threadIdx.x] = pls;
+      Dl[threadIdx.x] = pdl;
+    }
+    __syncthreads();
+    if (it + 1 < items) prefetch(it + 1);
+
+    // S[q][key], dP[q][key] for this wave's 32 query rows and 32 keys.
+    f32x16 sa, pa;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+    for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sa[qt][r] = pa[qt][r] = 0.0f;
+    for (int kc = 0; kc < 8; ++kc) {
+      const int ro = (qh * 32 + c) * RLD + kc * 16 + g * 8;
+      sa = mfma32(lds8(Qs + ro), kf[kc], sa);
+      pa = mfma32(lds8(Os + ro), vf[kc], pa);
+    }
+    // P and dS in place: sa <- P, pa <- dS.
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
+    for (int r = 0; r < 16; ++r) {
+      const int qi = qh * 32 + acc_row(r, g);
+      float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Ls[qi]);
+      if (diag && key > qi) p = 0.0f;
+      const float ds = p * (pa[r] - Dl[qi]);
+      sa[r] = p;
+      pa[r] = ds;
+      dlsum += ds;
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over this half's two 16-row chunks.
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const bf16x8 aq = lds8(Qs + (qt * 32 + c) * RLD + kc * 16 + g * 8);
-          const bf16x8 ao = lds8(Os + (qt * 32 + c) * RLD + kc * 16 + g * 8);
-          sa[qt] = mfma32(aq, kf[kc], sa[qt]);
-          pa[qt] = mfma32(ao, vf[kc], pa[qt]);
-        }
-      }
-      // P and dS in place: sa <- P, pa <- dS.
+    for (int ch = 0; ch < 2; ++ch) {
+      const bf16x8 pb = pack8(sa, ch * 8);
+      const bf16x8 db = pack8(pa, ch * 8);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qt * 32 + acc_row(r, g);
-          float p = fast_exp2(fmaf(sa[qt][r], sc2, bias2) - Ls[qi]);
-          if (diag && key > qi) p = 0.0f;
-          const float ds = p * (pa[qt][r] - Dl[qi]);
-          sa[qt][r] = p;
-          pa[qt][r] = ds;
-          dlsum += ds;
-        }
-      // dV^T += dO^T P, dK^T += Q^T dS over four 16-query chunks.
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        const int qt = ch >> 1, half = ch & 1;
-        const bf16x8 pb = pack8(sa[qt], half * 8);
-        const bf16x8 db = pack8(pa[qt], half * 8);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dva[dt] = mfma32(trans_frag(Ot, dt * 32 + c, ch, g), pb, dva[dt]);
-          dka[dt] = mfma32(trans_frag(Qt, dt * 32 + c, ch, g), db, dka[dt]);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        dva[dt] = mfma32(trans_frag(Ot, dt * 32 + c, qh * 2 + ch, g), pb, dva[dt]);
+        dka[dt] = mfma32(trans_frag(Qt, dt * 32 + c, qh * 2 + ch, g), db, dka[dt]);
       }
     }
-    if (!diag && dlogg) {
-      // sum over the workgroup (2 waves) in a fixed order
-      const float ws = wave_sum(dlsum);
-      if (lane == 0) red[wave] = ws;
-      __syncthreads();
-      if (threadIdx.x == 0) dlogg[(bk * dm.T + t) * (size_t)dm.K + slot] = red[0] + red[1];
+    if (it % dm.g == dm.g - 1) {
+      if (!diag && dlogg) {
+        // sum over the workgroup in a fixed order
+        const float ws = wave_sum(dlsum);
+        if (lane == 0) red[wave] = ws;
+        __syncthreads();
+        if (threadIdx.x == 0)
+          dlogg[(bk * dm.T + t) * (size_t)dm.K + slot] = (red[0] + red[1]) + (red[2] + red[3]);
+      }
+      dlsum = 0.0f;
     }
   }
 
-  // dK = scale * dK^T^T, dV: lane holds key `key`, dims dt*32 + acc_row(r, g).
-  bf16_t* dkp = dk + kvrow;
-  bf16_t* dvp = dv + kvrow;
+  // Sum the two query halves through LDS: partial [kt][dk|dv][dt*16 + r][lane].
+  float* part = reinterpret_cast<float*>(smem);
+  __syncthreads();
+  if (qh == 1) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dd = dt * 32 + r4 * 8 + g * 4;
-      uint2 wk, wv;
-      wk.x = pack_bf16x2(dka[dt][r4 * 4] * dm.scale, dka[dt][r4 * 4 + 1] * dm.scale);
-      wk.y = pack_bf16x2(dka[dt][r4 * 4 + 2] * dm.scale, dka[dt][r4 * 4 + 3] * dm.scale);
-      wv.x = pack_bf16x2(dva[dt][r4 * 4], dva[dt][r4 * 4 + 1]);
-      wv.y = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
-      *reinterpret_cast<uint2*>(dkp + dd) = wk;
-      *reinterpret_cast<uint2*>(dvp + dd) = wv;
-    }
+      for (int r = 0; r < 16; ++r) {
+        part[((kt * 2 + 0) * 64 + dt * 16 + r) * 64 + lane] = dka[dt][r];
+        part[((kt * 2 + 1) * 64 + dt * 16 + r) * 64 + lane] = dva[dt][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dka[dt][r] += part[((kt * 2 + 0) * 64 + dt * 16 + r) * 64 + lane];
+        dva[dt][r] += part[((kt * 2 + 1) * 64 + dt * 16 + r) * 64 + lane];
+      }
+    // dK = scale * (dK^T)^T, dV: lane holds key `key`, dims dt*32 + acc_row(r, g).
+    bf16_t* dkp = dk + kvrow;
+    bf16_t* dvp = dv + kvrow;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dd = dt * 32 + r4 * 8 + g * 4;
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(dka[dt][r4 * 4] * dm.scale, dka[dt][r4 * 4 + 1] * dm.scale);
+        wk.y = pack_bf16x2(dka[dt][r4 * 4 + 2] * dm.scale, dka[dt][r4 * 4 + 3] * dm.scale);
+        wv.x = pack_bf16x2(dva[dt][r4 * 4], dva[dt][r4 * 4 + 1]);
+        wv.y = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
+        *reinterpret_cast<uint2*>(dkp + dd) = wk;
+        *reinterpret_cast<uint2*>(dvp + dd) = wv;
+      }
+  }
 }
 
 // ---------------------------------------------------------------- dQ
 constexpr int HPW = 4;
-constexpr int DQ_NT = 64 * HPW;
+constexpr int DQ_NW = 8;
+constexpr int DQ_NT = 64 * DQ_NW;
 
 __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -264,7 +357,9 @@ __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
   const int t = dm.T - 1 - tile / dm.b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
-  const int h = kv * dm.g + chunk * HPW + wave;
+  const int h = kv * dm.g + chunk * HPW + (wave >> 1);
+  const int qt = wave & 1;
+  const int qi = qt * 32 + c;
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
   if (threadIdx.x == 0) {
@@ -283,114 +378,92 @@ __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
     nblk = cnt + 1;
   }
 
-  const size_t rbase = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
-  bf16x8 qf[2][8], of[2][8];
+  const size_t row = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
+  bf16x8 qf[8], of[8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const size_t o = (rbase + qt * 32 + c) * D + kc * 16 + g * 8;
-      qf[qt][kc] = *reinterpret_cast<const bf16x8*>(q + o);
-      of[qt][kc] = *reinterpret_cast<const bf16x8*>(dout + o);
-    }
-  float l2[2], dd_[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    l2[qt] = lse[rbase + qt * 32 + c] * LOG2E;
-    dd_[qt] = Dv[rbase + qt * 32 + c];
+  for (int kc = 0; kc < 8; ++kc) {
+    qf[kc] = *reinterpret_cast<const bf16x8*>(q + row * D + kc * 16 + g * 8);
+    of[kc] = *reinterpret_cast<const bf16x8*>(dout + row * D + kc * 16 + g * 8);
   }
-  f32x16 dqa[4][2];
+  const float l2 = lse[row] * LOG2E;
+  const float dval = Dv[row];
+  f32x16 dqa[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dqa[dt][qt][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) dqa[dt][r] = 0.0f;
   const float sc2 = dm.scale * LOG2E;
 
   __syncthreads();
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
+  RowPairs<DQ_NT> pk, pv;
+  pk.load(kbase + (size_t)blist[0] * BS * D);
+  pv.load(vbase + (size_t)blist[0] * BS * D);
   for (int bi = 0; bi < nb; ++bi) {
     const int m = blist[bi];
-    const float bias2 = bbias[bi];
+    const float off2 = bbias[bi] - l2;
     const bool diag = m == t;
     __syncthreads();
-    stage_both<DQ_NT>(kbase + (size_t)m * BS * D, Ks, Kt);
-    stage_rows<DQ_NT>(vbase + (size_t)m * BS * D, Vs);
+    pk.store(Ks, Kt);
+    pv.store(Vs, nullptr);
     __syncthreads();
-
-    // S^T[key][query], dP^T[key][query]
-    f32x16 sa[2][2], pa[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sa[kt][qt][r] = pa[kt][qt][r] = 0.0f;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ak = lds8(Ks + (kt * 32 + c) * RLD + kc * 16 + g * 8);
-        const bf16x8 av = lds8(Vs + (kt * 32 + c) * RLD + kc * 16 + g * 8);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sa[kt][qt] = mfma32(ak, qf[qt][kc], sa[kt][qt]);
-          pa[kt][qt] = mfma32(av, of[qt][kc], pa[kt][qt]);
-        }
-      }
+    if (bi + 1 < nb) {
+      pk.load(kbase + (size_t)blist[bi + 1] * BS * D);
+      pv.load(vbase + (size_t)blist[bi + 1] * BS * D);
     }
-    // dS^T (in pa)
+
+    // Per 32-key tile: S^T, dP^T (keys x this wave's 32 queries), then dS^T
+    // packed to bf16 as the B operand of the dQ^T update.
+    bf16x8 db[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 sa, pa;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = kt * 32 + acc_row(r, g);
-          float p = fast_exp2(fmaf(sa[kt][qt][r], sc2, bias2) - l2[qt]);
-          if (diag && kk > qt * 32 + c) p = 0.0f;
-          pa[kt][qt][r] = p * (pa[kt][qt][r] - dd_[qt]);
-        }
+      for (int kc = 0; kc < 8; ++kc) {
+        const int ro = (kt * 32 + c) * RLD + kc * 16 + g * 8;
+        sa = mfma32(lds8(Ks + ro), qf[kc], sa);
+        pa = mfma32(lds8(Vs + ro), of[kc], pa);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sa[r], sc2, off2));
+        if (diag && kt * 32 + acc_row(r, g) > qi) p = 0.0f;
+        pa[r] = p * (pa[r] - dval);
+      }
+      db[2 * kt] = pack8(pa, 0);
+      db[2 * kt + 1] = pack8(pa, 8);
+    }
     // dQ^T += K^T dS^T over four 16-key chunks
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int kt = ch >> 1, half = ch & 1;
-      bf16x8 db[2];
+    for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) db[qt] = pack8(pa[kt][qt], half * 8);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 a = trans_frag(Kt, dt * 32 + c, ch, g);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) dqa[dt][qt] = mfma32(a, db[qt], dqa[dt][qt]);
-      }
-    }
+      for (int dt = 0; dt < 4; ++dt)
+        dqa[dt] = mfma32(trans_frag(Kt, dt * 32 + c, ch, g), db[ch], dqa[dt]);
   }
 
-  // dQ = scale * (dQ^T)^T: lane holds query qt*32 + c, dims dt*32 + acc_row(r, g).
+  // dQ = scale * (dQ^T)^T: lane holds query qi, dims dt*32 + acc_row(r, g).
+  bf16_t* op = dq + row * D;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    bf16_t* op = dq + (rbase + qt * 32 + c) * D;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dd = dt * 32 + r4 * 8 + g * 4;
-        uint2 w;
-        w.x = pack_bf16x2(dqa[dt][qt][r4 * 4] * dm.scale, dqa[dt][qt][r4 * 4 + 1] * dm.scale);
-        w.y = pack_bf16x2(dqa[dt][qt][r4 * 4 + 2] * dm.scale, dqa[dt][qt][r4 * 4 + 3] * dm.scale);
-        *reinterpret_cast<uint2*>(op + dd) = w;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dd = dt * 32 + r4 * 8 + g * 4;
+      uint2 w;
+      w.x = pack_bf16x2(dqa[dt][r4 * 4] * dm.scale, dqa[dt][r4 * 4 + 1] * dm.scale);
+      w.y = pack_bf16x2(dqa[dt][r4 * 4 + 2] * dm.scale, dqa[dt][r4 * 4 + 3] * dm.scale);
+      *reinterpret_cast<uint2*>(op + dd) = w;
+    }
 }
 
 }  // namespace
 
 bool mfma_bwd_supported(const Dims& dm) {
-  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0;
+  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
+         dm.T <= DKV_MAXT;
 }
 
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
@@ -404,8 +477,8 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
     ProfScope ps("bwd_dkdv_mfma", st);
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm,
                        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                       (const bf16_t*)dout, lse, ws.D, logg, ws.csr_count, ws.csr_off,
-                       ws.csr_list, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part);
+                       (const bf16_t*)dout, lse, ws.D, logg, ws.slotmap, (bf16_t*)dk,
+                       (bf16_t*)dv, ws.dlogg_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -8,15 +8,19 @@
 //
 // Work unit: one (batch, KV head, query block, 4-head chunk) tile = 4 heads x
 // 64 query rows; every K/V block it needs is gathered once into LDS and serves
-// the 4 heads (one selection per KV head).  Wave w owns head kv*G + 4*chunk + w
-// and its 64 rows.
+// the 4 heads (one selection per KV head).  Eight waves: wave w owns 32 rows
+// (half w % 2 of the block) of head kv*G + 4*chunk + w / 2, which keeps each
+// wave's working set (Q fragments, S^T, O^T) inside 256 VGPRs.
 //   S^T = K Q^T   (32x32x16 MFMA; A = K rows from LDS, B = Q rows held in
 //                  registers), so each lane holds one query column and the
 //                  softmax max/sum over keys stays inside the lane (plus one
 //                  exchange with lane l^32);
 //   O^T += V^T P^T (A = V^T from a transposed LDS copy of V, B = P^T straight
 //                  from the S^T accumulators, converted to bf16).
-// The bias (log-gate) is added before the running max, in log2 units.
+// The bias (log-gate) is added before the running max, in log2 units.  The
+// running max is a reference that is only moved (and O, l rescaled) when a
+// block's max exceeds it by more than 2^8; the final normalisation uses the
+// same reference, so the result is unchanged.
 // Workgroups are issued longest-row-first (query block descending), KV head
 // fastest, so consecutive workgroups (spread over the 8 XCDs) share K/V.
 #include <math.h>
@@ -36,10 +40,12 @@ constexpr int VLD = BS + 4;  // V^T row stride in LDS (bf16 elements): 136 B
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-constexpr int HPW = 4;  // heads (waves) per workgroup
+constexpr int HPW = 4;   // heads per workgroup
+constexpr int NW = 8;    // waves per workgroup (two 32-row halves per head)
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 struct Stage {
-  static constexpr int NT = 64 * HPW;
+  static constexpr int NT = 64 * NW;
   static constexpr int KCH = (BS * D / 8) / NT;   // 16-byte K chunks per thread
   static constexpr int VUN = (BS / 2) * (D / 8) / NT;  // (key pair, 8 dims) units per thread
   uint4 kreg[KCH];
@@ -87,7 +93,7 @@ struct Stage {
   }
 };
 
-__global__ void __launch_bounds__(64 * HPW) fwd_mfma_kernel(
+__global__ void __launch_bounds__(64 * NW) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, bf16_t* __restrict__ o, float* __restrict__ lse) {
@@ -107,7 +113,8 @@ __global__ void __launch_bounds__(64 * HPW) fwd_mfma_kernel(
   const int t = dm.T - 1 - tile / dm.b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
-  const int h = kv * dm.g + chunk * HPW + wave;
+  const int h = kv * dm.g + chunk * HPW + (wave >> 1);
+  const int qt = wave & 1;  // which 32-row half of the query block
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
   if (threadIdx.x == 0) {
@@ -127,25 +134,21 @@ __global__ void __launch_bounds__(64 * HPW) fwd_mfma_kernel(
   }
 
   // Q^T fragments (B operand): query qt*32 + c, dims kc*16 + g*8 .. +8.
-  const bf16_t* qrow = q + (((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS) * D;
-  bf16x8 qf[2][8];
+  const bf16_t* qrow = q + (((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qt * 32) * D;
+  bf16x8 qf[8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-      qf[qt][kc] = *reinterpret_cast<const bf16x8*>(qrow + (size_t)(qt * 32 + c) * D + kc * 16 +
-                                                    g * 8);
+  for (int kc = 0; kc < 8; ++kc)
+    qf[kc] = *reinterpret_cast<const bf16x8*>(qrow + (size_t)c * D + kc * 16 + g * 8);
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][qt][r] = 0.0f;
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lrun[2] = {0.0f, 0.0f};
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+  float mref = -INFINITY;  // reference max (log2 units) of this lane's query
+  float lsum = 0.0f;       // sum of 2^(z - mref) over this lane's keys
   const float sc2 = dm.scale * LOG2E;
+  const int qi = qt * 32 + c;  // query row within the block
 
   __syncthreads();
   const int nb = nblk;
@@ -164,96 +167,85 @@ __global__ void __launch_bounds__(64 * HPW) fwd_mfma_kernel(
     if (bi + 1 < nb)
       st.load(kbase + (size_t)blist[bi + 1] * BS * D, vbase + (size_t)blist[bi + 1] * BS * D);
 
-    // S^T[key][query] for the 64 keys of this block and the wave's 64 queries.
-    f32x16 sacc[2][2];
+    // S^T[key][query]: 64 keys x the wave's 32 queries.
+    f32x16 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][qt][r] = 0.0f;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
+    for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 a =
             *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + c) * KLD + kc * 16 + g * 8);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = mfma32(a, qf[qt][kc], sacc[kt][qt]);
+        sacc[kt] = mfma32(a, qf[kc], sacc[kt]);
       }
-    }
 
-    // Online softmax, per query column (log2 domain).
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = fmaf(sacc[kt][qt][r], sc2, bias2);
-          if (diag && (kt * 32 + acc_row(r, g)) > (qt * 32 + c)) z = -INFINITY;
-          sacc[kt][qt][r] = z;
-          mx = fmaxf(mx, z);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = fast_exp2(mrun[qt] - mnew);
-      mrun[qt] = mnew;
-      float ls = 0.0f;
+    // Max of the raw logits (scale > 0, bias uniform over the block).
+    float smax = -INFINITY;
+    if (diag) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[kt][qt][r] - mnew);
-          sacc[kt][qt][r] = p;
-          ls += p;
-        }
-      lrun[qt] = lrun[qt] * alpha + ls;
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + acc_row(r, g) > qi) sacc[kt][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kt][r]);
+    float mx = fmaf(smax, sc2, bias2);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx > mref + RESCALE_SLACK) {
+      const float alpha = fast_exp2(mref - mx);
+      mref = mx;
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][qt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+    const float off2 = bias2 - mref;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sacc[kt][r], sc2, off2));
+        sacc[kt][r] = p;
+        lsum += p;
+      }
 
     // O^T += V^T P^T over four 16-key chunks.
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      const int kt = ch >> 1, half = ch & 1;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) pf[qt] = pack8(sacc[kt][qt], half * 8);
+      const bf16x8 pf = pack8(sacc[ch >> 1], (ch & 1) * 8);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16_t* vr = Vt + (dt * 32 + c) * VLD + ch * 16 + g * 4;
         const bf16x8 a = cat4(*reinterpret_cast<const bf16x4*>(vr),
                               *reinterpret_cast<const bf16x4*>(vr + 8));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = mfma32(a, pf[qt], oacc[dt][qt]);
+        oacc[dt] = mfma32(a, pf, oacc[dt]);
       }
     }
   }
 
   // Normalise and store o (bf16) and LSE (natural log).
-  bf16_t* orow = o + (((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS) * D;
-  float* lrow = lse + ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
+  const size_t row = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.0f / ltot;
+  if (g == 0) lse[row] = (mref + log2f(ltot)) * LN2;
+  bf16_t* op = o + row * D;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float ltot = lrun[qt] + __shfl_xor(lrun[qt], 32);
-    const float inv = 1.0f / ltot;
-    if (g == 0) lrow[qt * 32 + c] = (mrun[qt] + log2f(ltot)) * LN2;
-    bf16_t* op = orow + (size_t)(qt * 32 + c) * D;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dd = dt * 32 + r4 * 8 + g * 4;
-        uint2 w;
-        w.x = pack_bf16x2(oacc[dt][qt][r4 * 4 + 0] * inv, oacc[dt][qt][r4 * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[dt][qt][r4 * 4 + 2] * inv, oacc[dt][qt][r4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + dd) = w;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dd = dt * 32 + r4 * 8 + g * 4;
+      uint2 w;
+      w.x = pack_bf16x2(oacc[dt][r4 * 4 + 0] * inv, oacc[dt][r4 * 4 + 1] * inv);
+      w.y = pack_bf16x2(oacc[dt][r4 * 4 + 2] * inv, oacc[dt][r4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + dd) = w;
+    }
 }
 
 }  // namespace
@@ -267,7 +259,7 @@ hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const v
                            hipStream_t st) {
   const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
   ProfScope ps("fwd_mfma", st);
-  hipLaunchKernelGGL(fwd_mfma_kernel, dim3((unsigned)tiles), dim3(64 * HPW), 0, st, dm,
+  hipLaunchKernelGGL(fwd_mfma_kernel, dim3((unsigned)tiles), dim3(64 * NW), 0, st, dm,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
                      (bf16_t*)o, lse);
   return hipGetLastError();

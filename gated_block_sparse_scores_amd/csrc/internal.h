@@ -36,13 +36,10 @@ hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, cons
                               hipStream_t st);
 // Workspace layout helpers for the backward.
 struct BwdWorkspace {
-  float* D;          // [b, hq, n]
-  int* csr_count;    // [b*hkv*T]
-  int* csr_off;      // [b*hkv*T]
-  int* csr_list;     // [b*hkv*T*K]  entries (t << 8) | slot
-  float* dlogg_part; // [b*hkv*T, nchunk, K]
-  uint32_t* csr_bits;  // [b*hkv*T, csr_words] bitmap (key block m, query block t)
-  size_t csr_words;
+  float* D;            // [b, hq, n]          dout . o per query row
+  float* dlogg_part;   // [b*hkv*T, nchunk, K] per-chunk gate-gradient partials
+  uint8_t* slotmap;    // [b*hkv, T (m), T (t)] Top-K slot of block m in row t, 0xFF = none
+  size_t slotmap_bytes;
   size_t bytes;
 };
 BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base);
