@@ -20,7 +20,8 @@ SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_LAU
 SAS_DTYPE_F32, SAS_DTYPE_BF16 = 0, 1
 
 EXPORTED = [
-    "sas_status_string", "sas_version", "sas_block_pool", "sas_select_topk",
+    "sas_status_string", "sas_version", "sas_block_pool", "sas_select_topk_workspace_size",
+    "sas_select_topk",
     "sas_attn_fwd_workspace_size", "sas_attn_fwd", "sas_attn_bwd_workspace_size",
     "sas_attn_bwd", "sas_decode_workspace_size", "sas_decode", "sas_profiler_enable",
     "sas_profiler_reset", "sas_profiler_read",
@@ -77,8 +78,10 @@ def lib():
     L.sas_status_string.restype = C.c_char_p
     L.sas_version.restype = C.c_int
     L.sas_block_pool.argtypes = [sp, P, C.c_int, C.c_int, C.c_int, P, P]
+    L.sas_select_topk_workspace_size.argtypes = [sp, C.c_int, C.c_int, C.c_int]
+    L.sas_select_topk_workspace_size.restype = C.c_size_t
     L.sas_select_topk.argtypes = [sp, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int,
-                                  C.c_int, P, P, P, P, P]
+                                  C.c_int, P, P, P, P, P, C.c_size_t, P]
     L.sas_attn_fwd_workspace_size.argtypes = [sp, C.c_int]
     L.sas_attn_fwd_workspace_size.restype = C.c_size_t
     L.sas_attn_fwd.argtypes = [sp, C.c_int, P, P, P, P, P, P, P, P, C.c_size_t, P]
@@ -147,11 +150,17 @@ def sas_block_pool(shape: Shape, x, heads: int, group: int, out_dtype: int, out,
                                                    out_dtype, _ptr(out), _stream(stream)))
 
 
+def sas_select_topk_workspace_size(shape: Shape, T: int, C_: int, K: int) -> int:
+    return lib().sas_select_topk_workspace_size(C.byref(shape.c()), T, C_, K)
+
+
 def sas_select_topk(shape: Shape, T: int, C_: int, row_offset: int, K: int, s, qbar, kbar,
-                    kbar_dtype: int, kbar_ld: int, s_out, idx, logg, lse_s, stream=None):
+                    kbar_dtype: int, kbar_ld: int, s_out, idx, logg, lse_s, workspace=None,
+                    ws_bytes: int = 0, stream=None):
     _check("sas_select_topk", lib().sas_select_topk(
         C.byref(shape.c()), T, C_, row_offset, K, _ptr(s), _ptr(qbar), _ptr(kbar), kbar_dtype,
-        kbar_ld, _ptr(s_out), _ptr(idx), _ptr(logg), _ptr(lse_s), _stream(stream)))
+        kbar_ld, _ptr(s_out), _ptr(idx), _ptr(logg), _ptr(lse_s), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def sas_attn_fwd_workspace_size(shape: Shape, K: int) -> int:

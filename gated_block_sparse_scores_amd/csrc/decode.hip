@@ -9,9 +9,11 @@
 // block]; workgroup (b, kv, split) takes `bps` consecutive entries of it and
 // serves all G query heads of kv from one read of each K/V row.  Each key row
 // (head_dim values) is read by 16 lanes with one vector load per lane, so a
-// wave reads 4 rows per instruction, fully coalesced.  The partial (max, sum,
-// unnormalised output) of every split goes to the workspace; a second kernel
-// merges the splits of each (b, h) with log-sum-exp weights.
+// wave reads 4 rows per instruction, fully coalesced; all K and V loads of the
+// split are issued before any arithmetic.  Dot products are reduced across the
+// 16 lanes with DPP row operations (no LDS round trip).  The partial (max,
+// sum, unnormalised output) of every split goes to the workspace; a second
+// kernel merges the splits of each (b, h) with log-sum-exp weights.
 #include <math.h>
 
 #include <type_traits>
@@ -24,7 +26,8 @@ namespace sas {
 namespace {
 
 constexpr int kMaxG = 8;
-constexpr int kMaxBps = 4;
+constexpr int kMaxBps = 2;
+constexpr int kMaxSplit = 65;  // K + 1 blocks at one block per split
 
 template <typename T, int N> struct VecLoad;
 template <> struct VecLoad<bf16_t, 8> {
@@ -62,13 +65,67 @@ template <> struct VecLoad<float, 4> {
   }
 };
 
+// One lane's slice of a K or V row, kept in its storage format until used.
+template <typename T, int N> struct RawSlice;
+template <int N> struct RawSlice<bf16_t, N> {
+  uint32_t w[N / 2];
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    if constexpr (N == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float get(int e) const {
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+  }
+};
+template <int N> struct RawSlice<float, N> {
+  float f[N];
+  __device__ __forceinline__ void load(const float* p) { VecLoad<float, N>::load(p, f); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = 0.0f;
+  }
+  __device__ __forceinline__ float get(int e) const { return f[e]; }
+};
+
+// Sum over the 16 lanes of a DPP row (quad xor 1, quad xor 2, half-row
+// mirror, row mirror): every lane of the row ends with the row's total.
+__device__ __forceinline__ float row16_sum(float x) {
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {
+      case 0:
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+      case 1:
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+      case 2:
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+      default:
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+    }
+  };
+  x += dpp(x, 0);
+  x += dpp(x, 1);
+  x += dpp(x, 2);
+  x += dpp(x, 3);
+  return x;
+}
+
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(256) decode_split_kernel(
     Dims dm, int L, int cache_len, int bps, int nsplit, const T* __restrict__ q,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc) {
-  constexpr int DPL = D / 16;
+  constexpr int DPL = D / 16;                  // dims per lane (one vector load)
   constexpr int MAXKEYS = kMaxBps * BS;
+  constexpr int KPT = MAXKEYS / 16;            // keys per thread (16 key groups)
   __shared__ float sc[kMaxG][MAXKEYS];
   __shared__ __align__(16) float red[4][kMaxG][D];
   __shared__ int blist[kMaxBps];
@@ -110,9 +167,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h < G) {
-      const T* qp = q + (((size_t)b * dm.hq + kv * G + h) * D) + sub * DPL;
+      RawSlice<T, DPL> qs;
+      qs.load(q + (((size_t)b * dm.hq + kv * G + h) * D) + sub * DPL);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[h][e] = Elem<T>::load(qp, e);
+      for (int e = 0; e < DPL; ++e) qv[h][e] = qs.get(e);
     } else {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) qv[h][e] = 0.0f;
@@ -122,25 +180,37 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int nkeys = nb_sh * BS;
   const size_t kvbase = ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
 
-  // Phase A: scores of every key of this split for the G heads.
-  for (int kk = grp; kk < nkeys; kk += 16) {
-    const int bi = kk / BS;
-    const int pos = blist[bi] * BS + (kk % BS);
-    const bool valid = pos < L;
-    float kr[DPL];
-    if (valid)
-      VecLoad<T, DPL>::load(kc + kvbase + (size_t)pos * D + sub * DPL, kr);
-    else
+  // Issue every K and V row load of this split before any arithmetic.
+  RawSlice<T, DPL> kr[KPT], vr[KPT];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) kr[e] = 0.0f;
+  for (int i = 0; i < KPT; ++i) {
+    const int kk = grp + 16 * i;
+    const int pos = kk < nkeys ? blist[kk / BS] * BS + (kk % BS) : L;
+    if (pos < L) {
+      kr[i].load(kc + kvbase + (size_t)pos * D + sub * DPL);
+      vr[i].load(vc + kvbase + (size_t)pos * D + sub * DPL);
+    } else {
+      kr[i].zero();
+      vr[i].zero();
+    }
+  }
+
+  // Phase A: scores of every key of this split for the G heads.
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int kk = grp + 16 * i;
+    if (kk >= nkeys) break;  // uniform across each 16-lane row
+    const int pos = blist[kk / BS] * BS + (kk % BS);
+    const float bias = bbias[kk / BS];
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
-      float a = 0.0f;
+      if (h < G) {
+        float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) a += qv[h][e] * kr[e];
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) a += __shfl_xor(a, o);
-      if (sub == 0 && h < G) sc[h][kk] = valid ? a * dm.scale + bbias[bi] : -INFINITY;
+        for (int e = 0; e < DPL; ++e) a += qv[h][e] * kr[i].get(e);
+        a = row16_sum(a);
+        if (sub == 0) sc[h][kk] = pos < L ? a * dm.scale + bias : -INFINITY;
+      }
     }
   }
   __syncthreads();
@@ -171,18 +241,16 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   for (int h = 0; h < kMaxG; ++h)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.0f;
-  for (int kk = grp; kk < nkeys; kk += 16) {
-    const int bi = kk / BS;
-    const int pos = blist[bi] * BS + (kk % BS);
-    if (pos < L) {
-      float vr[DPL];
-      VecLoad<T, DPL>::load(vc + kvbase + (size_t)pos * D + sub * DPL, vr);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int kk = grp + 16 * i;
+    if (kk < nkeys) {
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {
         if (h < G) {
           const float pz = sc[h][kk];
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] += pz * vr[e];
+          for (int e = 0; e < DPL; ++e) acc[h][e] += pz * vr[i].get(e);
         }
       }
     }
@@ -191,10 +259,12 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   for (int h = 0; h < kMaxG; ++h)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-      float a = acc[h][e];
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[h][e] = a;
+      if (h < G) {
+        float a = acc[h][e];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        acc[h][e] = a;
+      }
     }
   if (lane < 16) {
 #pragma unroll
@@ -216,27 +286,245 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   }
 }
 
-// Merge: o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, lse = M + log(...).
+// Merge, one wave per (b, h): weights w_s = e^{m_s - M} (0 for empty splits),
+// o = sum_s w_s acc_s / sum_s w_s l_s, lse = M + log(sum_s w_s l_s).
 template <typename T>
-__global__ void __launch_bounds__(128) decode_merge_kernel(int nsplit, int D,
-                                                           const float* __restrict__ part_ml,
-                                                           const float* __restrict__ part_acc,
-                                                           T* __restrict__ o,
-                                                           float* __restrict__ lse) {
+__global__ void __launch_bounds__(64) decode_merge_kernel(int nsplit, int D,
+                                                          const float* __restrict__ part_ml,
+                                                          const float* __restrict__ part_acc,
+                                                          T* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  __shared__ float w[kMaxSplit];
   const size_t row = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* ml = part_ml + row * nsplit * 2;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float Lsum = 0.0f;
-  for (int s = 0; s < nsplit; ++s)
-    if (ml[2 * s + 1] > 0.0f) Lsum += ml[2 * s + 1] * expf(ml[2 * s] - M);
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float a = 0.0f;
-    for (int s = 0; s < nsplit; ++s)
-      if (ml[2 * s + 1] > 0.0f) a += part_acc[(row * nsplit + s) * D + dd] * expf(ml[2 * s] - M);
-    Elem<T>::store(o, row * D + dd, a / Lsum);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  float Ls = 0.0f;
+  for (int s = lane; s < nsplit; s += 64) {
+    const float l = ml[2 * s + 1];
+    const float ws = l > 0.0f ? expf(ml[2 * s] - M) : 0.0f;
+    w[s] = ws;
+    Ls += ws * l;
   }
-  if (threadIdx.x == 0) lse[row] = M + logf(Lsum);
+  Ls = wave_sum(Ls);
+  __syncthreads();
+  const float inv = 1.0f / Ls;
+  const float* acc = part_acc + row * nsplit * D;
+  for (int dd = lane; dd < D; dd += 64) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += w[s + u] * acc[(size_t)(s + u) * D + dd];
+    }
+    for (; s < nsplit; ++s) a[0] += w[s] * acc[(size_t)s * D + dd];
+    const float tot = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    Elem<T>::store(o, row * D + dd, tot * inv);
+  }
+  if (lane == 0) lse[row] = M + logf(Ls);
+}
+
+// ---------------------------------------------------------------- bf16, d 128, block 64
+// One wave per selected block (64 keys).  Scores S[h][key] = q_h . k_key come
+// from v_mfma_f32_16x16x32_bf16 with A = the G query heads (rows, zero-padded
+// to 16) and B = K^T: lane l loads 8 consecutive dims (16 B) of key l % 16 of
+// each 16-key tile, so a load instruction covers 64 contiguous bytes of 16
+// rows, and the result lands with one key per lane column and four heads per
+// lane -- no cross-lane dot-product reductions.  The per-head max and sum over
+// the block's 64 keys use DPP within 16-lane rows.  P goes to LDS as
+// [key][head]; for P V every lane owns two dims of every V row, so each V row
+// is one 256-byte coalesced wave load and no cross-lane reduction is needed.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true)));
+  return x;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int G>
+__global__ void __launch_bounds__(64) decode_block_mfma_kernel(
+    Dims dm, int L, int cache_len, int nsplit, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const int32_t* __restrict__ idx,
+    const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc) {
+  constexpr int D = 128, BS = 64;
+  constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
+  __shared__ __align__(16) uint32_t Pb[BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1) per head
+  const int split = blockIdx.x % nsplit;
+  const int bk = blockIdx.x / nsplit;
+  const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int c = (L - 1) / BS;
+  const int lane = threadIdx.x;
+  const size_t prow = (size_t)b * dm.hq + (size_t)kv * G;
+
+  // The split-th entry of [valid selected blocks (slot order)..., current block].
+  int m = -1;
+  float bias = 0.0f;
+  {
+    const int mm = lane < dm.K ? idx[(size_t)bk * dm.K + lane] : -1;
+    const bool ok = mm >= 0 && mm < c;
+    const unsigned long long bal = __ballot(ok);
+    const int nvalid = __popcll(bal);
+    if (split < nvalid) {
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      const unsigned long long hit = __ballot(ok && before == split);
+      const int src = __ffsll((long long)hit) - 1;
+      m = __shfl(mm, src);
+      bias = logg ? logg[(size_t)bk * dm.K + src] : 0.0f;
+    } else if (split == nvalid) {
+      m = c;
+    }
+  }
+  if (m < 0) {  // empty split
+    if (lane < G) {
+      part_ml[((prow + lane) * nsplit + split) * 2 + 0] = -INFINITY;
+      part_ml[((prow + lane) * nsplit + split) * 2 + 1] = 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      *reinterpret_cast<float2*>(&part_acc[((prow + h) * nsplit + split) * D + 2 * lane]) =
+          make_float2(0.0f, 0.0f);
+    return;
+  }
+  const bf16_t* kbase = kc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
+  const bf16_t* vbase = vc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
+  const int pos0 = m * BS;
+  const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
+
+  // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
+  bf16x8_t kf[4][4];
+  uint32_t vr[BS];
+  if (pos0 + BS <= L) {  // full block (every history block): plain offsets
+    const bf16_t* krow = kbase + ((size_t)pos0 + (lane & 15)) * D + (lane >> 4) * 8;
+    const bf16_t* vrow = vbase + (size_t)pos0 * D + 2 * lane;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
+#pragma unroll
+    for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+  } else {  // the current block: rows past L - 1 are read clamped, then masked
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int pos = min(pos0 + kt * 16 + (lane & 15), last);
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kbase + (size_t)pos * D + ch * 32 +
+                                                        (lane >> 4) * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < BS; ++r)
+      vr[r] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)min(pos0 + r, last) * D +
+                                                 2 * lane);
+  }
+  bf16x8_t qf[4];
+  {
+    const int h = lane & 15;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      qf[ch] = h < G ? *reinterpret_cast<const bf16x8_t*>(q + (prow + h) * D + ch * 32 +
+                                                          (lane >> 4) * 8)
+                     : bf16x8_t{};
+  }
+
+  // S[h][key]: lane holds key kt*16 + lane%16, heads 4*(lane/16) + r.
+  f32x4_t sacc[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ch], kf[kt][ch], sacc[kt], 0, 0, 0);
+  }
+  const int hbase = (lane >> 4) * 4;
+  float mh[4], lh[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int pos = pos0 + kt * 16 + (lane & 15);
+      const float z = pos < L ? sacc[kt][r] * dm.scale + bias : -INFINITY;
+      sacc[kt][r] = z;
+      mx = fmaxf(mx, z);
+    }
+    mx = row16_max(mx);
+    float sm = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const float pz = expf(sacc[kt][r] - mx);  // exp(-inf) = 0 for masked keys
+      sacc[kt][r] = pz;
+      sm += pz;
+    }
+    mh[r] = mx;
+    lh[r] = row16_sum(sm);
+  }
+  // P as bf16 pairs of consecutive keys: the even lane of each pair writes.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = hbase + r;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const float mine = sacc[kt][r];
+      const float nb = __int_as_float(
+          __builtin_amdgcn_update_dpp(0, __float_as_int(mine), 0xB1, 0xF, 0xF, true));
+      if (h < G && (lane & 1) == 0)
+        Pb[(kt * 16 + (lane & 15)) >> 1][h] = pack_bf16x2(mine, nb);
+    }
+  }
+  __syncthreads();
+
+  float acc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
+#pragma unroll
+  for (int kp = 0; kp < BS / 2; ++kp) {
+    const uint32_t v0 = vr[2 * kp], v1 = vr[2 * kp + 1];
+    const bf16x2_t vlo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x05040100u));
+    const bf16x2_t vhi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x07060302u));
+    uint32_t pw[GP];
+    *reinterpret_cast<uint4*>(&pw[0]) = *reinterpret_cast<const uint4*>(&Pb[kp][0]);
+    if constexpr (GP == 8)
+      *reinterpret_cast<uint4*>(&pw[4]) = *reinterpret_cast<const uint4*>(&Pb[kp][4]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bf16x2_t ph = __builtin_bit_cast(bf16x2_t, pw[h]);
+      acc[h][0] = __builtin_amdgcn_fdot2_f32_bf16(ph, vlo, acc[h][0], false);
+      acc[h][1] = __builtin_amdgcn_fdot2_f32_bf16(ph, vhi, acc[h][1], false);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    *reinterpret_cast<float2*>(&part_acc[((prow + h) * nsplit + split) * D + 2 * lane]) =
+        make_float2(acc[h][0], acc[h][1]);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hbase + r;
+      if (h < G) {
+        part_ml[((prow + h) * nsplit + split) * 2 + 0] = mh[r];
+        part_ml[((prow + h) * nsplit + split) * 2 + 1] = lh[r];
+      }
+    }
+  }
+}
+
+template <int G>
+void launch_decode_block(const Dims& dm, int L, int cache_len, int nsplit, const void* q,
+                         const void* kc, const void* vc, const int32_t* idx, const float* logg,
+                         float* part_ml, float* part_acc, hipStream_t st) {
+  const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
+  hipLaunchKernelGGL(decode_block_mfma_kernel<G>, dim3((unsigned)wgs), dim3(64), 0, st, dm, L,
+                     cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
+                     idx, logg, part_ml, part_acc);
 }
 
 template <typename T, int D, int BS>
@@ -250,15 +538,28 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
   {
     ProfScope ps("decode_split", st);
     const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, BS>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       dm, L, cache_len, bps, nsplit, (const T*)q, (const T*)kc, (const T*)vc,
-                       idx, logg, part_ml, part_acc);
+    (void)wgs;
+    if constexpr (std::is_same<T, bf16_t>::value && D == 128 && BS == 64) {
+      switch (dm.g) {
+        case 1: launch_decode_block<1>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 2: launch_decode_block<2>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 3: launch_decode_block<3>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 4: launch_decode_block<4>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 5: launch_decode_block<5>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 6: launch_decode_block<6>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        case 7: launch_decode_block<7>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        default: launch_decode_block<8>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+      }
+    } else
+      hipLaunchKernelGGL((decode_split_kernel<T, D, BS>), dim3((unsigned)wgs), dim3(256), 0, st,
+                         dm, L, cache_len, bps, nsplit, (const T*)q, (const T*)kc, (const T*)vc,
+                         idx, logg, part_ml, part_acc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     ProfScope ps("decode_merge", st);
-    hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)(dm.b * dm.hq)), dim3(128), 0,
+    hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)(dm.b * dm.hq)), dim3(64), 0,
                        st, nsplit, D, part_ml, part_acc, (T*)o, lse);
   }
   return hipGetLastError();
@@ -266,7 +567,10 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
 
 }  // namespace
 
+bool decode_mfma_path(const Dims& dm) { return dm.bf16 && dm.d == 128 && dm.bs == 64; }
+
 int decode_blocks_per_split(const Dims& dm) {
+  if (decode_mfma_path(dm)) return 1;
   const long total = (long)dm.b * dm.hkv * (dm.K + 1);
   return total >= 2048 ? 2 : 1;
 }

@@ -29,6 +29,13 @@ hipError_t launch_standin_scores(const float* qbar, const void* kbar, bool kbar_
                                  int d, double scale, float* s_out, hipStream_t st);
 hipError_t launch_topk(const float* s, int rows_bk, int T, int C, int row_offset, int K,
                        int32_t* idx, float* logg, float* lse_s, hipStream_t st);
+// Rows with more than kLongHistory history blocks use the two-stage path.
+constexpr int kLongHistory = 512;
+size_t select_workspace_bytes(int rows_bk, int T, int C, int K);
+hipError_t launch_select_long(const float* s, const float* qbar, const void* kbar,
+                              bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
+                              int T, int C, int row_offset, int K, float* s_out, int32_t* idx,
+                              float* logg, float* lse_s, void* ws, hipStream_t st);
 
 // ---- attention, portable fp32-arithmetic kernels (attn_generic.hip)
 hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,

@@ -183,26 +183,43 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
       shape->head_dim, shape->block, out_dtype == SAS_DTYPE_BF16, out, (hipStream_t)stream));
 }
 
+size_t sas_select_topk_workspace_size(const sas_shape* shape, int T, int C, int K) {
+  if (!shape || shape->batch <= 0 || shape->hkv <= 0 || T <= 0 || C < 0 || K <= 0 || K > 64 ||
+      C > 16384)
+    return 0;
+  return sas::select_workspace_bytes(shape->batch * shape->hkv, T, C, K);
+}
+
 sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset, int K,
                            const float* s, const float* qbar, const void* kbar,
                            sas_dtype kbar_dtype, int kbar_ld, float* s_out, int32_t* idx,
-                           float* logg, float* lse_s, void* stream) {
+                           float* logg, float* lse_s, void* workspace, size_t ws_bytes,
+                           void* stream) {
   if (!shape || shape->batch <= 0 || shape->hkv <= 0) return SAS_ERR_INVALID_ARG;
   if (T <= 0 || C < 0 || row_offset < 0 || K <= 0) return SAS_ERR_INVALID_ARG;
   if (!idx || !logg || !lse_s) return SAS_ERR_INVALID_ARG;
   if (K > 64 || C > 16384) return SAS_ERR_UNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   const int rows_bk = shape->batch * shape->hkv;
-  const float* scores = s;
+  double scale = 0.0;
   if (!s) {
     if (!qbar || !kbar || !s_out) return SAS_ERR_INVALID_ARG;
     if (kbar_dtype != SAS_DTYPE_F32 && kbar_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
     if (kbar_ld < C) return SAS_ERR_INVALID_ARG;
     if (shape->head_dim <= 0) return SAS_ERR_INVALID_ARG;
-    if (shape->head_dim > 128) return SAS_ERR_UNSUPPORTED;
+    if (shape->head_dim != 64 && shape->head_dim != 128) return SAS_ERR_UNSUPPORTED;
     if (!(shape->scale >= 0.0f)) return SAS_ERR_INVALID_ARG;
-    const double scale =
-        shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
+    if (!aligned16(qbar) || !aligned16(kbar)) return SAS_ERR_INVALID_ARG;
+    scale = shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
+  }
+  const size_t need = sas::select_workspace_bytes(rows_bk, T, C, K);
+  if (need > 0 && (!workspace || ws_bytes < need)) return SAS_ERR_WORKSPACE;
+  if (C > sas::kLongHistory)
+    return launch_status(sas::launch_select_long(
+        s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim, scale, rows_bk, T,
+        C, row_offset, K, s_out, idx, logg, lse_s, workspace, st));
+  const float* scores = s;
+  if (!s) {
     if (C > 0)
       SAS_LAUNCH(sas::launch_standin_scores(qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                             rows_bk, T, C, row_offset, shape->head_dim, scale,

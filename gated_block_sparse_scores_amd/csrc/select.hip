@@ -222,6 +222,275 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ s, 
   if (tid == 0) lse_s[row] = lse;
 }
 
+// ---------------------------------------------------------------- long histories: two stages
+// For rows with many history blocks (decode over long contexts) one workgroup
+// per row leaves the chip idle and serialises the radix histograms.  Stage 1:
+// one workgroup per (row, chunk of 256 history blocks) forms the scores (given,
+// or the stand-in score with fp64 dot products read by 16 lanes per summary row
+// and reduced with DPP), records the chunk's max and sum of exp, and ranks its
+// 256 composite keys (order-preserving score bits, then the complemented block
+// index, so equal scores rank the lower block first; all keys are distinct) by
+// counting, against LDS broadcasts, the keys above each one; keys of rank < K
+// are written in rank order as the chunk's candidates.  Every block of the
+// row's Top-K is among its chunk's first K.  Stage 2 merges the sorted chunk
+// lists pairwise (log2(chunks) rounds; each output of a pair is located by a
+// merge-path binary search), combines the chunk statistics into lse_s, and
+// emits the K winners in ascending block order.
+constexpr int kChunk = 256;
+
+__device__ __forceinline__ double row16_sum_d(double x) {
+  auto step = [](double v, int ctrl) -> double {
+    const long long bits = __double_as_longlong(v);
+    int lo = (int)(bits & 0xFFFFFFFFll), hi = (int)(bits >> 32);
+    switch (ctrl) {
+      case 0:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, true);
+        break;
+      case 1:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, true);
+        break;
+      case 2:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, true);
+        break;
+      default:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, true);
+        break;
+    }
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+  };
+  x += step(x, 0);
+  x += step(x, 1);
+  x += step(x, 2);
+  x += step(x, 3);
+  return x;
+}
+
+__device__ __forceinline__ float from_order_key(uint32_t k) {
+  const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(b);
+}
+
+// Loads 8 consecutive summary values (one lane's slice) widened to double.
+template <typename Tk> struct Slice8;
+template <> struct Slice8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ double get(int e) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t x = w[e >> 1];
+    return (double)__uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+template <> struct Slice8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ double get(int e) const {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return (double)v[e];
+  }
+};
+
+template <typename Tk>
+__global__ void __launch_bounds__(256) select_chunk_kernel(
+    const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
+    int kbar_ld, int d, double scale, int T, int C, int row_offset, int K, int nchunk,
+    float* __restrict__ s_out, uint64_t* __restrict__ cand, float2* __restrict__ stats) {
+  __shared__ uint64_t keys[kChunk];
+  __shared__ float sval[kChunk];
+  __shared__ float fscr[16];
+  __shared__ double dscr[16];
+  const int chunk = blockIdx.x;
+  const size_t row = blockIdx.y;
+  const int t = (int)(row % T);
+  const size_t bk = row / T;
+  const int ct = min(t + row_offset, C);
+  const int m0 = chunk * kChunk;
+  const int tid = threadIdx.x;
+  const int m = m0 + tid;
+  const bool valid = m < ct;
+
+  float f = 0.0f;
+  if (s) {
+    f = valid ? s[row * C + m] : 0.0f;
+  } else {
+    // 16 groups of 16 lanes; group grp scores blocks m0 + grp + 16 i.
+    const int sub = tid & 15, grp = tid >> 4;
+    const float* qr = qbar + row * (size_t)d;
+    const int nsl = d / 8;  // lanes carrying 8 dims each (16 for d = 128, 8 for d = 64)
+    double qd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qd[e] = sub < nsl ? (double)qr[sub * 8 + e] : 0.0;
+    Slice8<Tk> sl[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mm = m0 + grp + 16 * i;
+      if (sub < nsl && mm < ct) sl[i].load(kbar + (bk * kbar_ld + mm) * (size_t)d + sub * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mm = m0 + grp + 16 * i;
+      double a = 0.0;
+      if (sub < nsl && mm < ct) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += qd[e] * sl[i].get(e);
+      }
+      a = row16_sum_d(a);
+      if (sub == 0) sval[grp + 16 * i] = mm < ct ? (float)(a * scale) : 0.0f;
+    }
+    __syncthreads();
+    f = sval[tid];
+    if (m < C) s_out[row * C + m] = valid ? f : 0.0f;
+  }
+  // Invalid entries get keys below every valid one (high word 0), still distinct.
+  const uint64_t mykey = ((valid ? (uint64_t)order_key(f) : 0ull) << 32) |
+                         (uint64_t)(0xFFFFFFFFu - (uint32_t)m);
+  keys[tid] = mykey;
+  const float mx = block_max(valid ? f : -INFINITY, fscr);  // barriers: keys[] complete
+  const double se = block_sum_d(valid ? (double)expf(f - mx) : 0.0, dscr);
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < kChunk; ++j) rank += keys[j] > mykey;
+  const size_t cbase = (row * nchunk + chunk) * (size_t)K;
+  if (rank < K) cand[cbase + rank] = mykey;
+  if (tid == 0) stats[row * nchunk + chunk] = make_float2(mx, (float)se);
+}
+
+// Top K of two descending lists of exactly K distinct keys, by merge path:
+// output j is found by binary search for how many of the first j + 1 come from A.
+__device__ __forceinline__ uint64_t merge_path_kth(const uint64_t* A, const uint64_t* B, int K,
+                                                  int j) {
+  const int d = j + 1;
+  int lo = d > K ? d - K : 0, hi = d < K ? d : K;
+  // smallest a in [lo, hi] such that taking a from A is not too few:
+  // too few <=> a < K and d - a > 0 and A[a] > B[d - a - 1]
+  while (lo < hi) {
+    const int a = (lo + hi) >> 1;
+    if (A[a] > B[d - a - 1])
+      lo = a + 1;
+    else
+      hi = a;
+  }
+  const int a = lo, b = d - lo;
+  if (a == 0) return B[b - 1];
+  if (b == 0) return A[a - 1];
+  const uint64_t x = A[a - 1], y = B[b - 1];
+  return x < y ? x : y;
+}
+
+__global__ void __launch_bounds__(256) select_merge_kernel(
+    const uint64_t* __restrict__ cand, const float2* __restrict__ stats, int T, int C,
+    int row_offset, int K, int nchunk, int32_t* __restrict__ idx, float* __restrict__ logg,
+    float* __restrict__ lse_s) {
+  extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
+  __shared__ int widx[64];
+  __shared__ float wval[64];
+  __shared__ float lse_sh;
+  __shared__ float fscr[16];
+  __shared__ double dscr[16];
+  const size_t row = blockIdx.x;
+  const int t = (int)(row % T);
+  const int ct = min(t + row_offset, C);
+  const int nc = nchunk * K;
+  const uint64_t* crow = cand + row * (size_t)nc;
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) lists[i] = crow[i];
+  {
+    // combine the chunks' (max, sum of exp) in parallel (nchunk <= 64)
+    const float2 st = (int)threadIdx.x < nchunk ? stats[row * nchunk + threadIdx.x]
+                                                : make_float2(-INFINITY, 0.0f);
+    const float M = block_max(st.x, fscr);  // barriers: lists[] complete afterwards
+    const double S = block_sum_d(st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0,
+                                 dscr);
+    if (threadIdx.x == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
+  }
+  // Pairwise merges, keeping the top K of each pair, until one list remains.
+  uint64_t* src = lists;
+  uint64_t* dst = lists + nc;
+  int nl = nchunk;
+  while (nl > 1) {
+    const int np = nl >> 1;
+    for (int job = threadIdx.x; job < np * K; job += blockDim.x) {
+      const int pr = job / K, j = job % K;
+      dst[pr * K + j] = merge_path_kth(src + (2 * pr) * K, src + (2 * pr + 1) * K, K, j);
+    }
+    if (nl & 1)
+      for (int j = threadIdx.x; j < K; j += blockDim.x) dst[np * K + j] = src[(nl - 1) * K + j];
+    __syncthreads();
+    uint64_t* tmp = src;
+    src = dst;
+    dst = tmp;
+    nl = np + (nl & 1);
+  }
+  const int kk = min(K, ct);
+  if ((int)threadIdx.x < kk) {
+    const uint64_t key = src[threadIdx.x];
+    widx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+    wval[threadIdx.x] = from_order_key((uint32_t)(key >> 32));
+  }
+  __syncthreads();
+  const float lse = lse_sh;
+  int32_t* irow = idx + row * (size_t)K;
+  float* lrow = logg + row * (size_t)K;
+  if ((int)threadIdx.x < kk) {
+    const int mine = widx[threadIdx.x];
+    int rank = 0;
+    for (int j = 0; j < kk; ++j) rank += widx[j] < mine;
+    irow[rank] = mine;
+    lrow[rank] = wval[threadIdx.x] - lse;
+  }
+  for (int p = kk + threadIdx.x; p < K; p += blockDim.x) {
+    irow[p] = -1;
+    lrow[p] = 0.0f;
+  }
+  if (threadIdx.x == 0) lse_s[row] = lse;
+}
+
+size_t select_workspace_bytes(int rows_bk, int T, int C, int K) {
+  if (C <= kLongHistory) return 0;
+  const size_t rows = (size_t)rows_bk * T;
+  const size_t nchunk = (size_t)(C + kChunk - 1) / kChunk;
+  const size_t cand = rows * nchunk * K * sizeof(uint64_t);
+  return ((cand + 255) & ~(size_t)255) + rows * nchunk * sizeof(float2);
+}
+
+hipError_t launch_select_long(const float* s, const float* qbar, const void* kbar,
+                              bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
+                              int T, int C, int row_offset, int K, float* s_out, int32_t* idx,
+                              float* logg, float* lse_s, void* ws, hipStream_t st) {
+  const size_t rows = (size_t)rows_bk * T;
+  const int nchunk = (C + kChunk - 1) / kChunk;
+  uint64_t* cand = (uint64_t*)ws;
+  const size_t cand_bytes = rows * nchunk * K * sizeof(uint64_t);
+  float2* stats = (float2*)((char*)ws + ((cand_bytes + 255) & ~(size_t)255));
+  {
+    ProfScope ps("select_chunk", st);
+    dim3 grid(nchunk, (unsigned)rows);
+    if (kbar_bf16)
+      hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, s, qbar,
+                         (const bf16_t*)kbar, kbar_ld, d, scale, T, C, row_offset, K, nchunk,
+                         s_out, cand, stats);
+    else
+      hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, s, qbar,
+                         (const float*)kbar, kbar_ld, d, scale, T, C, row_offset, K, nchunk,
+                         s_out, cand, stats);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps("select_merge", st);
+    hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256),
+                       (size_t)2 * nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
+                       K, nchunk, idx, logg, lse_s);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* s, int rows_bk, int T, int C, int row_offset, int K,
                        int32_t* idx, float* logg, float* lse_s, hipStream_t st) {
   const size_t rows = (size_t)rows_bk * T;

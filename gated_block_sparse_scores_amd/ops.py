@@ -50,7 +50,7 @@ def block_pool(x: torch.Tensor, block: int, group: int = 1,
 def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int = 0,
                 s: Optional[torch.Tensor] = None, qbar: Optional[torch.Tensor] = None,
                 kbar: Optional[torch.Tensor] = None, head_dim: int = 0, scale: float = 0.0,
-                stream=None, device=None):
+                stream=None, device=None, workspace: Optional[torch.Tensor] = None):
     """Returns (idx, logg, lse_s, s_used).  With s None the stand-in score from
     qbar/kbar is formed on the device and returned as s_used."""
     dev = device or (s.device if s is not None else qbar.device)
@@ -65,8 +65,11 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
         kld = kbar.shape[2]
         head_dim = qbar.shape[-1]
     sh = Shape(batch, hkv, hkv, 1, head_dim or 1, 1, L.SAS_DTYPE_F32, scale)
+    ws_n = L.sas_select_topk_workspace_size(sh, T, C, K)
+    if ws_n and (workspace is None or workspace.numel() < ws_n):
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     L.sas_select_topk(sh, T, C, row_offset, K, s, qbar, kbar, kdt, kld, s_out, idx, logg, lse_s,
-                      stream)
+                      workspace if ws_n else None, ws_n, stream)
     return idx, logg, lse_s, (s if s is not None else s_out)
 
 

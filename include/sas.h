@@ -119,11 +119,17 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
  *               -1 padded
  *   logg[r,:] = s_idx - lse_s (fp32; 0 on padded slots)
  * Uses shape->batch, hkv, head_dim, scale.  C <= 16384.
+ *
+ * Rows with more than 512 history blocks are served by two kernels (chunked
+ * candidates, then a per-row merge) whose candidates live in the workspace:
+ * sas_select_topk_workspace_size bytes (0 when C <= 512).
  * ---------------------------------------------------------------------- */
+size_t sas_select_topk_workspace_size(const sas_shape* shape, int T, int C, int K);
 sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset, int K,
                            const float* s, const float* qbar, const void* kbar,
                            sas_dtype kbar_dtype, int kbar_ld, float* s_out,
-                           int32_t* idx, float* logg, float* lse_s, void* stream);
+                           int32_t* idx, float* logg, float* lse_s, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Fused gated block-sparse forward (picx Eq. 9, 'Kernel Design'):

@@ -103,14 +103,20 @@ def test_select_checks():
     lib = L.lib()
     # no scores and no stand-in inputs
     assert lib.sas_select_topk(C.byref(sh), 4, 4, 0, 2, None, None, None, 0, 4, None, FAKE,
-                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+                               FAKE, FAKE, None, 0, None) == L.SAS_ERR_INVALID_ARG
     # kbar_ld smaller than C
     assert lib.sas_select_topk(C.byref(sh), 1, 8, 8, 2, None, FAKE, FAKE, 0, 7, FAKE, FAKE,
-                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+                               FAKE, FAKE, None, 0, None) == L.SAS_ERR_INVALID_ARG
     assert lib.sas_select_topk(C.byref(sh), 4, 20000, 0, 2, FAKE, None, None, 0, 0, None, FAKE,
-                               FAKE, FAKE, None) == L.SAS_ERR_UNSUPPORTED
+                               FAKE, FAKE, None, 0, None) == L.SAS_ERR_UNSUPPORTED
     assert lib.sas_select_topk(C.byref(sh), 4, 4, 0, 0, FAKE, None, None, 0, 0, None, FAKE,
-                               FAKE, FAKE, None) == L.SAS_ERR_INVALID_ARG
+                               FAKE, FAKE, None, 0, None) == L.SAS_ERR_INVALID_ARG
+    # long histories need the candidate workspace
+    need = lib.sas_select_topk_workspace_size(C.byref(sh), 1, 8191, 31)
+    assert need >= 32 * 31 * 8 * 2 and lib.sas_select_topk_workspace_size(C.byref(sh), 4, 512,
+                                                                            31) == 0
+    assert lib.sas_select_topk(C.byref(sh), 1, 8191, 8191, 31, FAKE, None, None, 0, 0, None,
+                               FAKE, FAKE, FAKE, None, 0, None) == L.SAS_ERR_WORKSPACE
 
 
 def test_decode_checks():

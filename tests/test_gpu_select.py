@@ -31,7 +31,8 @@ def test_select_tiny_fp32_workload():
     check_select(synth.train_inputs(w)["s"], w.topk)
 
 
-@pytest.mark.parametrize("T,K", [(1, 4), (5, 4), (16, 16), (33, 7), (130, 31), (200, 64)])
+@pytest.mark.parametrize("T,K", [(1, 4), (5, 4), (16, 16), (33, 7), (130, 31), (200, 64),
+                                 (700, 31), (1100, 64)])
 def test_select_shapes(T, K):
     s = synth.random_scores((2, 3, T, T), seed=T * 100 + K)
     s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
@@ -51,9 +52,33 @@ def test_select_ties_lowest_index_and_signed_zero():
 
 def test_select_decode_mode_long_history():
     """Decode rows: T = 1, C = history blocks, row_offset = C (all visible)."""
-    for C in (1, 63, 1023, 8191, 16384):
+    for C in (1, 63, 513, 1023, 8191, 16384):
         s = synth.random_scores((1, 8, 1, C), seed=C)
         check_select(s, 31, row_offset=C, C=C)
+    # many exact ties across chunk boundaries
+    s = torch.round(synth.random_scores((2, 4, 1, 3000), seed=7))
+    check_select(s, 64, row_offset=3000, C=3000)
+
+
+def test_decode_selection_fp32_pooled_keys_long():
+    """Stand-in scores over an fp32 pooled-key cache with 2000 history blocks
+    (chunked path), d = 64 and d = 128."""
+    from gated_block_sparse_scores_amd import ops
+    for d in (64, 128):
+        gen = torch.Generator().manual_seed(d)
+        kb = torch.randn(2, 3, 2001, d, generator=gen) * 0.1
+        qb = torch.randn(2, 3, 1, d, generator=gen)
+        C = 2000
+        idx, logg, lse_s, s = ops.select_topk(2, 3, 1, C, 17, row_offset=C, qbar=qb.to(DEV),
+                                              kbar=kb.to(DEV))
+        torch.cuda.synchronize()
+        so = O.standin_scores(qb.numpy(), kb.numpy(), O.default_scale(d), C, row_offset=C)
+        s_gpu = s.cpu().numpy()
+        assert np.sum(s_gpu != so) <= 2
+        oi, ol, ols = O.select_topk(so, 17, row_offset=C, C=C)
+        np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+        assert max_abs(logg.cpu().numpy(), ol) <= GATE_ATOL
+        assert max_abs(lse_s.cpu().numpy(), ols) <= GATE_ATOL
 
 
 def test_select_large_training_rows():
