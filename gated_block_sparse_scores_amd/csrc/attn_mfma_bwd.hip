@@ -14,14 +14,19 @@
 //    through LDS at the end.  The workgroup visits the diagonal query block
 //    t = m and every later query block whose selection holds m (read from the
 //    slot map, compacted 256 at a time), for each of the G heads, staging that
-//    head's 64 rows of q and dout in LDS row-major (A operand of S = Q K^T and
-//    dP = dO V^T) and transposed (A operand of dK^T = Q^T dS, dV^T = dO^T P).
+//    head's 64 rows of q and dout in LDS row-major: rows are the A operand of
+//    S = Q K^T and dP = dO V^T, and the transposing LDS read
+//    (ds_read_b64_tr_b16) gives the A operand of dK^T = Q^T dS, dV^T = dO^T P.
 //    Block m is the only owner of the (t, slot) pairs that selected it, so it
 //    also writes dlogg[t][slot] (sum over G heads, 64 rows, 64 keys) directly.
-//  * dQ (query-major): the forward's tiling (4 heads x 64 rows per workgroup,
-//    eight waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
-//    selected block and accumulating dQ^T += K^T dS^T, with K staged row-major
-//    and transposed and V row-major in LDS.
+//  All tiles are copied global -> LDS with the direct-to-LDS load into double
+//  buffers (the next tile streams in while the current one is computed) and
+//  laid out swizzled so that row fragments and transposed reads are both free
+//  of bank conflicts.
+//  * dQ (query-major): the forward's tiling (2 heads x 64 rows per workgroup,
+//    four waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
+//    selected block and accumulating dQ^T += K^T dS^T, with K and V staged
+//    row-major in LDS (K^T read with ds_read_b64_tr_b16).
 #include <math.h>
 
 #include "common.h"
@@ -34,114 +39,15 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BS = 64;
-constexpr int RLD = D + 8;   // row-major tile stride (bf16 elements): 272 B
-constexpr int TLD = BS + 4;  // transposed tile stride (bf16 elements): 136 B
+// q / dout / K / V tiles: 64 x 128 bf16, swizzled (see mfma.h)
 constexpr float LOG2E = 1.4426950408889634f;
-
-// Stages 64 rows x 128 dims of a bf16 tensor (row stride D) into LDS twice:
-// row-major (stride RLD) and transposed (stride TLD).  NT threads.
-template <int NT>
-__device__ __forceinline__ void stage_both(const bf16_t* __restrict__ src, bf16_t* rowm,
-                                           bf16_t* trans) {
-  constexpr int UN = (BS / 2) * (D / 8) / NT;  // (row pair, 8 dims) units per thread
-  uint4 ra[UN], rb[UN];
-#pragma unroll
-  for (int i = 0; i < UN; ++i) {
-    const int u = threadIdx.x + i * NT;
-    const int dg = u & 15, rp = u >> 4;
-    ra[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp) * D + dg * 8);
-    rb[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp + 1) * D + dg * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < UN; ++i) {
-    const int u = threadIdx.x + i * NT;
-    const int dg = u & 15, rp = u >> 4;
-    *reinterpret_cast<uint4*>(rowm + (2 * rp) * RLD + dg * 8) = ra[i];
-    *reinterpret_cast<uint4*>(rowm + (2 * rp + 1) * RLD + dg * 8) = rb[i];
-    const uint32_t a[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-    const uint32_t b[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
-      const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w) * TLD + 2 * rp) = lo;
-      *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w + 1) * TLD + 2 * rp) = hi;
-    }
-  }
-}
-
-// Row-major only.
-template <int NT>
-__device__ __forceinline__ void stage_rows(const bf16_t* __restrict__ src, bf16_t* rowm) {
-  constexpr int UN = BS * (D / 8) / NT;
-  uint4 r[UN];
-#pragma unroll
-  for (int i = 0; i < UN; ++i) {
-    const int u = threadIdx.x + i * NT;
-    r[i] = *reinterpret_cast<const uint4*>(src + (size_t)(u >> 4) * D + (u & 15) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < UN; ++i) {
-    const int u = threadIdx.x + i * NT;
-    *reinterpret_cast<uint4*>(rowm + (u >> 4) * RLD + (u & 15) * 8) = r[i];
-  }
-}
-
-// Register-staged copy of 64 rows x 128 dims (row pairs x 8-dim groups),
-// loaded from global memory ahead of use and written to LDS later, both
-// row-major (stride RLD) and, optionally, transposed (stride TLD).
-template <int NT>
-struct RowPairs {
-  static constexpr int UN = (BS / 2) * (D / 8) / NT;
-  uint4 ra[UN], rb[UN];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ src) {
-#pragma unroll
-    for (int i = 0; i < UN; ++i) {
-      const int u = threadIdx.x + i * NT;
-      const int dg = u & 15, rp = u >> 4;
-      ra[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp) * D + dg * 8);
-      rb[i] = *reinterpret_cast<const uint4*>(src + (size_t)(2 * rp + 1) * D + dg * 8);
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* rowm, bf16_t* trans) const {
-#pragma unroll
-    for (int i = 0; i < UN; ++i) {
-      const int u = threadIdx.x + i * NT;
-      const int dg = u & 15, rp = u >> 4;
-      *reinterpret_cast<uint4*>(rowm + (2 * rp) * RLD + dg * 8) = ra[i];
-      *reinterpret_cast<uint4*>(rowm + (2 * rp + 1) * RLD + dg * 8) = rb[i];
-      if (trans) {
-        const uint32_t a[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-        const uint32_t b[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
-          const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-          *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w) * TLD + 2 * rp) = lo;
-          *reinterpret_cast<uint32_t*>(trans + (dg * 8 + 2 * w + 1) * TLD + 2 * rp) = hi;
-        }
-      }
-    }
-  }
-};
-
-__device__ __forceinline__ bf16x8 lds8(const bf16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// A operand from a transposed tile: row `row`, k-values for 16-column chunk
-// `ch` in the accumulator-row order of lane group g.
-__device__ __forceinline__ bf16x8 trans_frag(const bf16_t* tile, int row, int ch, int g) {
-  const bf16_t* p = tile + row * TLD + ch * 16 + g * 4;
-  return cat4(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 8));
-}
 
 // ---------------------------------------------------------------- dK / dV
 constexpr int DKV_NT = 256;
 constexpr int DKV_MAXT = 8192;  // longest inverse list (query blocks) held in LDS
-constexpr int TILE_BYTES_R = BS * RLD * 2;   // one row-major 64 x 128 tile
-constexpr int TILE_BYTES_T = D * TLD * 2;    // one transposed 128 x 64 tile
-constexpr int DKV_SMEM = 2 * TILE_BYTES_R + 2 * TILE_BYTES_T;
+constexpr int TILE_BYTES_R = BS * TILE_LD * 2;   // one 64 x 128 tile
+constexpr int DKV_SMEM = 4 * TILE_BYTES_R;       // q and dout, double buffered (also the
+                                                 // 64 KB of the final half-sum)
 
 __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -150,11 +56,7 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     const float* __restrict__ logg, const uint8_t* __restrict__ slotmap,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg) {
   __shared__ __align__(16) unsigned char smem[DKV_SMEM];
-  bf16_t* Qs = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* Os = reinterpret_cast<bf16_t*>(smem + TILE_BYTES_R);
-  bf16_t* Qt = reinterpret_cast<bf16_t*>(smem + 2 * TILE_BYTES_R);
-  bf16_t* Ot = reinterpret_cast<bf16_t*>(smem + 2 * TILE_BYTES_R + TILE_BYTES_T);
-  __shared__ float Ls[BS], Dl[BS];
+  __shared__ float Ls[2][BS], Dl[2][BS];
   __shared__ float red[4];
   __shared__ int lst[DKV_MAXT];
   __shared__ int scan_scr[16];
@@ -207,43 +109,46 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
   }
   __syncthreads();
 
-  // Flat loop over (entry, head); the next tile's q / dout rows are loaded
-  // into registers while the current one is computed.
+  // Flat loop over (entry, head); the next item's q / dout rows, LSE and D are
+  // copied global -> LDS (direct-to-LDS loads, double buffered) while the
+  // current item is computed.
   const int items = ne * dm.g;
-  RowPairs<DKV_NT> pq, po;
-  float pls = 0.0f, pdl = 0.0f;
   auto tile_base = [&](int it) {
     const int t = lst[it / dm.g] >> 8;
     const int h = kv * dm.g + it % dm.g;
     return ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
   };
-  auto prefetch = [&](int it) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto prefetch = [&](int it, int buf) {
     const size_t rb = tile_base(it);
-    pq.load(q + rb * D);
-    po.load(dout + rb * D);
-    if (threadIdx.x < BS) {
-      pls = lse[rb + threadIdx.x] * LOG2E;
-      pdl = Dv[rb + threadIdx.x];
+    bf16_t* Qb = reinterpret_cast<bf16_t*>(smem + (2 * buf) * TILE_BYTES_R);
+    bf16_t* Ob = reinterpret_cast<bf16_t*>(smem + (2 * buf + 1) * TILE_BYTES_R);
+    tile_load_lds<4>(Qb, q + rb * D);
+    tile_load_lds<4>(Ob, dout + rb * D);
+    if (wave == 0) {
+      __builtin_amdgcn_global_load_lds((const void*)(lse + rb + lane), (lds_void*)&Ls[buf][0], 4,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Dv + rb + lane), (lds_void*)&Dl[buf][0], 4,
+                                       0, 0);
     }
   };
-  if (items > 0) prefetch(0);
+  if (items > 0) prefetch(0, 0);
+  wait_all_loads();
+  __syncthreads();
   float dlsum = 0.0f;
   for (int it = 0; it < items; ++it) {
+    const int cur = it & 1;
     const int e = it / dm.g;
     const int t = lst[e] >> 8;
     const int slot = (lst[e] & 255) == 0xFE ? -1 : (lst[e] & 255);
     const bool diag = slot < 0;
     const float bias2 =
         (!diag && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] * LOG2E : 0.0f;
-    __syncthreads();
-    pq.store(Qs, Qt);
-    po.store(Os, Ot);
-    if (threadIdx.x < BS) {
-      Ls[threadIdx.x] = pls;
-      Dl[threadIdx.x] = pdl;
-    }
-    __syncthreads();
-    if (it + 1 < items) prefetch(it + 1);
+    if (it + 1 < items) prefetch(it + 1, cur ^ 1);
+    const bf16_t* Qs = reinterpret_cast<const bf16_t*>(smem + (2 * cur) * TILE_BYTES_R);
+    const bf16_t* Os = reinterpret_cast<const bf16_t*>(smem + (2 * cur + 1) * TILE_BYTES_R);
+    const float* Lc = Ls[cur];
+    const float* Dc = Dl[cur];
 
     // S[q][key], dP[q][key] for this wave's 32 query rows and 32 keys.
     f32x16 sa, pa;
@@ -251,17 +156,16 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.0f;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const int ro = (qh * 32 + c) * RLD + kc * 16 + g * 8;
-      sa = mfma32(lds8(Qs + ro), kf[kc], sa);
-      pa = mfma32(lds8(Os + ro), vf[kc], pa);
+      sa = mfma32(row_frag(Qs, qh * 32 + c, kc * 16 + g * 8), kf[kc], sa);
+      pa = mfma32(row_frag(Os, qh * 32 + c, kc * 16 + g * 8), vf[kc], pa);
     }
     // P and dS in place: sa <- P, pa <- dS.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = qh * 32 + acc_row(r, g);
-      float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Ls[qi]);
+      float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Lc[qi] * LOG2E);
       if (diag && key > qi) p = 0.0f;
-      const float ds = p * (pa[r] - Dl[qi]);
+      const float ds = p * (pa[r] - Dc[qi]);
       sa[r] = p;
       pa[r] = ds;
       dlsum += ds;
@@ -273,8 +177,8 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
       const bf16x8 db = pack8(pa, ch * 8);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        dva[dt] = mfma32(trans_frag(Ot, dt * 32 + c, qh * 2 + ch, g), pb, dva[dt]);
-        dka[dt] = mfma32(trans_frag(Qt, dt * 32 + c, qh * 2 + ch, g), db, dka[dt]);
+        dva[dt] = mfma32(tr_frag(Os, qh * 32 + ch * 16, dt * 32), pb, dva[dt]);
+        dka[dt] = mfma32(tr_frag(Qs, qh * 32 + ch * 16, dt * 32), db, dka[dt]);
       }
     }
     if (it % dm.g == dm.g - 1) {
@@ -288,6 +192,8 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
       }
       dlsum = 0.0f;
     }
+    wait_all_loads();   // this wave's copies of the next item
+    __syncthreads();    // all copies landed; everyone is done with `cur`
   }
 
   // Sum the two query halves through LDS: partial [kt][dk|dv][dt*16 + r][lane].
@@ -331,18 +237,17 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int HPW = 4;
-constexpr int DQ_NW = 8;
+constexpr int HPW = 2;   // heads per dQ workgroup
+constexpr int DQ_NW = 4;  // waves: two 32-row halves per head
 constexpr int DQ_NT = 64 * DQ_NW;
 
-__global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
+__global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ Dv,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, bf16_t* __restrict__ dq) {
-  __shared__ __align__(16) bf16_t Ks[BS * RLD];
-  __shared__ __align__(16) bf16_t Vs[BS * RLD];
-  __shared__ __align__(16) bf16_t Kt[D * TLD];
+  __shared__ __align__(16) bf16_t Ks[2][BS * TILE_LD];
+  __shared__ __align__(16) bf16_t Vs[2][BS * TILE_LD];
   __shared__ int blist[65];
   __shared__ float bbias[65];
   __shared__ int nblk;
@@ -398,21 +303,21 @@ __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  RowPairs<DQ_NT> pk, pv;
-  pk.load(kbase + (size_t)blist[0] * BS * D);
-  pv.load(vbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<DQ_NW>(Ks[0], kbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<DQ_NW>(Vs[0], vbase + (size_t)blist[0] * BS * D);
+  wait_all_loads();
+  __syncthreads();
   for (int bi = 0; bi < nb; ++bi) {
+    const int cur = bi & 1;
     const int m = blist[bi];
     const float off2 = bbias[bi] - l2;
     const bool diag = m == t;
-    __syncthreads();
-    pk.store(Ks, Kt);
-    pv.store(Vs, nullptr);
-    __syncthreads();
     if (bi + 1 < nb) {
-      pk.load(kbase + (size_t)blist[bi + 1] * BS * D);
-      pv.load(vbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<DQ_NW>(Ks[cur ^ 1], kbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<DQ_NW>(Vs[cur ^ 1], vbase + (size_t)blist[bi + 1] * BS * D);
     }
+    const bf16_t* Kc = Ks[cur];
+    const bf16_t* Vc = Vs[cur];
 
     // Per 32-key tile: S^T, dP^T (keys x this wave's 32 queries), then dS^T
     // packed to bf16 as the B operand of the dQ^T update.
@@ -424,9 +329,8 @@ __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
       for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        const int ro = (kt * 32 + c) * RLD + kc * 16 + g * 8;
-        sa = mfma32(lds8(Ks + ro), qf[kc], sa);
-        pa = mfma32(lds8(Vs + ro), of[kc], pa);
+        sa = mfma32(row_frag(Kc, kt * 32 + c, kc * 16 + g * 8), qf[kc], sa);
+        pa = mfma32(row_frag(Vc, kt * 32 + c, kc * 16 + g * 8), of[kc], pa);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -442,7 +346,9 @@ __global__ void __launch_bounds__(DQ_NT) bwd_dq_mfma_kernel(
     for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        dqa[dt] = mfma32(trans_frag(Kt, dt * 32 + c, ch, g), db[ch], dqa[dt]);
+        dqa[dt] = mfma32(tr_frag(Kc, ch * 16, dt * 32), db[ch], dqa[dt]);
+    wait_all_loads();
+    __syncthreads();
   }
 
   // dQ = scale * (dQ^T)^T: lane holds query qi, dims dt*32 + acc_row(r, g).

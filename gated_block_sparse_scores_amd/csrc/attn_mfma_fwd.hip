@@ -6,16 +6,20 @@
 // (g0 = 1), unselected blocks are never loaded, the softmax is online and no
 // attention matrix is stored.
 //
-// Work unit: one (batch, KV head, query block, 4-head chunk) tile = 4 heads x
-// 64 query rows; every K/V block it needs is gathered once into LDS and serves
-// the 4 heads (one selection per KV head).  Eight waves: wave w owns 32 rows
-// (half w % 2 of the block) of head kv*G + 4*chunk + w / 2, which keeps each
-// wave's working set (Q fragments, S^T, O^T) inside 256 VGPRs.
+// Work unit: one (batch, KV head, query block, 2-head chunk) tile = 2 heads x
+// 64 query rows; every K/V block it needs is gathered into LDS and serves both
+// heads (one selection per KV head).  Four waves: wave w owns 32 rows (half
+// w % 2 of the block) of head kv*G + 2*chunk + w / 2, which keeps each wave's
+// working set (Q fragments, S^T, O^T) inside 256 VGPRs and lets two workgroups
+// share a CU.  K/V blocks are copied global -> LDS with the direct-to-LDS load
+// into a double buffer: the next block's copy is in flight while the current
+// one is computed, with one barrier per block.
 //   S^T = K Q^T   (32x32x16 MFMA; A = K rows from LDS, B = Q rows held in
 //                  registers), so each lane holds one query column and the
 //                  softmax max/sum over keys stays inside the lane (plus one
 //                  exchange with lane l^32);
-//   O^T += V^T P^T (A = V^T from a transposed LDS copy of V, B = P^T straight
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with the
+//                  transposing LDS read ds_read_b64_tr_b16, B = P^T straight
 //                  from the S^T accumulators, converted to bf16).
 // The bias (log-gate) is added before the running max, in log2 units.  The
 // running max is a reference that is only moved (and O, l rescaled) when a
@@ -35,70 +39,20 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BS = 64;
-constexpr int KLD = D + 8;   // K row stride in LDS (bf16 elements): 272 B
-constexpr int VLD = BS + 4;  // V^T row stride in LDS (bf16 elements): 136 B
+// K and V tiles: 64 x 128 bf16 each, swizzled (see mfma.h)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-constexpr int HPW = 4;   // heads per workgroup
-constexpr int NW = 8;    // waves per workgroup (two 32-row halves per head)
+constexpr int HPW = 2;   // heads per workgroup
+constexpr int NW = 4;    // waves per workgroup (two 32-row halves per head)
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
-struct Stage {
-  static constexpr int NT = 64 * NW;
-  static constexpr int KCH = (BS * D / 8) / NT;   // 16-byte K chunks per thread
-  static constexpr int VUN = (BS / 2) * (D / 8) / NT;  // (key pair, 8 dims) units per thread
-  uint4 kreg[KCH];
-  uint4 vreg[VUN][2];
-
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ kblk,
-                                       const bf16_t* __restrict__ vblk) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int u = tid + i * NT;
-      kreg[i] = *reinterpret_cast<const uint4*>(kblk + (size_t)(u >> 4) * D + (u & 15) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT;
-      const int dg = u & 15, kp = u >> 4;
-      vreg[i][0] = *reinterpret_cast<const uint4*>(vblk + (size_t)(2 * kp) * D + dg * 8);
-      vreg[i][1] = *reinterpret_cast<const uint4*>(vblk + (size_t)(2 * kp + 1) * D + dg * 8);
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16_t* Ks, bf16_t* Vt) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int u = tid + i * NT;
-      *reinterpret_cast<uint4*>(Ks + (u >> 4) * KLD + (u & 15) * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT;
-      const int dg = u & 15, kp = u >> 4;
-      const uint32_t a[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-      const uint32_t b[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims dg*8 + 2w (low halves) and dg*8 + 2w + 1 (high halves)
-        const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
-        const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(Vt + (dg * 8 + 2 * w) * VLD + 2 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(Vt + (dg * 8 + 2 * w + 1) * VLD + 2 * kp) = hi;
-      }
-    }
-  }
-};
-
-__global__ void __launch_bounds__(64 * NW) fwd_mfma_kernel(
+__global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, bf16_t* __restrict__ o, float* __restrict__ lse) {
-  __shared__ __align__(16) bf16_t Ks[BS * KLD];
-  __shared__ __align__(16) bf16_t Vt[D * VLD];
+  __shared__ __align__(16) bf16_t Ks[2][BS * TILE_LD];
+  __shared__ __align__(16) bf16_t Vs[2][BS * TILE_LD];
   __shared__ int blist[65];
   __shared__ float bbias[65];
   __shared__ int nblk;
@@ -154,18 +108,22 @@ __global__ void __launch_bounds__(64 * NW) fwd_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  Stage st;
-  st.load(kbase + (size_t)blist[0] * BS * D, vbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<NW>(Ks[0], kbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<NW>(Vs[0], vbase + (size_t)blist[0] * BS * D);
+  wait_all_loads();
+  __syncthreads();
 
   for (int bi = 0; bi < nb; ++bi) {
-    __syncthreads();
-    st.store(Ks, Vt);
-    __syncthreads();
+    const int cur = bi & 1;
     const int m = blist[bi];
     const float bias2 = bbias[bi];
     const bool diag = m == t;
-    if (bi + 1 < nb)
-      st.load(kbase + (size_t)blist[bi + 1] * BS * D, vbase + (size_t)blist[bi + 1] * BS * D);
+    if (bi + 1 < nb) {
+      tile_load_lds<NW>(Ks[cur ^ 1], kbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<NW>(Vs[cur ^ 1], vbase + (size_t)blist[bi + 1] * BS * D);
+    }
+    const bf16_t* Kc = Ks[cur];
+    const bf16_t* Vc = Vs[cur];
 
     // S^T[key][query]: 64 keys x the wave's 32 queries.
     f32x16 sacc[2];
@@ -177,9 +135,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_mfma_kernel(
     for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + c) * KLD + kc * 16 + g * 8);
-        sacc[kt] = mfma32(a, qf[kc], sacc[kt]);
+        sacc[kt] = mfma32(row_frag(Kc, kt * 32 + c, kc * 16 + g * 8), qf[kc], sacc[kt]);
       }
 
     // Max of the raw logits (scale > 0, bias uniform over the block).
@@ -221,13 +177,11 @@ __global__ void __launch_bounds__(64 * NW) fwd_mfma_kernel(
     for (int ch = 0; ch < 4; ++ch) {
       const bf16x8 pf = pack8(sacc[ch >> 1], (ch & 1) * 8);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16_t* vr = Vt + (dt * 32 + c) * VLD + ch * 16 + g * 4;
-        const bf16x8 a = cat4(*reinterpret_cast<const bf16x4*>(vr),
-                              *reinterpret_cast<const bf16x4*>(vr + 8));
-        oacc[dt] = mfma32(a, pf, oacc[dt]);
-      }
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = mfma32(tr_frag(Vc, ch * 16, dt * 32), pf, oacc[dt]);
     }
+    wait_all_loads();   // this wave's copies of the next block
+    __syncthreads();    // everyone's copies landed; everyone is done with `cur`
   }
 
   // Normalise and store o (bf16) and LSE (natural log).
