@@ -44,10 +44,66 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- dK / dV
 constexpr int DKV_NT = 256;
-constexpr int DKV_MAXT = 8192;  // longest inverse list (query blocks) held in LDS
+constexpr int DKV_MAXT = 4096;  // longest inverse list (query blocks) held in LDS
 constexpr int TILE_BYTES_R = BS * TILE_LD * 2;   // one 64 x 128 tile
 constexpr int DKV_SMEM = 4 * TILE_BYTES_R;       // q and dout, double buffered (also the
                                                  // 64 KB of the final half-sum)
+
+// One item's q and dout rows (two 64 x 128 tiles) plus its 64 LSE and D
+// values, held in registers between the global load and the LDS store:
+// thread i holds the 16-byte chunks j = i + 256 u (u = 0..3) of each tile, so
+// consecutive threads read consecutive 16 bytes.
+// Ordinary loads are used here rather than the direct-to-LDS copy because the
+// compiler makes every transposing LDS read wait for all direct-to-LDS copies
+// in flight, which would serialise the prefetch with the compute.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct DkvStage {
+  u32x4 q0, q1, q2, q3, o0, o1, o2, o3;
+  float ld;
+};
+
+__device__ __forceinline__ void dkv_stage_load(DkvStage& st, const bf16_t* __restrict__ q,
+                                               const bf16_t* __restrict__ dout,
+                                               const float* __restrict__ lse,
+                                               const float* __restrict__ Dv, size_t rb) {
+  const int tid = threadIdx.x;
+  constexpr int U = DKV_NT * 8;  // elements between a thread's chunks
+  const u32x4* qs = reinterpret_cast<const u32x4*>(q + rb * D + tid * 8);
+  const u32x4* os = reinterpret_cast<const u32x4*>(dout + rb * D + tid * 8);
+  st.q0 = qs[0];
+  st.o0 = os[0];
+  st.q1 = qs[U / 8];
+  st.o1 = os[U / 8];
+  st.q2 = qs[2 * U / 8];
+  st.o2 = os[2 * U / 8];
+  st.q3 = qs[3 * U / 8];
+  st.o3 = os[3 * U / 8];
+  // every thread loads (threads past 128 re-read a D value) so the load is
+  // unconditional and its register is never written on another path
+  st.ld = (tid < BS ? lse : Dv)[rb + (tid & (BS - 1))];
+}
+
+// Chunk j = tid + 256 u sits in row j / 16 = tid / 16 + 16 u at chunk tid % 16;
+// the swizzle depends on row % 16 only, so the four rows share one pattern.
+__device__ __forceinline__ void dkv_stage_store(const DkvStage& st, bf16_t* Qb, bf16_t* Ob,
+                                                float* Lb, float* Db) {
+  const int tid = threadIdx.x;
+  const int o = swz(tid >> 4, (tid & 15) * 8);
+  constexpr int U = 16 * TILE_LD;
+  *reinterpret_cast<u32x4*>(Qb + o) = st.q0;
+  *reinterpret_cast<u32x4*>(Ob + o) = st.o0;
+  *reinterpret_cast<u32x4*>(Qb + o + U) = st.q1;
+  *reinterpret_cast<u32x4*>(Ob + o + U) = st.o1;
+  *reinterpret_cast<u32x4*>(Qb + o + 2 * U) = st.q2;
+  *reinterpret_cast<u32x4*>(Ob + o + 2 * U) = st.o2;
+  *reinterpret_cast<u32x4*>(Qb + o + 3 * U) = st.q3;
+  *reinterpret_cast<u32x4*>(Ob + o + 3 * U) = st.o3;
+  if (tid < BS)
+    Lb[tid] = st.ld;
+  else if (tid < 2 * BS)
+    Db[tid - BS] = st.ld;
+}
 
 __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -58,7 +114,11 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
   __shared__ __align__(16) unsigned char smem[DKV_SMEM];
   __shared__ float Ls[2][BS], Dl[2][BS];
   __shared__ float red[4];
-  __shared__ int lst[DKV_MAXT];
+  // Query blocks t attending to block m (ascending), with the slot of m in
+  // t's selection (0xFF on the diagonal) and its log gate (x log2 e).
+  __shared__ uint16_t lst[DKV_MAXT];
+  __shared__ uint8_t lslot[DKV_MAXT];
+  __shared__ float lbias[DKV_MAXT];
   __shared__ int scan_scr[16];
 
   // key blocks ascending (low blocks are selected by the most query blocks, so
@@ -96,60 +156,58 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
   int ne = 0;
   for (int t0 = m; t0 < dm.T; t0 += DKV_NT) {
     const int tt = t0 + (int)threadIdx.x;
-    int sl = 0xFF;
-    if (tt == m)
-      sl = 0xFE;
-    else if (tt < dm.T)
-      sl = srow[tt];
-    const int flag = sl != 0xFF;
+    const int sl = (tt < dm.T && tt != m) ? srow[tt] : 0xFF;
+    const int flag = tt == m || sl != 0xFF;
     int cnt;
     const int pos = block_excl_scan(flag, scan_scr, &cnt);
-    if (flag) lst[ne + pos] = (tt << 8) | sl;
+    if (flag) {
+      lst[ne + pos] = (uint16_t)tt;
+      lslot[ne + pos] = (uint8_t)sl;
+      lbias[ne + pos] =
+          (sl != 0xFF && logg) ? logg[(bk * dm.T + tt) * (size_t)dm.K + sl] * LOG2E : 0.0f;
+    }
     ne += cnt;
   }
+  // K / V fragments in place before the loop, so that the only loads in
+  // flight inside it are the staged rows.
+  wait_all_loads();
   __syncthreads();
 
-  // Flat loop over (entry, head); the next item's q / dout rows, LSE and D are
-  // copied global -> LDS (direct-to-LDS loads, double buffered) while the
-  // current item is computed.
+  // Flat loop over (entry, head).  The q / dout rows, LSE and D of items
+  // it + 2 and it + 3 are in flight (two register stages, used alternately)
+  // while item it is computed; item it + 1 is already in the other LDS buffer.
   const int items = ne * dm.g;
   auto tile_base = [&](int it) {
-    const int t = lst[it / dm.g] >> 8;
+    const int t = lst[it / dm.g];
     const int h = kv * dm.g + it % dm.g;
     return ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
   };
-  typedef __attribute__((address_space(3))) void lds_void;
-  auto prefetch = [&](int it, int buf) {
-    const size_t rb = tile_base(it);
-    bf16_t* Qb = reinterpret_cast<bf16_t*>(smem + (2 * buf) * TILE_BYTES_R);
-    bf16_t* Ob = reinterpret_cast<bf16_t*>(smem + (2 * buf + 1) * TILE_BYTES_R);
-    tile_load_lds<4>(Qb, q + rb * D);
-    tile_load_lds<4>(Ob, dout + rb * D);
-    if (wave == 0) {
-      __builtin_amdgcn_global_load_lds((const void*)(lse + rb + lane), (lds_void*)&Ls[buf][0], 4,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(Dv + rb + lane), (lds_void*)&Dl[buf][0], 4,
-                                       0, 0);
-    }
+  auto qbuf = [&](int buf) { return reinterpret_cast<bf16_t*>(smem + (2 * buf) * TILE_BYTES_R); };
+  auto obuf = [&](int buf) {
+    return reinterpret_cast<bf16_t*>(smem + (2 * buf + 1) * TILE_BYTES_R);
   };
-  if (items > 0) prefetch(0, 0);
-  wait_all_loads();
+  DkvStage sa_st, sb_st;
+  if (items > 0) {
+    dkv_stage_load(sa_st, q, dout, lse, Dv, tile_base(0));
+    dkv_stage_store(sa_st, qbuf(0), obuf(0), Ls[0], Dl[0]);
+  }
+  if (items > 1) dkv_stage_load(sa_st, q, dout, lse, Dv, tile_base(1));
+  if (items > 2) dkv_stage_load(sb_st, q, dout, lse, Dv, tile_base(2));
   __syncthreads();
   float dlsum = 0.0f;
-  for (int it = 0; it < items; ++it) {
+  // One item: compute from buffer it % 2, then move `st` (item it + 1) into
+  // the other buffer and start loading item it + 3 into it.
+  auto item = [&](int it, DkvStage& st) {
     const int cur = it & 1;
     const int e = it / dm.g;
-    const int t = lst[e] >> 8;
-    const int slot = (lst[e] & 255) == 0xFE ? -1 : (lst[e] & 255);
-    const bool diag = slot < 0;
-    const float bias2 =
-        (!diag && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] * LOG2E : 0.0f;
-    if (it + 1 < items) prefetch(it + 1, cur ^ 1);
-    const bf16_t* Qs = reinterpret_cast<const bf16_t*>(smem + (2 * cur) * TILE_BYTES_R);
-    const bf16_t* Os = reinterpret_cast<const bf16_t*>(smem + (2 * cur + 1) * TILE_BYTES_R);
+    const bool diag = lst[e] == m;
+    const int slot = lslot[e];
+    const float bias2 = lbias[e];
+    const int t = lst[e];
+    const bf16_t* Qs = qbuf(cur);
+    const bf16_t* Os = obuf(cur);
     const float* Lc = Ls[cur];
     const float* Dc = Dl[cur];
-
     // S[q][key], dP[q][key] for this wave's 32 query rows and 32 keys.
     f32x16 sa, pa;
 #pragma unroll
@@ -192,8 +250,14 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
       }
       dlsum = 0.0f;
     }
-    wait_all_loads();   // this wave's copies of the next item
-    __syncthreads();    // all copies landed; everyone is done with `cur`
+    if (it + 1 < items)
+      dkv_stage_store(st, qbuf(cur ^ 1), obuf(cur ^ 1), Ls[cur ^ 1], Dl[cur ^ 1]);
+    if (it + 3 < items) dkv_stage_load(st, q, dout, lse, Dv, tile_base(it + 3));
+    __syncthreads();    // item it + 1 stored; everyone is done with `cur`
+  };
+  for (int it = 0; it < items; it += 2) {
+    item(it, sa_st);
+    if (it + 1 < items) item(it + 1, sb_st);
   }
 
   // Sum the two query halves through LDS: partial [kt][dk|dv][dt*16 + r][lane].
