@@ -1,6 +1,8 @@
 """Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--part all|train|decode] [--decode-workloads 4,5]
+    python bench.py --calibrate-copy      # plain 256 MiB device copy (counter scale)
 
 One step is one pass of the training hot path over the Qwen3-4B-shaped 8K
 workload (batch 1, 8192 tokens, 32 query / 8 KV heads, head_dim 128, bf16,
@@ -11,11 +13,19 @@ gradient ds.  `value` is selected-attention TFLOP/s: 12*d FLOP per attended
 (query head, query, key) pair (4d forward, 8d backward), divided by the step
 time.  The decode part of the path (batch 8 x 64K and batch 1 x 512K contexts)
 is measured in the same run and reported under "decode" in GB/s of selected
-K/V bytes.  Prints one JSON line.
+K/V bytes: each decode call takes a fresh query and the calls rotate over
+distinct per-layer K/V caches, so the selected blocks come from HBM rather than
+from the last-level cache.  Prints one JSON line.
+
+`roofline.traffic` is the HBM bytes per launch of the dominant kernel from the
+committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, scaled by the
+plain-copy calibration recorded there; it is null when that kernel's sources
+have changed since the counters were taken (source hash mismatch).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -73,6 +83,63 @@ def kernel_flops(name, pairs, d):
     return None
 
 
+# Sources of each measured kernel (its file plus the headers it includes): the
+# counter summary of a kernel is used only while these hash to the same value.
+CSRC = os.path.join(ROOT, "gated_block_sparse_scores_amd", "csrc")
+KERNEL_SOURCES = {
+    "bwd_dkdv_mfma": ["attn_mfma_bwd.hip", "mfma.h", "common.h", "internal.h"],
+    "bwd_dq_mfma": ["attn_mfma_bwd.hip", "mfma.h", "common.h", "internal.h"],
+    "fwd_mfma": ["attn_mfma_fwd.hip", "mfma.h", "common.h", "internal.h"],
+    "decode_split": ["decode.hip", "mfma.h", "common.h", "internal.h"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash(name):
+    files = KERNEL_SOURCES.get(name)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name, workload):
+    """HBM bytes per launch of `name` on `workload` from the committed counter
+    summary profiles/<name>.<workload>.traffic.txt (key: value lines), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{name}.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "$")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(name):
+        return None
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(n_bytes=256 << 20, reps=5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n_bytes, "reps": reps}), flush=True)
+
+
 def bench_train(args):
     import torch
     import synth
@@ -113,16 +180,20 @@ def bench_train(args):
     if kf is not None:
         ach = kf / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma" if mfma else "alu", "kernel": name, "achieved": round(ach, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                "avg_launch_ms": round(avg_ms, 4)}
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": recorded_traffic(name, w.name), "avg_launch_ms": round(avg_ms, 4)}
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
     return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
                 kernels=kernels, x=x, idx=idx)
 
 
-def bench_decode(wl, steps, layers=8):
-    """Decode of one new token per sequence over `layers` independent
-    selections (distinct queries), so consecutive calls read different blocks."""
+def bench_decode(wl, steps, layers=12):
+    """Decode of one new token per sequence.  Each call takes a fresh random
+    query (so a new selection) and the calls rotate over `layers` distinct K/V
+    caches with their own pooled-key caches, as consecutive layers of a model
+    would: 2 GiB of K/V per layer, far more than the last-level cache holds.
+    One call = pool the query over its head group, stand-in scores over the
+    pooled-key cache + gate normalisation + Top-K, split-K decode + LSE merge."""
     import torch
     import synth
     from gated_block_sparse_scores_amd import _lib as L
@@ -130,56 +201,75 @@ def bench_decode(wl, steps, layers=8):
 
     w = synth.workload(wl)
     dev = "cuda"
-    x = synth.decode_inputs(w, device=dev)
     Lc = w.seqlen
     C = (Lc - 1) // w.block
-    kb = ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16)
+    caches = []
+    for layer in range(layers):
+        x = synth.decode_inputs(w, seed=w.number * 1000 + layer, device=dev)
+        kb = ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16)
+        caches.append((x["kcache"], x["vcache"], kb))
+        del x
+    torch.cuda.synchronize()
     gen = torch.Generator(device=dev).manual_seed(1000 + wl)
-    qs = [torch.randn(x["q"].shape, generator=gen, device=dev).to(torch.bfloat16)
-          for _ in range(layers)]
-    sh = ops.shape_of(qs[0], x["kcache"], w.block, seqlen=Lc)
+    qshape = (w.batch, w.hq, w.head_dim)
+    calls = steps * layers
+    qs = [torch.randn(qshape, generator=gen, device=dev).to(torch.bfloat16)
+          for _ in range(calls + layers)]
+    sh = ops.shape_of(qs[0], caches[0][0], w.block, seqlen=Lc)
     ws = torch.empty(L.sas_decode_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
 
-    def one(q):
+    def one(q, layer):
+        kc, vc, kb = caches[layer]
         qb = ops.block_pool(q.unsqueeze(2), w.block, w.group)
         idx, logg, _, _ = ops.select_topk(w.batch, w.hkv, 1, C, w.topk, row_offset=C, qbar=qb,
                                           kbar=kb)
-        return ops.decode(q, x["kcache"], x["vcache"], Lc, idx[:, :, 0], logg[:, :, 0],
-                          w.block, workspace=ws)
+        return ops.decode(q, kc, vc, Lc, idx[:, :, 0], logg[:, :, 0], w.block, workspace=ws)
 
-    for q in qs:
-        one(q)
+    for layer in range(layers):               # warm-up: one call per layer
+        one(qs[calls + layer], layer)
     torch.cuda.synchronize()
     L.sas_profiler_reset()
     L.sas_profiler_enable(True)
     t0 = time.perf_counter()
-    for it in range(steps):
-        for q in qs:
-            one(q)
+    for c in range(calls):
+        one(qs[c], c % layers)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     L.sas_profiler_enable(False)
     kt = L.sas_profiler_read()
-    calls = steps * layers
     us_step = (t1 - t0) * 1e6 / calls
     sel_bytes = w.batch * w.hkv * (w.topk + 1) * w.block * w.head_dim * 2 * 2
     kbar_bytes = w.batch * w.hkv * C * w.head_dim * 2
-    dsplit = kt.get("decode_split", (1, 0.0))
-    dmerge = kt.get("decode_merge", (1, 0.0))
-    split_us = dsplit[1] / dsplit[0] * 1e3
-    merge_us = dmerge[1] / dmerge[0] * 1e3
-    dec_gbs = sel_bytes / (split_us * 1e-6) / 1e9
+
+    def avg_us(name):
+        n, tot = kt.get(name, (1, 0.0))
+        return tot / n * 1e3
+
+    split_us, merge_us = avg_us("decode_split"), avg_us("decode_merge")
+    sel_us = avg_us("block_pool") + sum(avg_us(k) for k in
+                                        ("standin_scores", "topk", "select_chunk", "select_merge")
+                                        if k in kt)
+    split_gbs = sel_bytes / (split_us * 1e-6) / 1e9
+    dec_gbs = sel_bytes / ((split_us + merge_us) * 1e-6) / 1e9
+    gpu_us = sel_us + split_us + merge_us
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)} for k, v in kt.items()}
+    del caches
+    torch.cuda.empty_cache()
     return {
         "workload": w.name, "batch": w.batch, "context": Lc, "hq": w.hq, "hkv": w.hkv,
-        "topk": w.topk, "selected_kv_bytes": sel_bytes, "pooled_key_bytes": kbar_bytes,
+        "topk": w.topk, "layers_rotated": layers, "calls": calls,
+        "selected_kv_bytes": sel_bytes, "pooled_key_bytes": kbar_bytes,
         "decode_GBps": round(dec_gbs, 1),
-        "decode_plus_merge_us": round(split_us + merge_us, 2),
-        "step_us": round(us_step, 2),
-        "step_GBps": round((sel_bytes + kbar_bytes) / (us_step * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(dec_gbs, 1),
+        "decode_frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+        "decode_us": round(split_us + merge_us, 2),
+        "selection_us": round(sel_us, 2),
+        "gpu_us_per_call": round(gpu_us, 2),
+        "gpu_GBps_per_call": round((sel_bytes + kbar_bytes) / (gpu_us * 1e-6) / 1e9, 1),
+        "wall_us_per_call": round(us_step, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(split_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic("decode_split", w.name),
                      "avg_launch_us": round(split_us, 2)},
         "kernels": kernels,
     }
@@ -234,6 +324,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
+    ap.add_argument("--decode-workloads", default="4,5")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the path is single-GPU by design "
@@ -244,34 +337,38 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    log("training workload ...")
-    res = bench_train(args)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     out = {
         "metric": "gated sparse attn fwd+bwd TFLOP/s, decode GB/s; % of MI355X roofline",
-        "value": round(res["tflops"], 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(res["ms"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": res["w"].name, "batch": 1, "seq_len": res["w"].seqlen,
-                   "hq": 32, "hkv": 8, "head_dim": 128, "block": 64, "topk": res["w"].topk,
-                   "selector": "mean-pooled stand-in", "parallelism": "none"},
-        "selected_pairs": int(res["pairs"]),
-        "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
-        "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
-        "roofline": res["roofline"],
-        "kernels": res["kernels"],
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
     }
-    if not args.no_decode:
+    res = None
+    if args.part in ("all", "train"):
+        log("training workload ...")
+        res = bench_train(args)
+        out.update({
+            "value": round(res["tflops"], 3),
+            "ms_per_step": round(res["ms"], 4),
+            "config": {"workload": res["w"].name, "batch": 1, "seq_len": res["w"].seqlen,
+                       "hq": 32, "hkv": 8, "head_dim": 128, "block": 64,
+                       "topk": res["w"].topk, "selector": "mean-pooled stand-in",
+                       "parallelism": "none"},
+            "selected_pairs": int(res["pairs"]),
+            "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
+            "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "roofline": res["roofline"],
+            "kernels": res["kernels"],
+        })
+    if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")
-        out["decode"] = [bench_decode(4, steps=10), bench_decode(5, steps=25)]
-    if not args.no_cpu_baseline:
+        steps = {4: 10, 5: 25}
+        out["decode"] = [bench_decode(int(wl), steps=steps.get(int(wl), 10))
+                         for wl in args.decode_workloads.split(",") if wl]
+    if res is not None and not args.no_cpu_baseline:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(res)
     print(json.dumps(out), flush=True)

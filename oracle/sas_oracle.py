@@ -31,9 +31,14 @@ Per row r = (batch b, KV head kv, query block t), with valid history length C_t:
      ([picx] Eq. 5, inner gating), and ds through the gate softmax of step 2;
   7. decode: the same for a single query token at position L - 1.
 
-Readings taken where the pages leave a step open are listed in the design doc of
-the repository (all-history softmax domain, token-causal current block, one
-selection per KV head shared by its query heads, decode position L - 1, ...).
+Readings taken where the pages leave a step open: the gate softmax runs over
+all C_t history blocks of the row (not only the selected ones); the 1/sqrt(d)
+scale multiplies q . k only, never the log gate; Top-K ranks s (ties to the
+lower block index, -0.0 == +0.0) and takes all C_t blocks when K >= C_t; the
+current block is token-causal and selected blocks are fully visible; one
+selection per (batch, KV head, query block) is shared by the block's rows and
+the KV head's G query heads; a decode query sits at position L - 1 of a cache
+of valid length L, its current block being (L - 1) / bs.
 
 Arithmetic: float64 throughout, except where a floating-point value decides an
 integer (the Top-K ranking): that decision is taken on fp32 scores, the
