@@ -45,80 +45,31 @@ constexpr float LOG2E = 1.4426950408889634f;
 // ---------------------------------------------------------------- dK / dV
 constexpr int DKV_NT = 256;
 constexpr int DKV_MAXT = 4096;  // longest inverse list (query blocks) held in LDS
-constexpr int TILE_BYTES_R = BS * TILE_LD * 2;   // one 64 x 128 tile
-constexpr int DKV_SMEM = 4 * TILE_BYTES_R;       // q and dout, double buffered (also the
-                                                 // 64 KB of the final half-sum)
 
-// One item's q and dout rows (two 64 x 128 tiles) plus its 64 LSE and D
-// values, held in registers between the global load and the LDS store:
-// thread i holds the 16-byte chunks j = i + 256 u (u = 0..3) of each tile, so
-// consecutive threads read consecutive 16 bytes.
-// Ordinary loads are used here rather than the direct-to-LDS copy because the
-// compiler makes every transposing LDS read wait for all direct-to-LDS copies
-// in flight, which would serialise the prefetch with the compute.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-struct DkvStage {
-  u32x4 q0, q1, q2, q3, o0, o1, o2, o3;
-  float ld;
-};
-
-__device__ __forceinline__ void dkv_stage_load(DkvStage& st, const bf16_t* __restrict__ q,
-                                               const bf16_t* __restrict__ dout,
-                                               const float* __restrict__ lse,
-                                               const float* __restrict__ Dv, size_t rb) {
-  const int tid = threadIdx.x;
-  constexpr int U = DKV_NT * 8;  // elements between a thread's chunks
-  const u32x4* qs = reinterpret_cast<const u32x4*>(q + rb * D + tid * 8);
-  const u32x4* os = reinterpret_cast<const u32x4*>(dout + rb * D + tid * 8);
-  st.q0 = qs[0];
-  st.o0 = os[0];
-  st.q1 = qs[U / 8];
-  st.o1 = os[U / 8];
-  st.q2 = qs[2 * U / 8];
-  st.o2 = os[2 * U / 8];
-  st.q3 = qs[3 * U / 8];
-  st.o3 = os[3 * U / 8];
-  // every thread loads (threads past 128 re-read a D value) so the load is
-  // unconditional and its register is never written on another path
-  st.ld = (tid < BS ? lse : Dv)[rb + (tid & (BS - 1))];
-}
-
-// Chunk j = tid + 256 u sits in row j / 16 = tid / 16 + 16 u at chunk tid % 16;
-// the swizzle depends on row % 16 only, so the four rows share one pattern.
-__device__ __forceinline__ void dkv_stage_store(const DkvStage& st, bf16_t* Qb, bf16_t* Ob,
-                                                float* Lb, float* Db) {
-  const int tid = threadIdx.x;
-  const int o = swz(tid >> 4, (tid & 15) * 8);
-  constexpr int U = 16 * TILE_LD;
-  *reinterpret_cast<u32x4*>(Qb + o) = st.q0;
-  *reinterpret_cast<u32x4*>(Ob + o) = st.o0;
-  *reinterpret_cast<u32x4*>(Qb + o + U) = st.q1;
-  *reinterpret_cast<u32x4*>(Ob + o + U) = st.o1;
-  *reinterpret_cast<u32x4*>(Qb + o + 2 * U) = st.q2;
-  *reinterpret_cast<u32x4*>(Ob + o + 2 * U) = st.o2;
-  *reinterpret_cast<u32x4*>(Qb + o + 3 * U) = st.q3;
-  *reinterpret_cast<u32x4*>(Ob + o + 3 * U) = st.o3;
-  if (tid < BS)
-    Lb[tid] = st.ld;
-  else if (tid < 2 * BS)
-    Db[tid - BS] = st.ld;
-}
-
-__global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
+// Two workgroups share a CU (at most 256 registers per lane and 64.6 KB of LDS
+// each), so one workgroup's MFMA work overlaps the other's softmax, barriers
+// and tile copies.  Wave w computes S and dP for keys 32 (w % 2) .. +32 and
+// query rows 32 (w / 2) .. +32, but accumulates dK^T, dV^T for the same keys
+// and head dims 64 (w / 2) .. +64 over all 64 rows: it takes the partner wave's
+// (w ^ 2) P and dS fragments for the other 32 rows from LDS.  Each wave then
+// owns its part of dK and dV outright, with no reduction at the end.  The next
+// item's q / dout rows, LSE, D and log gate are copied global -> LDS (direct-to-
+// LDS loads) once every wave is done with the current tiles.
+__global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ Dv,
     const float* __restrict__ logg, const uint8_t* __restrict__ slotmap,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg) {
-  __shared__ __align__(16) unsigned char smem[DKV_SMEM];
-  __shared__ float Ls[2][BS], Dl[2][BS];
+  __shared__ __align__(16) bf16_t Qs[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t Os[BS * TILE_LD];
+  __shared__ __align__(16) bf16x8 xch[4][4][64];  // [wave][P0, P1, dS0, dS1][lane]
+  __shared__ float Ls[BS], Dl[BS];
+  __shared__ float cur_bias;
   __shared__ float red[4];
-  // Query blocks t attending to block m (ascending), with the slot of m in
-  // t's selection (0xFF on the diagonal) and its log gate (x log2 e).
-  __shared__ uint16_t lst[DKV_MAXT];
-  __shared__ uint8_t lslot[DKV_MAXT];
-  __shared__ float lbias[DKV_MAXT];
+  // Query blocks t attending to block m (ascending): t | slot << 16, where slot
+  // is m's position in t's selection (0xFF on the diagonal).
+  __shared__ uint32_t lst[DKV_MAXT];
   __shared__ int scan_scr[16];
 
   // key blocks ascending (low blocks are selected by the most query blocks, so
@@ -131,7 +82,7 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
   const size_t bk = (size_t)b * dm.hkv + kv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
-  const int kt = wave & 1, qh = wave >> 1;
+  const int kt = wave & 1, qh = wave >> 1;  // qh also selects the head-dim half
   const int key = kt * 32 + c;  // key within the block (this lane's column)
 
   // K, V of the wave's 32 keys as B operands (column = key, k = dims).
@@ -142,9 +93,9 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     kf[kc] = *reinterpret_cast<const bf16x8*>(k + kvrow + kc * 16 + g * 8);
     vf[kc] = *reinterpret_cast<const bf16x8*>(v + kvrow + kc * 16 + g * 8);
   }
-  f32x16 dka[4], dva[4];
+  f32x16 dka[2], dva[2];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.0f;
 
@@ -160,54 +111,48 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
     const int flag = tt == m || sl != 0xFF;
     int cnt;
     const int pos = block_excl_scan(flag, scan_scr, &cnt);
-    if (flag) {
-      lst[ne + pos] = (uint16_t)tt;
-      lslot[ne + pos] = (uint8_t)sl;
-      lbias[ne + pos] =
-          (sl != 0xFF && logg) ? logg[(bk * dm.T + tt) * (size_t)dm.K + sl] * LOG2E : 0.0f;
-    }
+    if (flag) lst[ne + pos] = (uint32_t)tt | ((uint32_t)sl << 16);
     ne += cnt;
   }
-  // K / V fragments in place before the loop, so that the only loads in
-  // flight inside it are the staged rows.
-  wait_all_loads();
   __syncthreads();
 
-  // Flat loop over (entry, head).  The q / dout rows, LSE and D of items
-  // it + 2 and it + 3 are in flight (two register stages, used alternately)
-  // while item it is computed; item it + 1 is already in the other LDS buffer.
   const int items = ne * dm.g;
-  auto tile_base = [&](int it) {
-    const int t = lst[it / dm.g];
+  typedef __attribute__((address_space(3))) void lds_void;
+  // Copies item `it` into the tiles: q and dout rows by all waves, LSE and D
+  // by wave 0, the log gate by lane 0 of wave 1 (or a 0 when ungated).
+  auto fetch = [&](int it) {
+    const uint32_t ent = lst[it / dm.g];
+    const int t = (int)(ent & 0xFFFF), sl = (int)(ent >> 16);
     const int h = kv * dm.g + it % dm.g;
-    return ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
+    const size_t rb = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS;
+    tile_load_lds<4>(Qs, q + rb * D);
+    tile_load_lds<4>(Os, dout + rb * D);
+    if (wave == 0) {
+      __builtin_amdgcn_global_load_lds((const void*)(lse + rb + lane), (lds_void*)Ls, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Dv + rb + lane), (lds_void*)Dl, 4, 0, 0);
+    } else if (wave == 1) {
+      if (logg && sl != 0xFF) {
+        if (lane == 0)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(logg + (bk * dm.T + t) * (size_t)dm.K + sl), (lds_void*)&cur_bias,
+              4, 0, 0);
+      } else if (lane == 0) {
+        cur_bias = 0.0f;
+      }
+    }
   };
-  auto qbuf = [&](int buf) { return reinterpret_cast<bf16_t*>(smem + (2 * buf) * TILE_BYTES_R); };
-  auto obuf = [&](int buf) {
-    return reinterpret_cast<bf16_t*>(smem + (2 * buf + 1) * TILE_BYTES_R);
-  };
-  DkvStage sa_st, sb_st;
-  if (items > 0) {
-    dkv_stage_load(sa_st, q, dout, lse, Dv, tile_base(0));
-    dkv_stage_store(sa_st, qbuf(0), obuf(0), Ls[0], Dl[0]);
-  }
-  if (items > 1) dkv_stage_load(sa_st, q, dout, lse, Dv, tile_base(1));
-  if (items > 2) dkv_stage_load(sb_st, q, dout, lse, Dv, tile_base(2));
+  if (items > 0) fetch(0);
+  wait_all_loads();
   __syncthreads();
   float dlsum = 0.0f;
-  // One item: compute from buffer it % 2, then move `st` (item it + 1) into
-  // the other buffer and start loading item it + 3 into it.
-  auto item = [&](int it, DkvStage& st) {
-    const int cur = it & 1;
+  for (int it = 0; it < items; ++it) {
     const int e = it / dm.g;
-    const bool diag = lst[e] == m;
-    const int slot = lslot[e];
-    const float bias2 = lbias[e];
-    const int t = lst[e];
-    const bf16_t* Qs = qbuf(cur);
-    const bf16_t* Os = obuf(cur);
-    const float* Lc = Ls[cur];
-    const float* Dc = Dl[cur];
+    const uint32_t ent = lst[e];
+    const int t = (int)(ent & 0xFFFF);
+    const int slot = (int)(ent >> 16);
+    const bool diag = t == m;
+    const float bias2 = cur_bias * LOG2E;
+
     // S[q][key], dP[q][key] for this wave's 32 query rows and 32 keys.
     f32x16 sa, pa;
 #pragma unroll
@@ -221,83 +166,74 @@ __global__ void __launch_bounds__(DKV_NT) bwd_dkdv_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = qh * 32 + acc_row(r, g);
-      float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Lc[qi] * LOG2E);
+      float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Ls[qi] * LOG2E);
       if (diag && key > qi) p = 0.0f;
-      const float ds = p * (pa[r] - Dc[qi]);
+      const float ds = p * (pa[r] - Dl[qi]);
       sa[r] = p;
       pa[r] = ds;
       dlsum += ds;
     }
-    // dV^T += dO^T P, dK^T += Q^T dS over this half's two 16-row chunks.
+    const bf16x8 p0 = pack8(sa, 0), p1 = pack8(sa, 8);
+    const bf16x8 d0 = pack8(pa, 0), d1 = pack8(pa, 8);
+    xch[wave][0][lane] = p0;
+    xch[wave][1][lane] = p1;
+    xch[wave][2][lane] = d0;
+    xch[wave][3][lane] = d1;
+    // dV^T += dO^T P, dK^T += Q^T dS for head dims 64 qh .. +64, first over this
+    // wave's own 32 rows (P, dS still in registers) ...
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      const bf16x8 pb = pack8(sa, ch * 8);
-      const bf16x8 db = pack8(pa, ch * 8);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        dva[dt] = mfma32(tr_frag(Os, qh * 32 + ch * 16, dt * 32), pb, dva[dt]);
-        dka[dt] = mfma32(tr_frag(Qs, qh * 32 + ch * 16, dt * 32), db, dka[dt]);
-      }
+    for (int dt = 0; dt < 2; ++dt) {
+      const int col = qh * 64 + dt * 32;
+      dva[dt] = mfma32(tr_frag(Os, qh * 32, col), p0, dva[dt]);
+      dka[dt] = mfma32(tr_frag(Qs, qh * 32, col), d0, dka[dt]);
+      dva[dt] = mfma32(tr_frag(Os, qh * 32 + 16, col), p1, dva[dt]);
+      dka[dt] = mfma32(tr_frag(Qs, qh * 32 + 16, col), d1, dka[dt]);
     }
-    if (it % dm.g == dm.g - 1) {
-      if (!diag && dlogg) {
-        // sum over the workgroup in a fixed order
-        const float ws = wave_sum(dlsum);
-        if (lane == 0) red[wave] = ws;
-        __syncthreads();
-        if (threadIdx.x == 0)
-          dlogg[(bk * dm.T + t) * (size_t)dm.K + slot] = (red[0] + red[1]) + (red[2] + red[3]);
-      }
+    const bool last_head = it % dm.g == dm.g - 1;
+    if (last_head) {
+      const float ws = wave_sum(dlsum);
+      if (lane == 0) red[wave] = ws;
       dlsum = 0.0f;
     }
-    if (it + 1 < items)
-      dkv_stage_store(st, qbuf(cur ^ 1), obuf(cur ^ 1), Ls[cur ^ 1], Dl[cur ^ 1]);
-    if (it + 3 < items) dkv_stage_load(st, q, dout, lse, Dv, tile_base(it + 3));
-    __syncthreads();    // item it + 1 stored; everyone is done with `cur`
-  };
-  for (int it = 0; it < items; it += 2) {
-    item(it, sa_st);
-    if (it + 1 < items) item(it + 1, sb_st);
+    __syncthreads();  // partner fragments and the dlogg partials are in LDS
+    if (last_head && !diag && dlogg && threadIdx.x == 0)
+      dlogg[(bk * dm.T + t) * (size_t)dm.K + slot] = (red[0] + red[1]) + (red[2] + red[3]);
+
+    // ... then over the partner wave's 32 rows (P, dS from LDS).
+    const int pw = wave ^ 2;
+    const int prow = (qh ^ 1) * 32;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 xp = xch[pw][hh][lane], xd = xch[pw][2 + hh][lane];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int col = qh * 64 + dt * 32;
+        dva[dt] = mfma32(tr_frag(Os, prow + 16 * hh, col), xp, dva[dt]);
+        dka[dt] = mfma32(tr_frag(Qs, prow + 16 * hh, col), xd, dka[dt]);
+      }
+    }
+    __syncthreads();  // everyone is done with the tiles and the exchange
+    if (it + 1 < items) fetch(it + 1);
+    wait_all_loads();
+    __syncthreads();  // item it + 1 is in the tiles
   }
 
-  // Sum the two query halves through LDS: partial [kt][dk|dv][dt*16 + r][lane].
-  float* part = reinterpret_cast<float*>(smem);
-  __syncthreads();
-  if (qh == 1) {
+  // dK = scale * (dK^T)^T, dV: lane holds key `key`, dims 64 qh + 32 dt + acc_row(r, g).
+  bf16_t* dkp = dk + kvrow;
+  bf16_t* dvp = dv + kvrow;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part[((kt * 2 + 0) * 64 + dt * 16 + r) * 64 + lane] = dka[dt][r];
-        part[((kt * 2 + 1) * 64 + dt * 16 + r) * 64 + lane] = dva[dt][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dka[dt][r] += part[((kt * 2 + 0) * 64 + dt * 16 + r) * 64 + lane];
-        dva[dt][r] += part[((kt * 2 + 1) * 64 + dt * 16 + r) * 64 + lane];
-      }
-    // dK = scale * (dK^T)^T, dV: lane holds key `key`, dims dt*32 + acc_row(r, g).
-    bf16_t* dkp = dk + kvrow;
-    bf16_t* dvp = dv + kvrow;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dd = dt * 32 + r4 * 8 + g * 4;
-        uint2 wk, wv;
-        wk.x = pack_bf16x2(dka[dt][r4 * 4] * dm.scale, dka[dt][r4 * 4 + 1] * dm.scale);
-        wk.y = pack_bf16x2(dka[dt][r4 * 4 + 2] * dm.scale, dka[dt][r4 * 4 + 3] * dm.scale);
-        wv.x = pack_bf16x2(dva[dt][r4 * 4], dva[dt][r4 * 4 + 1]);
-        wv.y = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
-        *reinterpret_cast<uint2*>(dkp + dd) = wk;
-        *reinterpret_cast<uint2*>(dvp + dd) = wv;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dd = qh * 64 + dt * 32 + r4 * 8 + g * 4;
+      uint2 wk, wv;
+      wk.x = pack_bf16x2(dka[dt][r4 * 4] * dm.scale, dka[dt][r4 * 4 + 1] * dm.scale);
+      wk.y = pack_bf16x2(dka[dt][r4 * 4 + 2] * dm.scale, dka[dt][r4 * 4 + 3] * dm.scale);
+      wv.x = pack_bf16x2(dva[dt][r4 * 4], dva[dt][r4 * 4 + 1]);
+      wv.y = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
+      *reinterpret_cast<uint2*>(dkp + dd) = wk;
+      *reinterpret_cast<uint2*>(dvp + dd) = wv;
+    }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -310,8 +246,13 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ Dv,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, bf16_t* __restrict__ dq) {
-  __shared__ __align__(16) bf16_t Ks[2][BS * TILE_LD];
-  __shared__ __align__(16) bf16_t Vs[2][BS * TILE_LD];
+  // Two K/V tile buffers as four separate arrays (see the forward kernel: the
+  // loop is unrolled by two so that copies and transposed reads of different
+  // buffers are known not to alias).
+  __shared__ __align__(16) bf16_t K0[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t V0[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t K1[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t V1[BS * TILE_LD];
   __shared__ int blist[65];
   __shared__ float bbias[65];
   __shared__ int nblk;
@@ -367,21 +308,19 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  tile_load_lds<DQ_NW>(Ks[0], kbase + (size_t)blist[0] * BS * D);
-  tile_load_lds<DQ_NW>(Vs[0], vbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<DQ_NW>(K0, kbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<DQ_NW>(V0, vbase + (size_t)blist[0] * BS * D);
   wait_all_loads();
   __syncthreads();
-  for (int bi = 0; bi < nb; ++bi) {
-    const int cur = bi & 1;
+  // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
+  auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
     const int m = blist[bi];
     const float off2 = bbias[bi] - l2;
     const bool diag = m == t;
     if (bi + 1 < nb) {
-      tile_load_lds<DQ_NW>(Ks[cur ^ 1], kbase + (size_t)blist[bi + 1] * BS * D);
-      tile_load_lds<DQ_NW>(Vs[cur ^ 1], vbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<DQ_NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<DQ_NW>(Vn, vbase + (size_t)blist[bi + 1] * BS * D);
     }
-    const bf16_t* Kc = Ks[cur];
-    const bf16_t* Vc = Vs[cur];
 
     // Per 32-key tile: S^T, dP^T (keys x this wave's 32 queries), then dS^T
     // packed to bf16 as the B operand of the dQ^T update.
@@ -413,6 +352,10 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
         dqa[dt] = mfma32(tr_frag(Kc, ch * 16, dt * 32), db[ch], dqa[dt]);
     wait_all_loads();
     __syncthreads();
+  };
+  for (int bi = 0; bi < nb; bi += 2) {
+    step(bi, K0, V0, K1, V1);
+    if (bi + 1 < nb) step(bi + 1, K1, V1, K0, V0);
   }
 
   // dQ = scale * (dQ^T)^T: lane holds query qi, dims dt*32 + acc_row(r, g).

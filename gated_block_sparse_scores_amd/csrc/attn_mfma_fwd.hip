@@ -51,8 +51,14 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, bf16_t* __restrict__ o, float* __restrict__ lse) {
-  __shared__ __align__(16) bf16_t Ks[2][BS * TILE_LD];
-  __shared__ __align__(16) bf16_t Vs[2][BS * TILE_LD];
+  // Two K/V tile buffers as four separate arrays: the loop below is unrolled
+  // by two so that each use names its buffer statically, which lets the
+  // compiler see that the copies into one buffer never alias the transposed
+  // reads of the other (it would otherwise wait for every copy in flight).
+  __shared__ __align__(16) bf16_t K0[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t V0[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t K1[BS * TILE_LD];
+  __shared__ __align__(16) bf16_t V1[BS * TILE_LD];
   __shared__ int blist[65];
   __shared__ float bbias[65];
   __shared__ int nblk;
@@ -108,22 +114,20 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  tile_load_lds<NW>(Ks[0], kbase + (size_t)blist[0] * BS * D);
-  tile_load_lds<NW>(Vs[0], vbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<NW>(K0, kbase + (size_t)blist[0] * BS * D);
+  tile_load_lds<NW>(V0, vbase + (size_t)blist[0] * BS * D);
   wait_all_loads();
   __syncthreads();
 
-  for (int bi = 0; bi < nb; ++bi) {
-    const int cur = bi & 1;
+  // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
+  auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
     const int m = blist[bi];
     const float bias2 = bbias[bi];
     const bool diag = m == t;
     if (bi + 1 < nb) {
-      tile_load_lds<NW>(Ks[cur ^ 1], kbase + (size_t)blist[bi + 1] * BS * D);
-      tile_load_lds<NW>(Vs[cur ^ 1], vbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
+      tile_load_lds<NW>(Vn, vbase + (size_t)blist[bi + 1] * BS * D);
     }
-    const bf16_t* Kc = Ks[cur];
-    const bf16_t* Vc = Vs[cur];
 
     // S^T[key][query]: 64 keys x the wave's 32 queries.
     f32x16 sacc[2];
@@ -181,7 +185,11 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
         oacc[dt] = mfma32(tr_frag(Vc, ch * 16, dt * 32), pf, oacc[dt]);
     }
     wait_all_loads();   // this wave's copies of the next block
-    __syncthreads();    // everyone's copies landed; everyone is done with `cur`
+    __syncthreads();    // everyone's copies landed; everyone is done with (Kc, Vc)
+  };
+  for (int bi = 0; bi < nb; bi += 2) {
+    step(bi, K0, V0, K1, V1);
+    if (bi + 1 < nb) step(bi + 1, K1, V1, K0, V0);
   }
 
   // Normalise and store o (bf16) and LSE (natural log).
