@@ -7,13 +7,16 @@
 //
 // Work split: the key list of (b, kv) is [valid selected blocks..., current
 // block]; workgroup (b, kv, split) takes `bps` consecutive entries of it and
-// serves all G query heads of kv from one read of each K/V row.  Each key row
-// (head_dim values) is read by 16 lanes with one vector load per lane, so a
-// wave reads 4 rows per instruction, fully coalesced; all K and V loads of the
-// split are issued before any arithmetic.  Dot products are reduced across the
-// 16 lanes with DPP row operations (no LDS round trip).  The partial (max,
-// sum, unnormalised output) of every split goes to the workspace; a second
-// kernel merges the splits of each (b, h) with log-sum-exp weights.
+// serves all G query heads of kv from one read of each K/V row.  The partial
+// (max, sum, unnormalised output) of every split goes to the workspace and the
+// splits of each (b, h) are merged with log-sum-exp weights.
+//  * bf16, head_dim 128, block 64 (decode_block4_kernel): four waves per
+//    workgroup, one selected block per wave, MFMA scores; the workgroup folds
+//    its four blocks in LDS into one partial.
+//  * every other shape (decode_split_kernel): each key row is read by 16 lanes
+//    with one vector load per lane, dot products reduced with DPP row
+//    operations.
+// A second kernel (decode_merge_kernel) merges the splits.
 #include <math.h>
 
 #include <type_traits>
@@ -349,22 +352,33 @@ __device__ __forceinline__ float row16_max(float x) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <int G>
-__global__ void __launch_bounds__(64) decode_block_mfma_kernel(
+// kDecWaves waves per workgroup (4 when there are enough workgroups to fill
+// the chip, else 1), one selected block per wave; the workgroup folds its
+// blocks into one partial in LDS, so the merge kernel reads a quarter of the
+// partials it would read at one block per workgroup.  (Merging in the last
+// workgroup to finish would need a device-scope fence per workgroup, which on
+// this multi-die part writes back the L2 and costs far more than the second
+// launch.)
+template <int G, int kDecWaves>
+__global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     Dims dm, int L, int cache_len, int nsplit, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const int32_t* __restrict__ idx,
     const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc) {
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
-  __shared__ __align__(16) uint32_t Pb[BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1) per head
+  __shared__ __align__(16) uint32_t Pb[kDecWaves][BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
+  __shared__ __align__(16) float wacc[kDecWaves][G][D];
+  __shared__ float wml[kDecWaves][G][2];
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int c = (L - 1) / BS;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t prow = (size_t)b * dm.hq + (size_t)kv * G;
+  const int hbase = (lane >> 4) * 4;
 
-  // The split-th entry of [valid selected blocks (slot order)..., current block].
+  // This wave's block: entry j of [valid selected blocks (slot order)..., current block].
+  const int j = split * kDecWaves + wave;
   int m = -1;
   float bias = 0.0f;
   {
@@ -372,161 +386,182 @@ __global__ void __launch_bounds__(64) decode_block_mfma_kernel(
     const bool ok = mm >= 0 && mm < c;
     const unsigned long long bal = __ballot(ok);
     const int nvalid = __popcll(bal);
-    if (split < nvalid) {
+    if (j < nvalid) {
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
-      const unsigned long long hit = __ballot(ok && before == split);
+      const unsigned long long hit = __ballot(ok && before == j);
       const int src = __ffsll((long long)hit) - 1;
       m = __shfl(mm, src);
       bias = logg ? logg[(size_t)bk * dm.K + src] : 0.0f;
-    } else if (split == nvalid) {
+    } else if (j == nvalid) {
       m = c;
     }
   }
-  if (m < 0) {  // empty split
-    if (lane < G) {
-      part_ml[((prow + lane) * nsplit + split) * 2 + 0] = -INFINITY;
-      part_ml[((prow + lane) * nsplit + split) * 2 + 1] = 0.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<float2*>(&part_acc[((prow + h) * nsplit + split) * D + 2 * lane]) =
-          make_float2(0.0f, 0.0f);
-    return;
-  }
-  const bf16_t* kbase = kc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
-  const bf16_t* vbase = vc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
-  const int pos0 = m * BS;
-  const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
-
-  // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
-  bf16x8_t kf[4][4];
-  uint32_t vr[BS];
-  if (pos0 + BS <= L) {  // full block (every history block): plain offsets
-    const bf16_t* krow = kbase + ((size_t)pos0 + (lane & 15)) * D + (lane >> 4) * 8;
-    const bf16_t* vrow = vbase + (size_t)pos0 * D + 2 * lane;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
-        kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
-#pragma unroll
-    for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
-  } else {  // the current block: rows past L - 1 are read clamped, then masked
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int pos = min(pos0 + kt * 16 + (lane & 15), last);
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
-        kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kbase + (size_t)pos * D + ch * 32 +
-                                                        (lane >> 4) * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < BS; ++r)
-      vr[r] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)min(pos0 + r, last) * D +
-                                                 2 * lane);
-  }
-  bf16x8_t qf[4];
-  {
-    const int h = lane & 15;
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
-      qf[ch] = h < G ? *reinterpret_cast<const bf16x8_t*>(q + (prow + h) * D + ch * 32 +
-                                                          (lane >> 4) * 8)
-                     : bf16x8_t{};
-  }
-
-  // S[h][key]: lane holds key kt*16 + lane%16, heads 4*(lane/16) + r.
-  f32x4_t sacc[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
-      sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ch], kf[kt][ch], sacc[kt], 0, 0, 0);
-  }
-  const int hbase = (lane >> 4) * 4;
-  float mh[4], lh[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int pos = pos0 + kt * 16 + (lane & 15);
-      const float z = pos < L ? sacc[kt][r] * dm.scale + bias : -INFINITY;
-      sacc[kt][r] = z;
-      mx = fmaxf(mx, z);
-    }
-    mx = row16_max(mx);
-    float sm = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const float pz = expf(sacc[kt][r] - mx);  // exp(-inf) = 0 for masked keys
-      sacc[kt][r] = pz;
-      sm += pz;
-    }
-    mh[r] = mx;
-    lh[r] = row16_sum(sm);
-  }
-  // P as bf16 pairs of consecutive keys: the even lane of each pair writes.
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = hbase + r;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const float mine = sacc[kt][r];
-      const float nb = __int_as_float(
-          __builtin_amdgcn_update_dpp(0, __float_as_int(mine), 0xB1, 0xF, 0xF, true));
-      if (h < G && (lane & 1) == 0)
-        Pb[(kt * 16 + (lane & 15)) >> 1][h] = pack_bf16x2(mine, nb);
-    }
-  }
-  __syncthreads();
-
+  float mh[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float acc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
+  if (m >= 0) {
+    const bf16_t* kbase = kc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
+    const bf16_t* vbase = vc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
+    const int pos0 = m * BS;
+    const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
+
+    // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
+    bf16x8_t kf[4][4];
+    uint32_t vr[BS];
+    if (pos0 + BS <= L) {  // full block (every history block): plain offsets
+      const bf16_t* krow = kbase + ((size_t)pos0 + (lane & 15)) * D + (lane >> 4) * 8;
+      const bf16_t* vrow = vbase + (size_t)pos0 * D + 2 * lane;
 #pragma unroll
-  for (int kp = 0; kp < BS / 2; ++kp) {
-    const uint32_t v0 = vr[2 * kp], v1 = vr[2 * kp + 1];
-    const bf16x2_t vlo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x05040100u));
-    const bf16x2_t vhi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x07060302u));
-    uint32_t pw[GP];
-    *reinterpret_cast<uint4*>(&pw[0]) = *reinterpret_cast<const uint4*>(&Pb[kp][0]);
-    if constexpr (GP == 8)
-      *reinterpret_cast<uint4*>(&pw[4]) = *reinterpret_cast<const uint4*>(&Pb[kp][4]);
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bf16x2_t ph = __builtin_bit_cast(bf16x2_t, pw[h]);
-      acc[h][0] = __builtin_amdgcn_fdot2_f32_bf16(ph, vlo, acc[h][0], false);
-      acc[h][1] = __builtin_amdgcn_fdot2_f32_bf16(ph, vhi, acc[h][1], false);
+        for (int ch = 0; ch < 4; ++ch)
+          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
+#pragma unroll
+      for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+    } else {  // the current block: rows past L - 1 are read clamped, then masked
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int pos = min(pos0 + kt * 16 + (lane & 15), last);
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kbase + (size_t)pos * D + ch * 32 +
+                                                          (lane >> 4) * 8);
+      }
+#pragma unroll
+      for (int r = 0; r < BS; ++r)
+        vr[r] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)min(pos0 + r, last) * D +
+                                                   2 * lane);
+    }
+    bf16x8_t qf[4];
+    {
+      const int h = lane & 15;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        qf[ch] = h < G ? *reinterpret_cast<const bf16x8_t*>(q + (prow + h) * D + ch * 32 +
+                                                            (lane >> 4) * 8)
+                       : bf16x8_t{};
+    }
+
+    // S[h][key]: lane holds key kt*16 + lane%16, heads 4*(lane/16) + r.
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ch], kf[kt][ch], sacc[kt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int pos = pos0 + kt * 16 + (lane & 15);
+        const float z = pos < L ? sacc[kt][r] * dm.scale + bias : -INFINITY;
+        sacc[kt][r] = z;
+        mx = fmaxf(mx, z);
+      }
+      mx = row16_max(mx);
+      float sm = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float pz = expf(sacc[kt][r] - mx);  // exp(-inf) = 0 for masked keys
+        sacc[kt][r] = pz;
+        sm += pz;
+      }
+      mh[r] = mx;
+      lh[r] = row16_sum(sm);
+    }
+    // P as bf16 pairs of consecutive keys: the even lane of each pair writes.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hbase + r;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float mine = sacc[kt][r];
+        const float nb = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(mine), 0xB1, 0xF, 0xF, true));
+        if (h < G && (lane & 1) == 0)
+          Pb[wave][(kt * 16 + (lane & 15)) >> 1][h] = pack_bf16x2(mine, nb);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own P is in LDS
+#pragma unroll
+    for (int kp = 0; kp < BS / 2; ++kp) {
+      const uint32_t v0 = vr[2 * kp], v1 = vr[2 * kp + 1];
+      const bf16x2_t vlo =
+          __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x05040100u));
+      const bf16x2_t vhi =
+          __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x07060302u));
+      uint32_t pw[GP];
+      *reinterpret_cast<uint4*>(&pw[0]) = *reinterpret_cast<const uint4*>(&Pb[wave][kp][0]);
+      if constexpr (GP == 8)
+        *reinterpret_cast<uint4*>(&pw[4]) = *reinterpret_cast<const uint4*>(&Pb[wave][kp][4]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bf16x2_t ph = __builtin_bit_cast(bf16x2_t, pw[h]);
+        acc[h][0] = __builtin_amdgcn_fdot2_f32_bf16(ph, vlo, acc[h][0], false);
+        acc[h][1] = __builtin_amdgcn_fdot2_f32_bf16(ph, vhi, acc[h][1], false);
+      }
     }
   }
+  // The wave's partial into LDS (an empty wave contributes max -inf, sum 0).
 #pragma unroll
   for (int h = 0; h < G; ++h)
-    *reinterpret_cast<float2*>(&part_acc[((prow + h) * nsplit + split) * D + 2 * lane]) =
-        make_float2(acc[h][0], acc[h][1]);
+    *reinterpret_cast<float2*>(&wacc[wave][h][2 * lane]) = make_float2(acc[h][0], acc[h][1]);
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = hbase + r;
       if (h < G) {
-        part_ml[((prow + h) * nsplit + split) * 2 + 0] = mh[r];
-        part_ml[((prow + h) * nsplit + split) * 2 + 1] = lh[r];
+        wml[wave][h][0] = mh[r];
+        wml[wave][h][1] = lh[r];
       }
     }
+  }
+  __syncthreads();
+
+  // Fold the four blocks: wave w takes heads w, w + 4, ...; weights e^{m - M},
+  // 0 for empty blocks.
+  for (int h = wave; h < G; h += kDecWaves) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wml[w][h][0]);
+    float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float l = wml[w][h][1];
+      const float wt = l > 0.0f ? expf(wml[w][h][0] - M) : 0.0f;
+      Ls += wt * l;
+      const float2 av = *reinterpret_cast<const float2*>(&wacc[w][h][2 * lane]);
+      a0 += wt * av.x;
+      a1 += wt * av.y;
+    }
+    const size_t pr = (prow + h) * nsplit + split;
+    *reinterpret_cast<float2*>(&part_acc[pr * D + 2 * lane]) = make_float2(a0, a1);
+    if (lane == 0) *reinterpret_cast<float2*>(&part_ml[pr * 2]) = make_float2(M, Ls);
   }
 }
 
 template <int G>
-void launch_decode_block(const Dims& dm, int L, int cache_len, int nsplit, const void* q,
-                         const void* kc, const void* vc, const int32_t* idx, const float* logg,
-                         float* part_ml, float* part_acc, hipStream_t st) {
+void launch_decode_block4(const Dims& dm, int L, int cache_len, int nsplit, int waves,
+                          const void* q, const void* kc, const void* vc, const int32_t* idx,
+                          const float* logg, float* part_ml, float* part_acc, hipStream_t st) {
   const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
-  hipLaunchKernelGGL(decode_block_mfma_kernel<G>, dim3((unsigned)wgs), dim3(64), 0, st, dm, L,
-                     cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
-                     idx, logg, part_ml, part_acc);
+  if (waves == 4)
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4>), dim3((unsigned)wgs), dim3(256), 0, st, dm,
+                       L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
+                       (const bf16_t*)vc, idx, logg, part_ml, part_acc);
+  else
+    hipLaunchKernelGGL((decode_block4_kernel<G, 1>), dim3((unsigned)wgs), dim3(64), 0, st, dm,
+                       L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
+                       (const bf16_t*)vc, idx, logg, part_ml, part_acc);
 }
 
+// Workspace: [partials (max, sum) per (b, h, split)][partial outputs per
+// (b, h, split, d)].
 template <typename T, int D, int BS>
 hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
                         const void* vc, const int32_t* idx, const float* logg, void* o,
@@ -537,31 +572,30 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
   {
     ProfScope ps("decode_split", st);
-    const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
-    (void)wgs;
     if constexpr (std::is_same<T, bf16_t>::value && D == 128 && BS == 64) {
+#define SAS_DEC_G(G_)                                                                     \
+  case G_:                                                                                \
+    launch_decode_block4<G_>(dm, L, cache_len, nsplit, bps, q, kc, vc, idx, logg, part_ml, \
+                             part_acc, st);                                               \
+    break;
       switch (dm.g) {
-        case 1: launch_decode_block<1>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 2: launch_decode_block<2>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 3: launch_decode_block<3>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 4: launch_decode_block<4>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 5: launch_decode_block<5>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 6: launch_decode_block<6>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        case 7: launch_decode_block<7>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
-        default: launch_decode_block<8>(dm, L, cache_len, nsplit, q, kc, vc, idx, logg, part_ml, part_acc, st); break;
+        SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4)
+        SAS_DEC_G(5) SAS_DEC_G(6) SAS_DEC_G(7) SAS_DEC_G(8)
+        default: return hipErrorInvalidValue;
       }
-    } else
+#undef SAS_DEC_G
+    } else {
+      const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
       hipLaunchKernelGGL((decode_split_kernel<T, D, BS>), dim3((unsigned)wgs), dim3(256), 0, st,
-                         dm, L, cache_len, bps, nsplit, (const T*)q, (const T*)kc, (const T*)vc,
-                         idx, logg, part_ml, part_acc);
+                         dm, L, cache_len, bps, nsplit, (const T*)q, (const T*)kc,
+                         (const T*)vc, idx, logg, part_ml, part_acc);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    ProfScope ps("decode_merge", st);
-    hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)(dm.b * dm.hq)), dim3(64), 0,
-                       st, nsplit, D, part_ml, part_acc, (T*)o, lse);
-  }
+  ProfScope ps("decode_merge", st);
+  hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)(dm.b * dm.hq)), dim3(64), 0, st,
+                     nsplit, D, part_ml, part_acc, (T*)o, lse);
   return hipGetLastError();
 }
 
@@ -570,7 +604,10 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
 bool decode_mfma_path(const Dims& dm) { return dm.bf16 && dm.d == 128 && dm.bs == 64; }
 
 int decode_blocks_per_split(const Dims& dm) {
-  if (decode_mfma_path(dm)) return 1;
+  // MFMA path: four blocks (waves) per workgroup when that still leaves at
+  // least two workgroups per CU, else one.
+  if (decode_mfma_path(dm))
+    return (long)dm.b * dm.hkv * ((dm.K + 4) / 4) >= 512 ? 4 : 1;
   const long total = (long)dm.b * dm.hkv * (dm.K + 1);
   return total >= 2048 ? 2 : 1;
 }

@@ -179,7 +179,8 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
  *   logg   [b, hkv, K] fp32 or NULL
  *   o      [b, hq, d] (shape->dtype);  lse fp32 [b, hq]
  * Split-K over the selected blocks with an LSE merge; the partials live in
- * the workspace.
+ * the workspace (no initial contents needed).  Calls that share a workspace
+ * must not run concurrently.
  * ---------------------------------------------------------------------- */
 size_t sas_decode_workspace_size(const sas_shape* shape, int K);
 sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* q,

@@ -40,6 +40,7 @@ CASES = [
     (2, 8, 1, 64, 128, 64, 3),      # no history: current block only
     (1, 16, 2, 3000, 128, 32, 64),
     (4, 32, 8, 2049, 128, 64, 8),
+    (8, 16, 8, 1500, 128, 64, 63),  # four blocks per workgroup; C = 23 < K: empty waves
 ]
 
 
@@ -119,3 +120,32 @@ def test_decode_workload_full(wl):
         eo, el = max_abs(o.cpu(), oo), max_abs(lse.cpu(), ol)
         say(f"  gated={gated}: o {eo:.2e} lse {el:.2e}")
         assert eo <= 2e-2 and el <= 2e-2
+
+
+def test_decode_workspace_reuse():
+    """One workspace (filled with garbage first) serves consecutive calls of
+    different shapes, every call matching the oracle.  Includes rows whose
+    selection has -1 pads and entries that are not history (empty splits)."""
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    shapes = [(4, 32, 8, 4097, 128, 64, 31), (16, 16, 4, 5000, 128, 64, 63),
+              (1, 8, 8, 130, 128, 64, 9)]
+    ws_n = max(L.sas_decode_workspace_size(
+        ops.Shape(b, hq, hkv, Lq, d, bs, L.SAS_DTYPE_BF16), K) for b, hq, hkv, Lq, d, bs, K in shapes)
+    ws = torch.full((ws_n,), 0x7F, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for i, (b, hq, hkv, Lq, d, bs, K) in enumerate(shapes):
+            say(f"workspace reuse rep {rep} shape {(b, hq, hkv, Lq, d, bs, K)}")
+            x, idx, logg = decode_case(100 + i, b, hq, hkv, Lq, d, bs, K, torch.bfloat16)
+            if i == 1:
+                idx = idx.copy()
+                idx[0, 0, 0, -3:] = -1            # pads in the middle of the slot list
+                idx[1, 1, 0, 0] = (Lq - 1) // bs  # an entry that is not history: ignored
+            idx_g = torch.from_numpy(idx[:, :, 0].astype(np.int32)).to(DEV)
+            lg = torch.from_numpy(logg[:, :, 0].astype(np.float32)).to(DEV)
+            o, lse = ops.decode(x["q"].to(DEV), x["kcache"].to(DEV), x["vcache"].to(DEV), Lq,
+                                idx_g, lg, bs, workspace=ws)
+            torch.cuda.synchronize()
+            idx_o = np.where(idx[:, :, 0] >= (Lq - 1) // bs, -1, idx[:, :, 0])  # ignored entries
+            oo, ol = O.decode(x["q"], x["kcache"], x["vcache"], Lq, idx_o, logg[:, :, 0], bs)
+            assert max_abs(o.cpu(), oo) <= 2e-2 and max_abs(lse.cpu(), ol) <= 2e-2
