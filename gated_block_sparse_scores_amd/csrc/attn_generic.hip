@@ -562,9 +562,9 @@ BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base) {
 }
 
 hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, const int32_t* idx,
-                           const BwdWorkspace& ws, hipStream_t st) {
+                           const BwdWorkspace& ws, bool with_d, hipStream_t st) {
   const size_t rows = (size_t)dm.b * dm.hq * dm.n;
-  {
+  if (with_d) {
     ProfScope ps("bwd_dot", st);
     const unsigned grid = (unsigned)((rows + 15) / 16);
     if (dm.bf16 && dm.d == 128)

@@ -243,8 +243,8 @@ constexpr int DQ_NT = 64 * DQ_NW;
 
 __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ Dv,
+    const bf16_t* __restrict__ v, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ Dv,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, bf16_t* __restrict__ dq) {
   // Two K/V tile buffers as four separate arrays (see the forward kernel: the
   // loop is unrolled by two so that copies and transposed reads of different
@@ -296,7 +296,17 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     of[kc] = *reinterpret_cast<const bf16x8*>(dout + row * D + kc * 16 + g * 8);
   }
   const float l2 = lse[row] * LOG2E;
-  const float dval = Dv[row];
+  // D = dO . o for this lane's row: 64 dims per lane half, then the halves;
+  // also stored for the dK / dV kernel, which runs after this one.
+  float dval = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * D + kc * 16 + g * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dval = fmaf((float)of[kc][e], (float)ov[e], dval);
+  }
+  dval += __shfl_xor(dval, 32);
+  if (g == 0) Dv[row] = dval;
   f32x16 dqa[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -380,11 +390,21 @@ bool mfma_bwd_supported(const Dims& dm) {
 }
 
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
-                           const void* dout, const float* lse, const int32_t* idx,
-                           const float* logg, void* dq, void* dk, void* dv,
+                           const void* o, const void* dout, const float* lse,
+                           const int32_t* idx, const float* logg, void* dq, void* dk, void* dv,
                            const BwdWorkspace& ws, int* nchunk_out, hipStream_t st) {
   // dlogg is written whole by the dK/dV kernel (one partial per row).
   *nchunk_out = 1;
+  {
+    // dQ first: it also forms D = rowsum(dO o), which dK / dV reads.
+    const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
+    ProfScope ps("bwd_dq_mfma", st);
+    hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm,
+                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
+                       (const bf16_t*)dout, lse, ws.D, idx, logg, (bf16_t*)dq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
     ProfScope ps("bwd_dkdv_mfma", st);
@@ -392,15 +412,6 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
                        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                        (const bf16_t*)dout, lse, ws.D, logg, ws.slotmap, (bf16_t*)dk,
                        (bf16_t*)dv, ws.dlogg_part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
-    ProfScope ps("bwd_dq_mfma", st);
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                       (const bf16_t*)dout, lse, ws.D, idx, logg, (bf16_t*)dq);
   }
   return hipGetLastError();
 }

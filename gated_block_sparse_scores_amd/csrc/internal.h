@@ -24,11 +24,12 @@ struct Dims {
 // ---- selection (select.hip)
 hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, int group,
                              int n, int d, int bs, bool out_bf16, void* out, hipStream_t st);
-hipError_t launch_standin_scores(const float* qbar, const void* kbar, bool kbar_bf16,
-                                 int kbar_ld, int rows_bk, int T, int C, int row_offset,
-                                 int d, double scale, float* s_out, hipStream_t st);
-hipError_t launch_topk(const float* s, int rows_bk, int T, int C, int row_offset, int K,
-                       int32_t* idx, float* logg, float* lse_s, hipStream_t st);
+// Gate LSE + Top-K per row; with s == NULL the stand-in scores are formed
+// from qbar / kbar first (written to s_out).
+hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
+                       int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
+                       int row_offset, int K, int32_t* idx, float* logg, float* lse_s,
+                       hipStream_t st);
 // Rows with more than kLongHistory history blocks use the two-stage path.
 constexpr int kLongHistory = 512;
 size_t select_workspace_bytes(int rows_bk, int T, int C, int K);
@@ -50,8 +51,10 @@ struct BwdWorkspace {
   size_t bytes;
 };
 BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base);
+// D = rowsum(dO o) (when with_d; the MFMA backward forms it in its dQ kernel)
+// and the slot map.
 hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, const int32_t* idx,
-                           const BwdWorkspace& ws, hipStream_t st);
+                           const BwdWorkspace& ws, bool with_d, hipStream_t st);
 hipError_t launch_bwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
                               const void* dout, const float* lse, const int32_t* idx,
                               const float* logg, void* dq, void* dk, void* dv,

@@ -21,8 +21,8 @@ hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const v
                            hipStream_t st);
 bool mfma_bwd_supported(const Dims& dm);
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
-                           const void* dout, const float* lse, const int32_t* idx,
-                           const float* logg, void* dq, void* dk, void* dv,
+                           const void* o, const void* dout, const float* lse,
+                           const int32_t* idx, const float* logg, void* dq, void* dk, void* dv,
                            const BwdWorkspace& ws, int* nchunk_out, hipStream_t st);
 }  // namespace sas
 
@@ -178,6 +178,7 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
   if (out_dtype != SAS_DTYPE_F32 && out_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
   if (shape->head_dim != 64 && shape->head_dim != 128) return SAS_ERR_UNSUPPORTED;
   if (shape->block > 4096) return SAS_ERR_UNSUPPORTED;
+  if (!aligned16(x)) return SAS_ERR_INVALID_ARG;  // 16-byte vector loads
   return launch_status(sas::launch_block_pool(
       x, shape->dtype == SAS_DTYPE_BF16, shape->batch, heads, group, shape->seqlen,
       shape->head_dim, shape->block, out_dtype == SAS_DTYPE_BF16, out, (hipStream_t)stream));
@@ -218,16 +219,9 @@ sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset,
     return launch_status(sas::launch_select_long(
         s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim, scale, rows_bk, T,
         C, row_offset, K, s_out, idx, logg, lse_s, workspace, st));
-  const float* scores = s;
-  if (!s) {
-    if (C > 0)
-      SAS_LAUNCH(sas::launch_standin_scores(qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
-                                            rows_bk, T, C, row_offset, shape->head_dim, scale,
-                                            s_out, st));
-    scores = s_out;
-  }
-  return launch_status(
-      sas::launch_topk(scores, rows_bk, T, C, row_offset, K, idx, logg, lse_s, st));
+  return launch_status(sas::launch_topk(s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
+                                        shape->head_dim, scale, s_out, rows_bk, T, C,
+                                        row_offset, K, idx, logg, lse_s, st));
 }
 
 size_t sas_attn_fwd_workspace_size(const sas_shape* shape, int K) {
@@ -279,11 +273,12 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
   const sas::BwdWorkspace ws = sas::bwd_workspace_layout(dm, workspace);
   if (!workspace || ws_bytes < ws.bytes) return SAS_ERR_WORKSPACE;
   const hipStream_t st = (hipStream_t)stream;
-  SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, st));
+  const bool mfma = sas::mfma_bwd_supported(dm);
+  SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, !mfma, st));
   int nchunk = 0;
-  if (sas::mfma_bwd_supported(dm))
-    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws, &nchunk,
-                                    st));
+  if (mfma)
+    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, logg, dq, dk, dv, ws,
+                                    &nchunk, st));
   else
     SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws,
                                        &nchunk, st));

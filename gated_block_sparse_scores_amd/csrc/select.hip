@@ -11,35 +11,62 @@
 namespace sas {
 
 // ---------------------------------------------------------------- pooling
-// One workgroup per (t, output head, batch).  256 threads = (256/d) token
-// lanes x d columns; fp64 accumulation, one rounding to fp32 (and optionally
+// One workgroup per (t, output head, batch).  Each lane reads 16 bytes (8 bf16
+// or 4 fp32 values) of a row, LPR = D / 16-byte-chunks lanes cover a row and
+// 256 / LPR rows are read per pass, so every load is a full 16-byte vector
+// load and all of a block's loads are independent.  fp64 accumulation, the
+// per-row-lane sums folded through LDS, one rounding to fp32 (and optionally
 // a second one to bf16).
-template <typename Tin>
+template <typename Tin, int D>
 __global__ void __launch_bounds__(256) pool_kernel(const Tin* __restrict__ x, int heads,
-                                                   int group, int n, int d, int bs,
-                                                   int out_bf16, void* __restrict__ out) {
-  __shared__ double red[256];
+                                                   int group, int n, int bs, int out_bf16,
+                                                   void* __restrict__ out) {
+  constexpr int E = 16 / (int)sizeof(Tin);  // values per 16-byte load
+  constexpr int LPR = D / E;                // lanes per row
+  constexpr int RPP = 256 / LPR;            // rows per pass
+  __shared__ double red[RPP][D];
   const int t = blockIdx.x, ho = blockIdx.y, b = blockIdx.z;
   const int T = gridDim.x, hout = gridDim.y;
   const int lo = t * bs, hi = min(lo + bs, n);
-  const int lanes = blockDim.x / d;
-  const int col = threadIdx.x % d, rl = threadIdx.x / d;
-  double acc = 0.0;
-  if (rl < lanes) {
-    for (int hh = 0; hh < group; ++hh) {
-      const Tin* base = x + ((size_t)b * heads + (size_t)ho * group + hh) * (size_t)n * d;
-      for (int i = lo + rl; i < hi; i += lanes)
-        acc += (double)Elem<Tin>::load(base, (size_t)i * d + col);
+  const int li = threadIdx.x % LPR, ri = threadIdx.x / LPR;
+  double acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0;
+  for (int hh = 0; hh < group; ++hh) {
+    const Tin* base = x + ((size_t)b * heads + (size_t)ho * group + hh) * (size_t)n * D + li * E;
+#pragma unroll 4
+    for (int i = lo + ri; i < hi; i += RPP) {
+      float v[E];
+      if constexpr (sizeof(Tin) == 2) {
+        const uint4 u = *reinterpret_cast<const uint4*>(base + (size_t)i * D);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = __uint_as_float(w[k] << 16);
+          v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(base + (size_t)i * D);
+        v[0] = f.x;
+        v[1] = f.y;
+        v[2] = f.z;
+        v[3] = f.w;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += (double)v[e];
     }
   }
-  red[threadIdx.x] = acc;
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[ri][li * E + e] = acc[e];
   __syncthreads();
-  if (rl == 0) {
-    double s = 0.0;
-    for (int r = 0; r < lanes; ++r) s += red[r * d + col];
-    const double mean = s / (double)((hi - lo) * group);
+  if (threadIdx.x < D) {
+    const int col = threadIdx.x;
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) sum += red[r][col];
+    const double mean = sum / (double)((hi - lo) * group);
     const float f = (float)mean;
-    const size_t o = (((size_t)b * hout + ho) * T + t) * d + col;
+    const size_t o = (((size_t)b * hout + ho) * T + t) * D + col;
     if (out_bf16)
       reinterpret_cast<bf16_t*>(out)[o] = f32_to_bf16(f);
     else
@@ -52,75 +79,98 @@ hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, 
   const int T = (n + bs - 1) / bs;
   dim3 grid(T, heads / group, batch);
   ProfScope ps("block_pool", st);
-  if (in_bf16)
-    hipLaunchKernelGGL(pool_kernel<bf16_t>, grid, dim3(256), 0, st,
-                       (const bf16_t*)x, heads, group, n, d, bs, (int)out_bf16, out);
+#define SAS_POOL(TIN, DD)                                                                 \
+  hipLaunchKernelGGL((pool_kernel<TIN, DD>), grid, dim3(256), 0, st, (const TIN*)x, heads, \
+                     group, n, bs, (int)out_bf16, out)
+  if (in_bf16 && d == 128)
+    SAS_POOL(bf16_t, 128);
+  else if (in_bf16)
+    SAS_POOL(bf16_t, 64);
+  else if (d == 128)
+    SAS_POOL(float, 128);
   else
-    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, st, (const float*)x, heads,
-                       group, n, d, bs, (int)out_bf16, out);
+    SAS_POOL(float, 64);
+#undef SAS_POOL
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- stand-in scores
-// s[r, m] = fp32((qbar[r] . kbar[m]) * scale) with the dot product in fp64.
-// Grid (m-chunks, T, b*hkv); 256 threads = 16 groups of 16 lanes, one key
-// block summary per group, lanes split head_dim.
-constexpr int kScoreChunk = 256;
-
-template <typename Tk>
-__global__ void __launch_bounds__(256) standin_score_kernel(
-    const float* __restrict__ qbar, const Tk* __restrict__ kbar, int kbar_ld, int T, int C,
-    int row_offset, int d, double scale, float* __restrict__ s_out) {
-  __shared__ double qs[128];
-  const int t = blockIdx.y, bk = blockIdx.z;
-  const int ct = min(t + row_offset, C);
-  const int m0 = blockIdx.x * kScoreChunk;
-  const float* qrow = qbar + ((size_t)bk * T + t) * d;
-  for (int e = threadIdx.x; e < d; e += blockDim.x) qs[e] = (double)qrow[e];
-  __syncthreads();
-  const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const Tk* kb = kbar + (size_t)bk * kbar_ld * d;
-  float* srow = s_out + ((size_t)bk * T + t) * C;
-  const int mend = min(m0 + kScoreChunk, C);
-  for (int m = m0 + grp; m < mend; m += 16) {
-    double acc = 0.0;
-    if (m < ct) {
-      for (int e = sub; e < d; e += 16)
-        acc += qs[e] * (double)Elem<Tk>::load(kb, (size_t)m * d + e);
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ double row16_sum_d(double x) {
+  auto step = [](double v, int ctrl) -> double {
+    const long long bits = __double_as_longlong(v);
+    int lo = (int)(bits & 0xFFFFFFFFll), hi = (int)(bits >> 32);
+    switch (ctrl) {
+      case 0:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, true);
+        break;
+      case 1:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, true);
+        break;
+      case 2:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, true);
+        break;
+      default:
+        lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, true);
+        hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, true);
+        break;
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (sub == 0) srow[m] = (m < ct) ? (float)(acc * scale) : 0.0f;
-  }
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+  };
+  x += step(x, 0);
+  x += step(x, 1);
+  x += step(x, 2);
+  x += step(x, 3);
+  return x;
 }
 
-hipError_t launch_standin_scores(const float* qbar, const void* kbar, bool kbar_bf16,
-                                 int kbar_ld, int rows_bk, int T, int C, int row_offset,
-                                 int d, double scale, float* s_out, hipStream_t st) {
-  dim3 grid((C + kScoreChunk - 1) / kScoreChunk, T, rows_bk);
-  ProfScope ps("standin_scores", st);
-  if (kbar_bf16)
-    hipLaunchKernelGGL(standin_score_kernel<bf16_t>, grid, dim3(256), 0, st, qbar,
-                       (const bf16_t*)kbar, kbar_ld, T, C, row_offset, d, scale, s_out);
-  else
-    hipLaunchKernelGGL(standin_score_kernel<float>, grid, dim3(256), 0, st, qbar,
-                       (const float*)kbar, kbar_ld, T, C, row_offset, d, scale, s_out);
-  return hipGetLastError();
+__device__ __forceinline__ float from_order_key(uint32_t k) {
+  const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(b);
 }
+
+// Loads 8 consecutive summary values (one lane's slice) widened to double.
+template <typename Tk> struct Slice8;
+template <> struct Slice8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ double get(int e) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t x = w[e >> 1];
+    return (double)__uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+template <> struct Slice8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ double get(int e) const {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return (double)v[e];
+  }
+};
 
 // ---------------------------------------------------------------- gate LSE + Top-K
-// One 256-thread workgroup per row.  The valid scores are held in LDS as
-// order-preserving uint32 keys.  A 4-pass MSB-first radix select (8 bits per
-// pass) finds the K-th largest key v and how many keys equal to v are still
-// needed; those are taken in ascending block order, which realises the
-// "equal score -> lower block index" rule.  The selection is then compacted in
-// ascending block order with two workgroup scans.
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ s, int T, int C,
-                                                   int row_offset, int K,
-                                                   int32_t* __restrict__ idx,
-                                                   float* __restrict__ logg,
-                                                   float* __restrict__ lse_s) {
-  extern __shared__ uint32_t keys[];
+// One 256-thread workgroup per row.  With STANDIN the row's scores are formed
+// first: s[m] = fp32((qbar . kbar[m]) * scale), the dot product in fp64 with 16
+// lanes per key-block summary (8 consecutive dims each, reduced with DPP),
+// kept in LDS and written to s_out (0 past the row's history).  The valid
+// scores are then held in LDS as order-preserving uint32 keys.  A 4-pass
+// MSB-first radix select (8 bits per pass) finds the K-th largest key v and
+// how many keys equal to v are still needed; those are taken in ascending
+// block order, which realises the "equal score -> lower block index" rule.
+// The selection is then compacted in ascending block order with two
+// workgroup scans.
+template <typename Tk, bool STANDIN>
+__global__ void __launch_bounds__(256) topk_kernel(
+    const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
+    int kbar_ld, int d, double scale, float* __restrict__ s_out, int T, int C, int row_offset,
+    int K, int32_t* __restrict__ idx, float* __restrict__ logg, float* __restrict__ lse_s) {
+  extern __shared__ uint32_t keys[];  // C keys (then, with STANDIN, C scores)
   __shared__ int hist[256];
   __shared__ int iscr[16];
   __shared__ float fscr[16];
@@ -133,6 +183,37 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ s, 
   const int t = (int)(row % T);
   const int ct = min(t + row_offset, C);
   const float* srow = s + row * (size_t)C;
+  if constexpr (STANDIN) {
+    float* sv = reinterpret_cast<float*>(keys + C);
+    const int sub = tid & 15, grp = tid >> 4;
+    const bool lane_on = sub * 8 < d;
+    double qv[8];
+    {
+      const float* qrow = qbar + row * (size_t)d + (lane_on ? sub * 8 : 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = (double)qrow[e];
+    }
+    const Tk* kb = kbar + (row / T) * (size_t)kbar_ld * d + (lane_on ? sub * 8 : 0);
+    float* orow = s_out + row * (size_t)C;
+#pragma unroll 4
+    for (int m = grp; m < C; m += 16) {
+      double acc = 0.0;
+      if (m < ct && lane_on) {
+        Slice8<Tk> ks;
+        ks.load(kb + (size_t)m * d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += qv[e] * ks.get(e);
+      }
+      acc = row16_sum_d(acc);
+      const float v = m < ct ? (float)(acc * scale) : 0.0f;
+      if (sub == 0) {
+        sv[m] = v;
+        orow[m] = v;
+      }
+    }
+    __syncthreads();
+    srow = sv;
+  }
 
   float mx = -INFINITY;
   for (int m = tid; m < ct; m += nth) {
@@ -237,65 +318,6 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ s, 
 // merge-path binary search), combines the chunk statistics into lse_s, and
 // emits the K winners in ascending block order.
 constexpr int kChunk = 256;
-
-__device__ __forceinline__ double row16_sum_d(double x) {
-  auto step = [](double v, int ctrl) -> double {
-    const long long bits = __double_as_longlong(v);
-    int lo = (int)(bits & 0xFFFFFFFFll), hi = (int)(bits >> 32);
-    switch (ctrl) {
-      case 0:
-        lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, true);
-        hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, true);
-        break;
-      case 1:
-        lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, true);
-        hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, true);
-        break;
-      case 2:
-        lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, true);
-        hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, true);
-        break;
-      default:
-        lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, true);
-        hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, true);
-        break;
-    }
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-  };
-  x += step(x, 0);
-  x += step(x, 1);
-  x += step(x, 2);
-  x += step(x, 3);
-  return x;
-}
-
-__device__ __forceinline__ float from_order_key(uint32_t k) {
-  const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(b);
-}
-
-// Loads 8 consecutive summary values (one lane's slice) widened to double.
-template <typename Tk> struct Slice8;
-template <> struct Slice8<bf16_t> {
-  uint4 u;
-  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ double get(int e) const {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    const uint32_t x = w[e >> 1];
-    return (double)__uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
-  }
-};
-template <> struct Slice8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
-  }
-  __device__ __forceinline__ double get(int e) const {
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    return (double)v[e];
-  }
-};
 
 template <typename Tk>
 __global__ void __launch_bounds__(256) select_chunk_kernel(
@@ -491,13 +513,25 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* s, int rows_bk, int T, int C, int row_offset, int K,
-                       int32_t* idx, float* logg, float* lse_s, hipStream_t st) {
+hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
+                       int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
+                       int row_offset, int K, int32_t* idx, float* logg, float* lse_s,
+                       hipStream_t st) {
   const size_t rows = (size_t)rows_bk * T;
-  const size_t lds = (size_t)(C > 0 ? C : 1) * sizeof(uint32_t);
+  const size_t lds = (size_t)(C > 0 ? C : 1) * sizeof(uint32_t) * (s ? 1 : 2);
   ProfScope ps("topk", st);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), lds, st, s, T, C,
-                     row_offset, K, idx, logg, lse_s);
+  if (s)
+    hipLaunchKernelGGL((topk_kernel<float, false>), dim3((unsigned)rows), dim3(256), lds, st, s,
+                       nullptr, nullptr, 0, 0, 0.0, nullptr, T, C, row_offset, K, idx, logg,
+                       lse_s);
+  else if (kbar_bf16)
+    hipLaunchKernelGGL((topk_kernel<bf16_t, true>), dim3((unsigned)rows), dim3(256), lds, st,
+                       nullptr, qbar, (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C,
+                       row_offset, K, idx, logg, lse_s);
+  else
+    hipLaunchKernelGGL((topk_kernel<float, true>), dim3((unsigned)rows), dim3(256), lds, st,
+                       nullptr, qbar, (const float*)kbar, kbar_ld, d, scale, s_out, T, C,
+                       row_offset, K, idx, logg, lse_s);
   return hipGetLastError();
 }
 

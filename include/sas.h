@@ -89,7 +89,7 @@ int sas_version(void);
  * h' of that group and the valid tokens i of block B_t, accumulated in fp64
  * and rounded to fp32 (out_dtype F32) or, for out_dtype BF16, rounded to fp32
  * and then to bf16 (both round-to-nearest-even).
- *   x   : [batch, heads, seqlen, head_dim] in shape->dtype
+ *   x   : [batch, heads, seqlen, head_dim] in shape->dtype, 16-byte aligned
  *   out : [batch, heads / group, ceil(seqlen / block), head_dim] in out_dtype
  * Uses shape->batch, seqlen, head_dim, block, dtype.  heads % group == 0.
  * ---------------------------------------------------------------------- */
