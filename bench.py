@@ -193,7 +193,9 @@ def bench_decode(wl, steps, layers=12):
     caches with their own pooled-key caches, as consecutive layers of a model
     would: 2 GiB of K/V per layer, far more than the last-level cache holds.
     One call = pool the query over its head group, stand-in scores over the
-    pooled-key cache + gate normalisation + Top-K, split-K decode + LSE merge."""
+    pooled-key cache + gate normalisation + Top-K, split-K decode + LSE merge,
+    through the separate calls; the same calls are then timed as fused steps
+    (sas_decode_step), reported under "fused_step"."""
     import torch
     import synth
     from gated_block_sparse_scores_amd import _lib as L
@@ -253,6 +255,38 @@ def bench_decode(wl, steps, layers=12):
     dec_gbs = sel_bytes / ((split_us + merge_us) * 1e-6) / 1e9
     gpu_us = sel_us + split_us + merge_us
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)} for k, v in kt.items()}
+
+    # The same calls as one fused step each (sas_decode_step): chunked scores +
+    # candidates, then the decode (which merges the candidates itself), then
+    # the LSE merge.
+    ws_step = torch.empty(L.sas_decode_step_workspace_size(sh, w.topk), dtype=torch.uint8,
+                          device=dev)
+
+    def one_step(q, layer):
+        kc, vc, kb = caches[layer]
+        return ops.decode_step(q, kb, kc, vc, Lc, w.topk, w.block, with_selection=False,
+                               workspace=ws_step)
+
+    for layer in range(layers):
+        one_step(qs[calls + layer], layer)
+    torch.cuda.synchronize()
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    t0 = time.perf_counter()
+    for c in range(calls):
+        one_step(qs[c], c % layers)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.sas_profiler_enable(False)
+    kt2 = L.sas_profiler_read()
+    step_gpu_us = sum(v[1] / v[0] * 1e3 for v in kt2.values())
+    fused = {
+        "gpu_us_per_call": round(step_gpu_us, 2),
+        "gpu_GBps_per_call": round((sel_bytes + kbar_bytes) / (step_gpu_us * 1e-6) / 1e9, 1),
+        "wall_us_per_call": round((t1 - t0) * 1e6 / calls, 2),
+        "kernels": {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)}
+                    for k, v in kt2.items()},
+    }
     del caches
     torch.cuda.empty_cache()
     return {
@@ -266,6 +300,7 @@ def bench_decode(wl, steps, layers=12):
         "gpu_us_per_call": round(gpu_us, 2),
         "gpu_GBps_per_call": round((sel_bytes + kbar_bytes) / (gpu_us * 1e-6) / 1e9, 1),
         "wall_us_per_call": round(us_step, 2),
+        "fused_step": fused,
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(split_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / PEAK_HBM_GBS, 4),

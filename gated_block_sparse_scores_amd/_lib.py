@@ -23,7 +23,8 @@ EXPORTED = [
     "sas_status_string", "sas_version", "sas_block_pool", "sas_select_topk_workspace_size",
     "sas_select_topk",
     "sas_attn_fwd_workspace_size", "sas_attn_fwd", "sas_attn_bwd_workspace_size",
-    "sas_attn_bwd", "sas_decode_workspace_size", "sas_decode", "sas_profiler_enable",
+    "sas_attn_bwd", "sas_decode_workspace_size", "sas_decode", "sas_decode_step_workspace_size",
+    "sas_decode_step", "sas_profiler_enable",
     "sas_profiler_reset", "sas_profiler_read",
 ]
 
@@ -91,12 +92,16 @@ def lib():
     L.sas_decode_workspace_size.argtypes = [sp, C.c_int]
     L.sas_decode_workspace_size.restype = C.c_size_t
     L.sas_decode.argtypes = [sp, C.c_int, C.c_int, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.sas_decode_step_workspace_size.argtypes = [sp, C.c_int]
+    L.sas_decode_step_workspace_size.restype = C.c_size_t
+    L.sas_decode_step.argtypes = [sp, C.c_int, C.c_int, P, P, C.c_int, C.c_int, P, P, C.c_int,
+                                  P, P, P, P, P, P, C.c_size_t, P]
     L.sas_profiler_enable.argtypes = [C.c_int]
     L.sas_profiler_reset.argtypes = []
     L.sas_profiler_read.argtypes = [C.POINTER(sas_kernel_time), C.c_int]
     L.sas_profiler_read.restype = C.c_int
     for name in ("sas_block_pool", "sas_select_topk", "sas_attn_fwd", "sas_attn_bwd",
-                 "sas_decode"):
+                 "sas_decode", "sas_decode_step"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -195,6 +200,19 @@ def sas_decode(shape: Shape, cache_len: int, K: int, q, kcache, vcache, idx, log
     _check("sas_decode", lib().sas_decode(
         C.byref(shape.c()), cache_len, K, _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(idx),
         _ptr(logg), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sas_decode_step_workspace_size(shape: Shape, K: int) -> int:
+    return lib().sas_decode_step_workspace_size(C.byref(shape.c()), K)
+
+
+def sas_decode_step(shape: Shape, cache_len: int, K: int, q, kbar, kbar_dtype: int, kbar_ld: int,
+                    kcache, vcache, gated: bool, o, lse, idx, logg, lse_s, workspace,
+                    ws_bytes: int, stream=None):
+    _check("sas_decode_step", lib().sas_decode_step(
+        C.byref(shape.c()), cache_len, K, _ptr(q), _ptr(kbar), kbar_dtype, kbar_ld, _ptr(kcache),
+        _ptr(vcache), 1 if gated else 0, _ptr(o), _ptr(lse), _ptr(idx), _ptr(logg), _ptr(lse_s),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sas_profiler_enable(on: bool = True):

@@ -359,11 +359,27 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // workgroup to finish would need a device-scope fence per workgroup, which on
 // this multi-die part writes back the L2 and costs far more than the second
 // launch.)
-template <int G, int kDecWaves>
+// With SEL the block list is not read from idx / logg but formed here from the
+// long-history selection's chunk candidates (SelectChunks): every workgroup of
+// a (b, kv) merges the sorted candidate lists of its row pairwise by merge path
+// (the rule the selection merge kernel uses), orders the K winners by block
+// index and takes the entries it serves; workgroup 0 of each (b, kv) also
+// stores idx, logg and lse_s for the caller.
+struct SelectChunks {
+  const uint64_t* cand;  // [b*hkv][nchunk][K] descending composite keys
+  const float2* stats;   // [b*hkv][nchunk] (max, sum of exp) of the chunk's scores
+  int nchunk, C, gated;
+  int32_t* idx_out;  // optional [b*hkv][K]
+  float* logg_out;   // optional [b*hkv][K]
+  float* lse_out;    // optional [b*hkv]
+};
+
+template <int G, int kDecWaves, bool SEL>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     Dims dm, int L, int cache_len, int nsplit, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const int32_t* __restrict__ idx,
-    const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc) {
+    const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc,
+    SelectChunks sel) {
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
   __shared__ __align__(16) uint32_t Pb[kDecWaves][BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
@@ -381,7 +397,78 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   const int j = split * kDecWaves + wave;
   int m = -1;
   float bias = 0.0f;
-  {
+  if constexpr (SEL) {
+    extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
+    __shared__ int widx[64];
+    __shared__ float wval[64];
+    __shared__ int sidx[64];
+    __shared__ float slg[64];
+    __shared__ float fscr[16];
+    __shared__ double dscr[16];
+    const int K = dm.K, nc = sel.nchunk * K;
+    const int tid = threadIdx.x, nth = 64 * kDecWaves;
+    const uint64_t* crow = sel.cand + (size_t)bk * nc;
+    for (int i = tid; i < nc; i += nth) lists[i] = crow[i];
+    float M = -INFINITY;
+    double S = 0.0;
+    for (int i = tid; i < sel.nchunk; i += nth) M = fmaxf(M, sel.stats[(size_t)bk * sel.nchunk + i].x);
+    M = block_max(M, fscr);  // barriers: lists[] complete afterwards
+    for (int i = tid; i < sel.nchunk; i += nth) {
+      const float2 st = sel.stats[(size_t)bk * sel.nchunk + i];
+      S += st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0;
+    }
+    S = block_sum_d(S, dscr);
+    const float lse_s = sel.C > 0 ? (float)((double)M + log(S)) : -INFINITY;
+    uint64_t* src = lists;
+    uint64_t* dst = lists + nc;
+    int nl = sel.nchunk;
+    while (nl > 1) {
+      const int np = nl >> 1;
+      for (int job = tid; job < np * K; job += nth) {
+        const int pr = job / K, jj = job % K;
+        dst[pr * K + jj] = merge_path_kth(src + (2 * pr) * K, src + (2 * pr + 1) * K, K, jj);
+      }
+      if (nl & 1)
+        for (int jj = tid; jj < K; jj += nth) dst[np * K + jj] = src[(nl - 1) * K + jj];
+      __syncthreads();
+      uint64_t* tmp = src;
+      src = dst;
+      dst = tmp;
+      nl = np + (nl & 1);
+    }
+    const int kk = min(K, sel.C);
+    if (tid < kk) {
+      const uint64_t key = src[tid];
+      widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+      wval[tid] = from_order_key((uint32_t)(key >> 32));
+    }
+    __syncthreads();
+    if (tid < kk) {
+      const int mine = widx[tid];
+      int rank = 0;
+      for (int q2 = 0; q2 < kk; ++q2) rank += widx[q2] < mine;
+      sidx[rank] = mine;
+      slg[rank] = wval[tid] - lse_s;
+      if (split == 0 && sel.idx_out) {
+        sel.idx_out[(size_t)bk * K + rank] = mine;
+        sel.logg_out[(size_t)bk * K + rank] = wval[tid] - lse_s;
+      }
+    }
+    if (split == 0 && sel.idx_out) {
+      for (int p2 = kk + tid; p2 < K; p2 += nth) {
+        sel.idx_out[(size_t)bk * K + p2] = -1;
+        sel.logg_out[(size_t)bk * K + p2] = 0.0f;
+      }
+      if (tid == 0) sel.lse_out[bk] = lse_s;
+    }
+    __syncthreads();
+    if (j < kk) {
+      m = sidx[j];
+      bias = sel.gated ? slg[j] : 0.0f;
+    } else if (j == kk) {
+      m = c;
+    }
+  } else {
     const int mm = lane < dm.K ? idx[(size_t)bk * dm.K + lane] : -1;
     const bool ok = mm >= 0 && mm < c;
     const unsigned long long bal = __ballot(ok);
@@ -545,19 +632,21 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 }
 
-template <int G>
+template <int G, bool SEL>
 void launch_decode_block4(const Dims& dm, int L, int cache_len, int nsplit, int waves,
                           const void* q, const void* kc, const void* vc, const int32_t* idx,
-                          const float* logg, float* part_ml, float* part_acc, hipStream_t st) {
+                          const float* logg, float* part_ml, float* part_acc,
+                          const SelectChunks& sel, hipStream_t st) {
   const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
+  const size_t lds = SEL ? (size_t)2 * sel.nchunk * dm.K * sizeof(uint64_t) : 0;
   if (waves == 4)
-    hipLaunchKernelGGL((decode_block4_kernel<G, 4>), dim3((unsigned)wgs), dim3(256), 0, st, dm,
-                       L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
-                       (const bf16_t*)vc, idx, logg, part_ml, part_acc);
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL>), dim3((unsigned)wgs), dim3(256), lds, st,
+                       dm, L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
+                       (const bf16_t*)vc, idx, logg, part_ml, part_acc, sel);
   else
-    hipLaunchKernelGGL((decode_block4_kernel<G, 1>), dim3((unsigned)wgs), dim3(64), 0, st, dm,
-                       L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
-                       (const bf16_t*)vc, idx, logg, part_ml, part_acc);
+    hipLaunchKernelGGL((decode_block4_kernel<G, 1, SEL>), dim3((unsigned)wgs), dim3(64), lds, st,
+                       dm, L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
+                       (const bf16_t*)vc, idx, logg, part_ml, part_acc, sel);
 }
 
 // Workspace: [partials (max, sum) per (b, h, split)][partial outputs per
@@ -575,8 +664,8 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
     if constexpr (std::is_same<T, bf16_t>::value && D == 128 && BS == 64) {
 #define SAS_DEC_G(G_)                                                                     \
   case G_:                                                                                \
-    launch_decode_block4<G_>(dm, L, cache_len, nsplit, bps, q, kc, vc, idx, logg, part_ml, \
-                             part_acc, st);                                               \
+    launch_decode_block4<G_, false>(dm, L, cache_len, nsplit, bps, q, kc, vc, idx, logg,  \
+                                    part_ml, part_acc, SelectChunks{}, st);               \
     break;
       switch (dm.g) {
         SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4)
@@ -630,6 +719,41 @@ hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, co
   SAS_DEC(bf16_t, 128, 16) SAS_DEC(bf16_t, 128, 32) SAS_DEC(bf16_t, 128, 64)
 #undef SAS_DEC
   return hipErrorInvalidValue;
+}
+
+size_t decode_step_partial_bytes(const Dims& dm) { return decode_workspace_bytes(dm); }
+
+hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int nchunk,
+                              const void* q, const void* kc, const void* vc,
+                              const uint64_t* cand, const float2* stats, bool gated,
+                              int32_t* idx_out, float* logg_out, float* lse_s_out, void* o,
+                              float* lse, void* ws, hipStream_t st) {
+  if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
+  const int bps = decode_blocks_per_split(dm);
+  const int nsplit = (dm.K + 1 + bps - 1) / bps;
+  float* part_ml = (float*)ws;
+  float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
+  const SelectChunks sel{cand, stats, nchunk, C, gated ? 1 : 0, idx_out, logg_out, lse_s_out};
+  {
+    ProfScope ps("step_decode_split", st);
+#define SAS_DEC_G(G_)                                                                          \
+  case G_:                                                                                     \
+    launch_decode_block4<G_, true>(dm, L, cache_len, nsplit, bps, q, kc, vc, nullptr, nullptr, \
+                                   part_ml, part_acc, sel, st);                                \
+    break;
+    switch (dm.g) {
+      SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4)
+      SAS_DEC_G(5) SAS_DEC_G(6) SAS_DEC_G(7) SAS_DEC_G(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef SAS_DEC_G
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("step_decode_merge", st);
+  hipLaunchKernelGGL((decode_merge_kernel<bf16_t>), dim3((unsigned)(dm.b * dm.hq)), dim3(64), 0,
+                     st, nsplit, 128, part_ml, part_acc, (bf16_t*)o, lse);
+  return hipGetLastError();
 }
 
 }  // namespace sas

@@ -67,6 +67,20 @@ int bwd_dlogg_chunks(const Dims& dm);
 // ---- decode (decode.hip)
 int decode_blocks_per_split(const Dims& dm);
 size_t decode_workspace_bytes(const Dims& dm);
+// Fused decode step (bf16, d 128, block 64): chunk selection over the pooled-key
+// cache with the query pooled in-kernel, then the decode kernel merging the
+// chunk candidates itself, then the LSE merge.
+constexpr int kSelectChunk = 256;  // history blocks per selection chunk
+hipError_t launch_select_chunks_rawq(const uint16_t* q, int qgroup, const void* kbar,
+                                     bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
+                                     int C, int K, uint64_t* cand, float2* stats,
+                                     hipStream_t st);
+bool decode_mfma_path(const Dims& dm);
+hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int nchunk,
+                              const void* q, const void* kc, const void* vc,
+                              const uint64_t* cand, const float2* stats, bool gated,
+                              int32_t* idx_out, float* logg_out, float* lse_s_out, void* o,
+                              float* lse, void* ws, hipStream_t st);
 hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
                          const void* vc, const int32_t* idx, const float* logg, void* o,
                          float* lse, void* ws, hipStream_t st);

@@ -313,6 +313,115 @@ sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* 
                                           workspace, (hipStream_t)stream));
 }
 
+// ---- fused decode step
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct StepLayout {
+  bool fused;
+  int C, nchunk;
+  size_t cand, stats, part;            // fused: offsets of the three regions
+  size_t qbar, idx, logg, lse_s, sel;  // composed: pooled q, selection outputs, select workspace
+  size_t dec;                          // decode partials
+  size_t bytes;
+};
+
+StepLayout step_layout(const sas_shape* shape, int K) {
+  StepLayout l{};
+  const Dims dm = make_dims(shape, K);
+  const size_t rows = (size_t)shape->batch * shape->hkv;
+  l.C = (shape->seqlen - 1) / shape->block;
+  l.nchunk = (l.C + sas::kSelectChunk - 1) / sas::kSelectChunk;
+  l.fused = sas::decode_mfma_path(dm) && (size_t)l.nchunk * K <= 2048;
+  if (l.fused) {
+    l.cand = 0;
+    l.stats = align256(rows * l.nchunk * K * sizeof(uint64_t));
+    l.part = l.stats + align256(rows * l.nchunk * sizeof(float2));
+    l.bytes = l.part + align256(sas::decode_workspace_bytes(dm));
+  } else {
+    l.qbar = 0;
+    l.idx = align256(rows * shape->head_dim * sizeof(float));
+    l.logg = l.idx + align256(rows * K * sizeof(int32_t));
+    l.lse_s = l.logg + align256(rows * K * sizeof(float));
+    l.sel = l.lse_s + align256(rows * sizeof(float));
+    // scores (s_out) first, then the long-history candidates
+    const size_t s_bytes = align256(rows * (size_t)(l.C > 0 ? l.C : 1) * sizeof(float));
+    l.dec = l.sel + s_bytes + align256(sas::select_workspace_bytes((int)rows, 1, l.C, K));
+    l.bytes = l.dec + align256(sas::decode_workspace_bytes(dm));
+  }
+  return l;
+}
+
+}  // namespace
+
+size_t sas_decode_step_workspace_size(const sas_shape* shape, int K) {
+  if (check_shape(shape) != SAS_OK || K <= 0 || K > 64) return 0;
+  return step_layout(shape, K).bytes;
+}
+
+sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const void* q,
+                           const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                           const void* kcache, const void* vcache, int gated, void* o,
+                           float* lse, int32_t* idx, float* logg, float* lse_s,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0 || cache_len < 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  const int L = shape->seqlen;
+  const int cl = cache_len == 0 ? L : cache_len;
+  if (cl < L) return SAS_ERR_INVALID_ARG;
+  if (!q || !kbar || !kcache || !vcache || !o || !lse) return SAS_ERR_INVALID_ARG;
+  if ((idx == nullptr) != (logg == nullptr) || (idx == nullptr) != (lse_s == nullptr))
+    return SAS_ERR_INVALID_ARG;
+  if (kbar_dtype != SAS_DTYPE_F32 && kbar_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kbar) || !aligned16(kcache) || !aligned16(vcache) ||
+      !aligned16(o))
+    return SAS_ERR_INVALID_ARG;
+  if (shape->hq / shape->hkv > 8) return SAS_ERR_UNSUPPORTED;
+  const StepLayout lay = step_layout(shape, K);
+  if (kbar_ld < lay.C) return SAS_ERR_INVALID_ARG;
+  if (lay.C > 16384) return SAS_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < lay.bytes) return SAS_ERR_WORKSPACE;
+  const Dims dm = make_dims(shape, K);
+  const hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const double scale =
+      shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
+  const int rows = shape->batch * shape->hkv;
+  const int G = shape->hq / shape->hkv;
+  if (lay.fused) {
+    uint64_t* cand = (uint64_t*)(ws + lay.cand);
+    float2* stats = (float2*)(ws + lay.stats);
+    SAS_LAUNCH(sas::launch_select_chunks_rawq((const uint16_t*)q, G, kbar,
+                                              kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
+                                              shape->head_dim, scale, rows, lay.C, K, cand, stats,
+                                              st));
+    return launch_status(sas::launch_decode_step(dm, L, cl, lay.C, lay.nchunk, q, kcache,
+                                                 vcache, cand, stats, gated != 0, idx, logg,
+                                                 lse_s, o, lse, ws + lay.part, st));
+  }
+  // Every other shape: the same three stages through the separate calls' kernels.
+  float* qbar = (float*)(ws + lay.qbar);
+  int32_t* idx_w = idx ? idx : (int32_t*)(ws + lay.idx);
+  float* logg_w = logg ? logg : (float*)(ws + lay.logg);
+  float* lse_s_w = lse_s ? lse_s : (float*)(ws + lay.lse_s);
+  float* s_out = (float*)(ws + lay.sel);
+  const size_t s_bytes = align256((size_t)rows * (lay.C > 0 ? lay.C : 1) * sizeof(float));
+  SAS_LAUNCH(sas::launch_block_pool(q, shape->dtype == SAS_DTYPE_BF16, shape->batch, shape->hq,
+                                    G, 1, shape->head_dim, shape->block, false, qbar, st));
+  if (lay.C > sas::kLongHistory)
+    SAS_LAUNCH(sas::launch_select_long(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
+                                       shape->head_dim, scale, rows, 1, lay.C, lay.C, K, s_out,
+                                       idx_w, logg_w, lse_s_w, ws + lay.sel + s_bytes, st));
+  else
+    SAS_LAUNCH(sas::launch_topk(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
+                                shape->head_dim, scale, s_out, rows, 1, lay.C, lay.C, K, idx_w,
+                                logg_w, lse_s_w, st));
+  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx_w,
+                                          gated ? logg_w : nullptr, o, lse, ws + lay.dec, st));
+}
+
 void sas_profiler_enable(int on) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);

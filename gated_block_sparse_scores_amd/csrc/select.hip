@@ -126,11 +126,6 @@ __device__ __forceinline__ double row16_sum_d(double x) {
   return x;
 }
 
-__device__ __forceinline__ float from_order_key(uint32_t k) {
-  const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(b);
-}
-
 // Loads 8 consecutive summary values (one lane's slice) widened to double.
 template <typename Tk> struct Slice8;
 template <> struct Slice8<bf16_t> {
@@ -321,9 +316,10 @@ constexpr int kChunk = 256;
 
 template <typename Tk>
 __global__ void __launch_bounds__(256) select_chunk_kernel(
-    const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
-    int kbar_ld, int d, double scale, int T, int C, int row_offset, int K, int nchunk,
-    float* __restrict__ s_out, uint64_t* __restrict__ cand, float2* __restrict__ stats) {
+    const float* __restrict__ s, const float* __restrict__ qbar, const bf16_t* __restrict__ qraw,
+    int qgroup, const Tk* __restrict__ kbar, int kbar_ld, int d, double scale, int T, int C,
+    int row_offset, int K, int nchunk, float* __restrict__ s_out, uint64_t* __restrict__ cand,
+    float2* __restrict__ stats) {
   __shared__ uint64_t keys[kChunk];
   __shared__ float sval[kChunk];
   __shared__ float fscr[16];
@@ -344,11 +340,31 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   } else {
     // 16 groups of 16 lanes; group grp scores blocks m0 + grp + 16 i.
     const int sub = tid & 15, grp = tid >> 4;
-    const float* qr = qbar + row * (size_t)d;
     const int nsl = d / 8;  // lanes carrying 8 dims each (16 for d = 128, 8 for d = 64)
     double qd[8];
+    if (qraw) {
+      // decode (T = 1): the pooled query is the mean of the qgroup heads of this
+      // KV head, formed here exactly as the pooling kernel forms it (the sum of
+      // bf16 values in fp64 is exact), rounded once to fp32
+      const bf16_t* qh = qraw + row * (size_t)qgroup * d + (sub < nsl ? sub * 8 : 0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qd[e] = sub < nsl ? (double)qr[sub * 8 + e] : 0.0;
+      for (int e = 0; e < 8; ++e) qd[e] = 0.0;
+      for (int h = 0; h < qgroup; ++h) {
+        const uint4 u = *reinterpret_cast<const uint4*>(qh + (size_t)h * d);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          qd[2 * k] += (double)__uint_as_float(w[k] << 16);
+          qd[2 * k + 1] += (double)__uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qd[e] = sub < nsl ? (double)(float)(qd[e] / qgroup) : 0.0;
+    } else {
+      const float* qr = qbar + row * (size_t)d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qd[e] = sub < nsl ? (double)qr[sub * 8 + e] : 0.0;
+    }
     Slice8<Tk> sl[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -368,7 +384,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     }
     __syncthreads();
     f = sval[tid];
-    if (m < C) s_out[row * C + m] = valid ? f : 0.0f;
+    if (s_out && m < C) s_out[row * C + m] = valid ? f : 0.0f;
   }
   // Invalid entries get keys below every valid one (high word 0), still distinct.
   const uint64_t mykey = ((valid ? (uint64_t)order_key(f) : 0ull) << 32) |
@@ -382,28 +398,6 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   const size_t cbase = (row * nchunk + chunk) * (size_t)K;
   if (rank < K) cand[cbase + rank] = mykey;
   if (tid == 0) stats[row * nchunk + chunk] = make_float2(mx, (float)se);
-}
-
-// Top K of two descending lists of exactly K distinct keys, by merge path:
-// output j is found by binary search for how many of the first j + 1 come from A.
-__device__ __forceinline__ uint64_t merge_path_kth(const uint64_t* A, const uint64_t* B, int K,
-                                                  int j) {
-  const int d = j + 1;
-  int lo = d > K ? d - K : 0, hi = d < K ? d : K;
-  // smallest a in [lo, hi] such that taking a from A is not too few:
-  // too few <=> a < K and d - a > 0 and A[a] > B[d - a - 1]
-  while (lo < hi) {
-    const int a = (lo + hi) >> 1;
-    if (A[a] > B[d - a - 1])
-      lo = a + 1;
-    else
-      hi = a;
-  }
-  const int a = lo, b = d - lo;
-  if (a == 0) return B[b - 1];
-  if (b == 0) return A[a - 1];
-  const uint64_t x = A[a - 1], y = B[b - 1];
-  return x < y ? x : y;
 }
 
 __global__ void __launch_bounds__(256) select_merge_kernel(
@@ -495,12 +489,12 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
     dim3 grid(nchunk, (unsigned)rows);
     if (kbar_bf16)
       hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, s, qbar,
-                         (const bf16_t*)kbar, kbar_ld, d, scale, T, C, row_offset, K, nchunk,
-                         s_out, cand, stats);
+                         (const bf16_t*)nullptr, 0, (const bf16_t*)kbar, kbar_ld, d, scale, T, C,
+                         row_offset, K, nchunk, s_out, cand, stats);
     else
       hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, s, qbar,
-                         (const float*)kbar, kbar_ld, d, scale, T, C, row_offset, K, nchunk,
-                         s_out, cand, stats);
+                         (const bf16_t*)nullptr, 0, (const float*)kbar, kbar_ld, d, scale, T, C,
+                         row_offset, K, nchunk, s_out, cand, stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -510,6 +504,25 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
                        (size_t)2 * nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
                        K, nchunk, idx, logg, lse_s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kbar,
+                                     bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
+                                     int C, int K, uint64_t* cand, float2* stats,
+                                     hipStream_t st) {
+  const int nchunk = (C + kChunk - 1) / kChunk;
+  if (nchunk == 0) return hipSuccess;
+  ProfScope ps("step_select_chunk", st);
+  dim3 grid(nchunk, (unsigned)rows);
+  if (kbar_bf16)
+    hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, (const float*)nullptr,
+                       (const float*)nullptr, q, qgroup, (const bf16_t*)kbar, kbar_ld, d, scale,
+                       1, C, C, K, nchunk, (float*)nullptr, cand, stats);
+  else
+    hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, (const float*)nullptr,
+                       (const float*)nullptr, q, qgroup, (const float*)kbar, kbar_ld, d, scale, 1,
+                       C, C, K, nchunk, (float*)nullptr, cand, stats);
   return hipGetLastError();
 }
 

@@ -114,3 +114,26 @@ def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0
     L.sas_decode(sh, kcache.shape[2], K, q, kcache, vcache, idx, logg, o, lse, workspace, ws_n,
                  stream)
     return o, lse
+
+
+def decode_step(q, kbar, kcache, vcache, L_: int, K: int, block: int, gated: bool = True,
+                scale: float = 0.0, with_selection: bool = True, stream=None,
+                workspace: Optional[torch.Tensor] = None):
+    """One fused decode step with the stand-in selector: q [b,hq,d]; kbar the
+    pooled-key cache [b,hkv,>=C,d]; caches [b,hkv,cache_len,d].  Returns
+    (o, lse) or, with with_selection, (o, lse, idx, logg, lse_s)."""
+    sh = shape_of(q, kcache, block, scale, seqlen=L_)
+    b, hkv = kcache.shape[0], kcache.shape[1]
+    o = torch.empty_like(q)
+    lse = _f32(q.shape[:2], q.device)
+    idx = logg = lse_s = None
+    if with_selection:
+        idx = _i32((b, hkv, K), q.device)
+        logg = _f32((b, hkv, K), q.device)
+        lse_s = _f32((b, hkv), q.device)
+    ws_n = L.sas_decode_step_workspace_size(sh, K)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_decode_step(sh, kcache.shape[2], K, q, kbar, L.dtype_code(kbar.dtype), kbar.shape[2],
+                      kcache, vcache, gated, o, lse, idx, logg, lse_s, workspace, ws_n, stream)
+    return (o, lse, idx, logg, lse_s) if with_selection else (o, lse)

@@ -189,6 +189,35 @@ sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* 
                       size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * One decode step with the stand-in selector, fused (picx 'Decode Efficiency'
+ * (Figure 7): at long contexts the block selection dominates the decode step).
+ * Computes what sas_block_pool (q over the G heads of each KV head, one token)
+ * + sas_select_topk (T = 1, C = row_offset = (L - 1) / block, scores from the
+ * pooled query and kbar) + sas_decode produce, with the same rounding and the
+ * same results, in three kernels for bf16 / head_dim 128 / block 64 (the
+ * chunked scores + Top-K candidates, then the decode, which merges the
+ * candidates itself, then the LSE merge), and through those calls' kernels for
+ * every other supported shape.
+ *   q      [b, hq, d] (shape->dtype); L = shape->seqlen (the new token at L - 1)
+ *   kbar   pooled-key cache [b, hkv, kbar_ld, d] in kbar_dtype (block means of
+ *          kcache, e.g. from sas_block_pool), kbar_ld >= C
+ *   kcache, vcache, cache_len: as for sas_decode
+ *   gated  1: the selected blocks carry their log gates (Eq. 9); 0: ungated
+ *          (Eq. 2), the selection unchanged
+ *   o, lse as for sas_decode
+ *   idx, logg, lse_s: optional ([b,hkv,K] int32, [b,hkv,K] fp32, [b,hkv] fp32;
+ *          all three or none), the selection as sas_select_topk returns it
+ * Needs C <= 16384.  The workspace holds the selection candidates and the
+ * decode partials (no initial contents needed).
+ * ---------------------------------------------------------------------- */
+size_t sas_decode_step_workspace_size(const sas_shape* shape, int K);
+sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const void* q,
+                           const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                           const void* kcache, const void* vcache, int gated, void* o,
+                           float* lse, int32_t* idx, float* logg, float* lse_s,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (not part of the method).  When enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same
  * stream; sas_profiler_read synchronises those events and returns, per kernel

@@ -144,3 +144,29 @@ def test_profiler_is_inert_when_off():
     L.sas_profiler_enable(False)
     L.sas_profiler_reset()
     assert L.sas_profiler_read() == {}
+
+
+def test_decode_step_checks():
+    sh = shape(seqlen=4097, hq=32, hkv=8)   # C = 64
+    lib = L.lib()
+    need = lib.sas_decode_step_workspace_size(C.byref(sh), 31)
+    assert need > 0 and lib.sas_decode_step_workspace_size(C.byref(sh), 65) == 0
+
+    def call(sh_=sh, K=31, kbar_ld=64, idx=FAKE, logg=FAKE, lse_s=FAKE, kdt=L.SAS_DTYPE_BF16,
+             ws=FAKE, n=need, cl=0, q=FAKE):
+        return lib.sas_decode_step(C.byref(sh_), cl, K, q, FAKE, kdt, kbar_ld, FAKE, FAKE, 1,
+                                   FAKE, FAKE, idx, logg, lse_s, ws, n, None)
+
+    assert call(idx=None) == L.SAS_ERR_INVALID_ARG              # idx/logg/lse_s: all or none
+    assert call(lse_s=None) == L.SAS_ERR_INVALID_ARG
+    assert call(kbar_ld=63) == L.SAS_ERR_INVALID_ARG            # kbar rows < C
+    assert call(kdt=7) == L.SAS_ERR_INVALID_ARG
+    assert call(q=FAKE + 8) == L.SAS_ERR_INVALID_ARG            # 16-byte alignment
+    assert call(cl=4096) == L.SAS_ERR_INVALID_ARG               # cache shorter than L
+    assert call(K=0) == L.SAS_ERR_INVALID_ARG
+    assert call(K=65) == L.SAS_ERR_UNSUPPORTED
+    assert call(ws=None) == L.SAS_ERR_WORKSPACE
+    assert call(n=need - 1) == L.SAS_ERR_WORKSPACE
+    assert call(shape(seqlen=4097, hq=36, hkv=4)) == L.SAS_ERR_UNSUPPORTED   # G = 9
+    big = shape(seqlen=64 * 16385 + 1, hq=4, hkv=1)                          # C = 16385
+    assert call(big, kbar_ld=16385, n=1 << 40) == L.SAS_ERR_UNSUPPORTED

@@ -158,12 +158,20 @@ def test_training_workload_sampled(wl):
     say(f"training workload {wl}")
     w, x, r = run_workload(wl)
     T = w.nblocks
-    s = r["s"].cpu()
-    s_np = s.numpy()
+    xc = {k_: x[k_].cpu() for k_ in ("q", "k", "v", "dout")}
+    if w.scores == "standin":
+        # the oracle's own stand-in scores from the inputs; the device's agree
+        # with them except where the fp64 dot lands on an fp32 rounding boundary
+        qo = O.to_f32(O.pool_queries(xc["q"], w.hkv, w.block))
+        ko = O.to_f32(O.pool_keys(xc["k"], w.block))
+        s_np = O.standin_scores(qo, ko, O.default_scale(w.head_dim), T)
+        valid = np.tril(np.ones((T, T), dtype=bool), -1)
+        assert np.sum((r["s"].cpu().numpy() != s_np) & valid) <= 2
+    else:
+        s_np = x["s"].cpu().numpy()
     oi, ol, ols = O.select_topk(s_np, w.topk)
     np.testing.assert_array_equal(r["idx"].cpu().numpy(), oi)
     assert max_abs(r["logg"].cpu().numpy(), ol) <= GATE_ATOL
-    xc = {k_: x[k_].cpu() for k_ in ("q", "k", "v", "dout")}
     scale = O.default_scale(w.head_dim)
     rng = np.random.default_rng(wl)
     tsamp = sorted({0, 1, T // 2, T - 1, *rng.integers(0, T, 3).tolist()})

@@ -97,26 +97,36 @@ def test_decode_equals_forward_last_row():
 
 @pytest.mark.parametrize("wl", [4, 5])
 def test_decode_workload_full(wl):
-    """8 x 64K (32/8 heads, K 63) and 1 x 512K (40/8 heads, K 31), bf16 caches:
-    every output against the oracle, with and without gates."""
+    """8 x 64K (32/8 heads, K 63) and 1 x 512K (40/8 heads, K 31), bf16 caches.
+    The selection is the oracle's (stand-in scores from the oracle's pooled query
+    and pooled keys); the device selection from the same pooled keys must match
+    it bit for bit, and the device decode under it must match the oracle's, with
+    and without gates."""
     from gated_block_sparse_scores_amd import ops
     w = synth.workload(wl)
     say(f"decode workload {wl}")
-    x = synth.decode_inputs(w, device=DEV)
+    x = synth.decode_inputs(w)
     L = w.seqlen
     C = (L - 1) // w.block
-    kb = ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16)
-    qb = ops.block_pool(x["q"].unsqueeze(2), w.block, w.group)
-    idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, 1, C, w.topk, row_offset=C, qbar=qb,
-                                          kbar=kb)
-    idx2, logg2 = idx[:, :, 0].contiguous(), logg[:, :, 0].contiguous()
-    xc = {k_: v_.cpu() for k_, v_ in x.items()}
+    kbar = torch.from_numpy(O.to_f32(O.pool_keys(x["kcache"][:, :, :C * w.block], w.block)))
+    kbar = kbar.to(torch.bfloat16)
+    qbar32 = O.to_f32(O.decode_qbar(x["q"], w.hkv))
+    s = O.standin_scores(qbar32, kbar.float().numpy(), O.default_scale(w.head_dim), C,
+                         row_offset=C)
+    ridx, rlogg, _ = O.select_topk(s, w.topk, row_offset=C, C=C)
+    xd = {k_: v_.to(DEV) for k_, v_ in x.items()}
+    qb = ops.block_pool(xd["q"].unsqueeze(2), w.block, w.group)
+    idx, _, _, _ = ops.select_topk(w.batch, w.hkv, 1, C, w.topk, row_offset=C, qbar=qb,
+                                   kbar=kbar.to(DEV))
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), ridx)
+    idx_g = torch.from_numpy(ridx[:, :, 0].astype(np.int32)).to(DEV)
+    logg_g = torch.from_numpy(rlogg[:, :, 0].astype(np.float32)).to(DEV)
     for gated in (True, False):
-        o, lse = ops.decode(x["q"], x["kcache"], x["vcache"], L, idx2, logg2 if gated else None,
-                            w.block)
+        o, lse = ops.decode(xd["q"], xd["kcache"], xd["vcache"], L, idx_g,
+                            logg_g if gated else None, w.block)
         torch.cuda.synchronize()
-        oo, ol = O.decode(xc["q"], xc["kcache"], xc["vcache"], L, idx2.cpu(),
-                          logg2.cpu() if gated else None, w.block)
+        oo, ol = O.decode(x["q"], x["kcache"], x["vcache"], L, ridx[:, :, 0],
+                          rlogg[:, :, 0] if gated else None, w.block)
         eo, el = max_abs(o.cpu(), oo), max_abs(lse.cpu(), ol)
         say(f"  gated={gated}: o {eo:.2e} lse {el:.2e}")
         assert eo <= 2e-2 and el <= 2e-2
