@@ -29,7 +29,9 @@ Per row r = (batch b, KV head kv, query block t), with valid history length C_t:
      ([daiwk] 'Core equations'; [picx] Eq. 9);
   6. gradients of L = sum dO . o: dq, dk, dv, d(log g) summed per selected block
      ([picx] Eq. 5, inner gating), and ds through the gate softmax of step 2;
-  7. decode: the same for a single query token at position L - 1.
+  7. decode: the same for a single query token at position L - 1;
+  8. the selector's own backward for the stand-in scores: ds to the pooled
+     summaries (dqbar, dkbar), and through the mean pools to dq and dk.
 
 Readings taken where the pages leave a step open: the gate softmax runs over
 all C_t history blocks of the row (not only the selected ones); the 1/sqrt(d)
@@ -471,6 +473,57 @@ def decode_qbar(q, hkv: int) -> np.ndarray:
     b, hq, d = q.shape
     g = hq // hkv
     return q.reshape(b, hkv, g, d).mean(axis=2)[:, :, None, :]
+
+
+# --------------------------------------------------------------------------- (8) selector backward
+
+def selector_bwd(ds, qbar, kbar, scale: float, row_offset: int = 0):
+    """Gradient of the stand-in scores s[t, m] = scale * qbar[t] . kbar[m] (m < C_t)
+    with respect to the pooled summaries, given ds = dL/ds:
+        dqbar[t] = scale * sum_{m < C_t} ds[t, m] kbar[m]
+        dkbar[m] = scale * sum_{t : m < C_t} ds[t, m] qbar[t]
+    Entries of ds with m >= C_t are not part of s and are not read.
+    ds [b,kv,T,C], qbar [b,kv,T,d], kbar [b,kv,>=C,d] -> dqbar [b,kv,T,d],
+    dkbar [b,kv,C,d] (float64).  The selector is trained through the gates, the
+    hard Top-K carrying no gradient ([picx] 'Theoretical Foundation' and 'Key
+    Idea'; [evolve] FAQ for the pooled block summaries)."""
+    ds = _np64(ds)
+    qb = _np64(qbar)
+    b, hkv, T, C = ds.shape
+    kb = _np64(kbar)[:, :, :C]
+    mask = np.zeros((T, C))
+    for t in range(T):
+        mask[t, :history_len(t, row_offset, C)] = 1.0
+    dsm = ds * mask
+    dqbar = scale * (dsm @ kb)
+    dkbar = scale * (np.swapaxes(dsm, 2, 3) @ qb)
+    return dqbar, dkbar
+
+
+def pool_queries_bwd(dqbar, hq: int, n: int, bs: int) -> np.ndarray:
+    """Adjoint of pool_queries: every query row i of block t and head h of group
+    kv receives dqbar[kv, t] / (G * n_t), n_t the block's valid token count."""
+    dqbar = _np64(dqbar)
+    b, hkv, T, d = dqbar.shape
+    g = hq // hkv
+    dq = np.zeros((b, hq, n, d))
+    for t in range(T):
+        lo, hi = block_span(t, bs, n)
+        share = dqbar[:, :, t] / (g * (hi - lo))          # [b, kv, d]
+        for h in range(hq):
+            dq[:, h, lo:hi] = share[:, h // g, None, :]
+    return dq
+
+
+def pool_keys_bwd(dkbar, n: int, bs: int) -> np.ndarray:
+    """Adjoint of pool_keys: every key row j of block m receives dkbar[m] / n_m."""
+    dkbar = _np64(dkbar)
+    b, hkv, C, d = dkbar.shape
+    dk = np.zeros((b, hkv, n, d))
+    for m in range(C):
+        lo, hi = block_span(m, bs, n)
+        dk[:, :, lo:hi] = dkbar[:, :, m, None, :] / (hi - lo)
+    return dk
 
 
 # --------------------------------------------------------------------------- work counts

@@ -55,6 +55,33 @@ def _bwd_row_dk_unscaled(*a, **k):
     return dq, dl, (J, dkj / a[7], dvj)
 
 
+_orig_selector_bwd = O.selector_bwd
+_orig_pool_q_bwd = O.pool_queries_bwd
+
+
+def _selector_bwd_no_scale(ds, qbar, kbar, scale, row_offset=0):
+    return _orig_selector_bwd(ds, qbar, kbar, 1.0, row_offset)
+
+
+def _selector_bwd_no_mask(ds, qbar, kbar, scale, row_offset=0):
+    ds = O._np64(ds)
+    return _orig_selector_bwd(ds, qbar, kbar, scale, row_offset=ds.shape[3])
+
+
+def _selector_bwd_untransposed(ds, qbar, kbar, scale, row_offset=0):
+    dq, _ = _orig_selector_bwd(ds, qbar, kbar, scale, row_offset)
+    ds = O._np64(ds)
+    C = ds.shape[3]
+    mask = np.array([[1.0 if m < O.history_len(t, row_offset, C) else 0.0 for m in range(C)]
+                     for t in range(ds.shape[2])])
+    return dq, scale * ((ds * mask) @ O._np64(qbar)[:, :, :C])
+
+
+def _pool_q_bwd_no_group(dqbar, hq, n, bs):
+    hkv = O._np64(dqbar).shape[1]
+    return _orig_pool_q_bwd(dqbar, hq, n, bs) * (hq // hkv)
+
+
 MUTATIONS = [
     ("ds_row", _ds_row_no_softmax_term),
     ("topk_history", _topk_ties_high_index),
@@ -63,6 +90,10 @@ MUTATIONS = [
     ("_logits", _logits_bias_sign),
     ("_logits", _logits_no_scale),
     ("bwd_row_block", _bwd_row_dk_unscaled),
+    ("selector_bwd", _selector_bwd_no_scale),
+    ("selector_bwd", _selector_bwd_no_mask),
+    ("selector_bwd", _selector_bwd_untransposed),
+    ("pool_queries_bwd", _pool_q_bwd_no_group),
 ]
 
 PINS = [
@@ -75,6 +106,9 @@ PINS = [
     lambda: pins.test_p1_single_history_block_is_dense_causal(2, 1),
     pins.test_p4_dense_scope_matches_library_softmax_and_autograd,
     pins.test_p6_finite_differences,
+    pins.test_p11_standin_chain_finite_differences,
+    pins.test_p12_pool_adjoints,
+    pins.test_p13_selector_bwd_matches_autograd,
 ]
 
 

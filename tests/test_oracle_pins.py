@@ -460,3 +460,113 @@ def test_selected_pairs_counts_keys():
         for i in range(lo, hi):
             count += int(np.sum(~cur)) + int(np.sum(cur & (J <= i)))
     assert O.selected_pairs(idx, n, bs, 2) == 2 * count
+
+
+# ---------------------------------------------------------------- P11-P13: selector backward (stand-in)
+
+def _standin_loss(q, k, v, dout, K, bs, idx_fixed=None):
+    """L = sum dO . o with s = scale * pooled(q) . pooled(k) in float64 (the
+    stand-in selector), gates log g = s - LSE(s) over the history, selection
+    decided on the fp32 scores.  Returns L, idx and the float64 scores."""
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    qb = O.pool_queries(q, hkv, bs)
+    kb = O.pool_keys(k, bs)
+    scale = 1.0 / math.sqrt(d)
+    s64 = np.einsum("bktd,bkmd->bktm", qb, kb) * scale
+    idx, _, _ = O.select_topk(s64.astype(np.float32), K)
+    if idx_fixed is not None:
+        assert np.array_equal(idx, idx_fixed), "selection moved under the perturbation"
+    T = s64.shape[2]
+    logg = np.zeros(idx.shape)
+    lse = np.full(s64.shape[:3], -math.inf)
+    for bb in range(b):
+        for kv in range(hkv):
+            for t in range(1, T):
+                lse[bb, kv, t] = O.gate_normaliser(s64[bb, kv, t, :t])
+                for sl, m in enumerate(idx[bb, kv, t]):
+                    if m >= 0:
+                        logg[bb, kv, t, sl] = s64[bb, kv, t, m] - lse[bb, kv, t]
+    o, _ = O.attn_fwd(q, k, v, idx, logg, bs)
+    return float((o * O._np64(dout)).sum()), idx, logg, s64, lse, qb, kb
+
+
+def test_p11_standin_chain_finite_differences():
+    """Central differences of L with respect to every entry of q and k, where q
+    and k reach L both through attention and through the stand-in scores (mean
+    pools, dot product, gate softmax).  The analytic gradient is the attention
+    backward plus the selector backward spread through the pools' adjoints."""
+    bs, n, K = 6, 20, 2                  # T = 4, ragged last block
+    w, x = small(seed=21, hq=4, hkv=2, n=n, d=4, bs=bs, K=K)
+    q, k, v, dout = (x[n_].to(F64) for n_ in ("q", "k", "v", "dout"))
+    L0, idx, logg, s64, lse, qb, kb = _standin_loss(q, k, v, dout, K, bs)
+    gr = O.attn_bwd(q, k, v, dout, idx, logg, s64, lse, bs)
+    dqb, dkb = O.selector_bwd(gr["ds"], qb, kb, 1.0 / math.sqrt(4))
+    dq = gr["dq"] + O.pool_queries_bwd(dqb, q.shape[1], n, bs)
+    dk = gr["dk"] + O.pool_keys_bwd(dkb, n, bs)
+    assert np.abs(O.pool_queries_bwd(dqb, q.shape[1], n, bs)).max() > 1e-4   # not vacuous
+    eps = 1e-6
+    for name, grad in (("q", dq), ("k", dk)):
+        base = q if name == "q" else k
+        for pos in itertools.product(*[range(sz) for sz in base.shape]):
+            tp, tm = base.clone(), base.clone()
+            tp[pos] += eps
+            tm[pos] -= eps
+            args_p = (tp, k) if name == "q" else (q, tp)
+            args_m = (tm, k) if name == "q" else (q, tm)
+            lp = _standin_loss(*args_p, v, dout, K, bs, idx_fixed=idx)[0]
+            lm = _standin_loss(*args_m, v, dout, K, bs, idx_fixed=idx)[0]
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-8 + 1e-6 * abs(fd), (name, pos, fd, grad[pos])
+
+
+def test_p12_pool_adjoints():
+    """<pool(x), y> == <x, pool_bwd(y)> for the query pool (heads and tokens)
+    and the key pool, ragged last block included."""
+    rng = np.random.default_rng(5)
+    b, hq, hkv, n, d, bs = 2, 6, 2, 23, 3, 5
+    q = rng.standard_normal((b, hq, n, d))
+    k = rng.standard_normal((b, hkv, n, d))
+    T = O.n_blocks(n, bs)
+    y = rng.standard_normal((b, hkv, T, d))
+    lhs = (O.pool_queries(q, hkv, bs) * y).sum()
+    rhs = (q * O.pool_queries_bwd(y, hq, n, bs)).sum()
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    lhs = (O.pool_keys(k, bs) * y).sum()
+    rhs = (k * O.pool_keys_bwd(y, n, bs)).sum()
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_p13_selector_bwd_matches_autograd():
+    """torch float64 autograd of sum(ds * s) over the valid history, with s the
+    pooled stand-in scores written with torch ops, against the oracle's selector
+    backward and pool adjoints (training rows: C_t = t; decode-style rows with
+    an offset: C_t = min(t + row_offset, C))."""
+    gen = torch.Generator().manual_seed(8)
+    b, hq, hkv, n, d, bs = 2, 4, 2, 29, 6, 6
+    T = O.n_blocks(n, bs)
+    for row_offset, C in ((0, T), (3, T + 2)):
+        q = torch.randn(b, hq, n, d, generator=gen, dtype=F64, requires_grad=True)
+        k = torch.randn(b, hkv, C * bs if C > T else n, d, generator=gen, dtype=F64,
+                        requires_grad=True)
+        nk = k.shape[2]
+        ds = torch.randn(b, hkv, T, C, generator=gen, dtype=F64)
+        # pooled q: mean over the G heads of each group and the block's tokens
+        g = hq // hkv
+        qg = q.reshape(b, hkv, g, n, d)
+        qbar = torch.stack([qg[:, :, :, t * bs:min(n, (t + 1) * bs)].mean(dim=(2, 3))
+                            for t in range(T)], dim=2)
+        kbar = torch.stack([k[:, :, m * bs:min(nk, (m + 1) * bs)].mean(dim=2)
+                            for m in range(C)], dim=2)
+        s = torch.matmul(qbar, kbar.transpose(2, 3)) / math.sqrt(d)
+        mask = torch.zeros(T, C, dtype=F64)
+        for t in range(T):
+            mask[t, :min(t + row_offset, C)] = 1.0
+        (ds * mask * s).sum().backward()
+        dqb, dkb = O.selector_bwd(ds.numpy(), qbar.detach().numpy(), kbar.detach().numpy(),
+                                  1.0 / math.sqrt(d), row_offset=row_offset)
+        assert torch.isfinite(q.grad).all() and torch.isfinite(k.grad).all()
+        np.testing.assert_allclose(O.pool_queries_bwd(dqb, hq, n, bs), q.grad.numpy(),
+                                   rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(O.pool_keys_bwd(dkb, nk, bs), k.grad.numpy(), rtol=1e-12,
+                                   atol=1e-13)
