@@ -68,7 +68,7 @@ def train_step_fn(w, x, ws):
         o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block)
         gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s,
                           w.block, workspace=ws)
-        return idx, gr
+        return idx, gr, qb, kb
     return step
 
 
@@ -153,7 +153,7 @@ def bench_train(args):
     ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
     step = train_step_fn(w, x, ws)
     for _ in range(args.warmup):
-        idx, _ = step()
+        idx, gr, qb, kb = step()
     torch.cuda.synchronize()
     pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
     flops = 12 * w.head_dim * pairs
@@ -184,7 +184,42 @@ def bench_train(args):
                 "traffic": recorded_traffic(name, w.name), "avg_launch_ms": round(avg_ms, 4)}
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
     return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
-                kernels=kernels, x=x, idx=idx)
+                kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb))
+
+
+def bench_selector_bwd(args, w, gr, qb, kb):
+    """The stand-in selector's backward after a step (not in the step time):
+    ds -> pooled summaries, then the pools' adjoints added into dq and dk in
+    place.  The spread reads and writes dq and dk once (HBM roofline)."""
+    import torch
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    call = lambda: ops.selector_bwd(gr["ds"], qb, kb, w.block, w.seqlen, w.hq, dq=gr["dq"],
+                                    dk=gr["dk"])
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.sas_profiler_enable(False)
+    kt = L.sas_profiler_read()
+    esz = 2 if w.dtype == "bf16" else 4
+    spread_bytes = 2 * esz * w.batch * (w.hq + w.hkv) * w.seqlen * w.head_dim
+    n_sp, t_sp = kt.get("pool_spread", (1, 0.0))
+    spread_us = t_sp / n_sp * 1e3 * 2          # two launches (dq, dk) per call
+    n_sb, t_sb = kt.get("selector_bwd", (1, 0.0))
+    sb_us = t_sb / n_sb * 1e3
+    gbs = spread_bytes / (spread_us * 1e-6) / 1e9 if spread_us > 0 else None
+    return {"wall_us_per_call": round((t1 - t0) * 1e6 / args.steps, 2),
+            "selector_bwd_us": round(sb_us, 2), "pool_spread_us": round(spread_us, 2),
+            "pool_spread_bytes": spread_bytes,
+            "pool_spread_GBps": None if gbs is None else round(gbs, 1),
+            "pool_spread_frac_of_hbm_peak": None if gbs is None else round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_decode(wl, steps, layers=12):
@@ -397,6 +432,7 @@ def main():
             "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
             "roofline": res["roofline"],
             "kernels": res["kernels"],
+            "selector_bwd": res["selector_bwd"],
         })
     if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")

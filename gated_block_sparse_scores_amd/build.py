@@ -25,6 +25,7 @@ SOURCES = [
     "attn_mfma_fwd.hip",
     "attn_mfma_bwd.hip",
     "decode.hip",
+    "selector_bwd.hip",
     "sas_api.cpp",
 ]
 

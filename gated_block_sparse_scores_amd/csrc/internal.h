@@ -85,4 +85,9 @@ hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, co
                          const void* vc, const int32_t* idx, const float* logg, void* o,
                          float* lse, void* ws, hipStream_t st);
 
+// ---- selector backward for the stand-in scores (selector_bwd.hip)
+hipError_t launch_selector_bwd(const Dims& dm, const float* ds, const float* qbar,
+                               const float* kbar, float* dqbar, float* dkbar, void* dq, void* dk,
+                               hipStream_t st);
+
 }  // namespace sas

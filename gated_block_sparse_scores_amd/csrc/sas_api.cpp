@@ -422,6 +422,21 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                                           gated ? logg_w : nullptr, o, lse, ws + lay.dec, st));
 }
 
+sas_status sas_selector_bwd(const sas_shape* shape, const float* ds, const float* qbar,
+                            const float* kbar, float* dqbar, float* dkbar, void* dq, void* dk,
+                            void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (!ds || !qbar || !kbar || !dqbar || !dkbar) return SAS_ERR_INVALID_ARG;
+  if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(dqbar) || !aligned16(dkbar) ||
+      (dq && !aligned16(dq)) || (dk && !aligned16(dk)))
+    return SAS_ERR_INVALID_ARG;
+  if ((long)shape->batch * shape->hq > 65535) return SAS_ERR_UNSUPPORTED;  // grid y / z
+  const Dims dm = make_dims(shape, 1);
+  if (dm.n == 0) return SAS_OK;
+  return launch_status(sas::launch_selector_bwd(dm, ds, qbar, kbar, dqbar, dkbar, dq, dk,
+                                                (hipStream_t)stream));
+}
+
 void sas_profiler_enable(int on) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);

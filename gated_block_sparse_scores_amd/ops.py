@@ -137,3 +137,17 @@ def decode_step(q, kbar, kcache, vcache, L_: int, K: int, block: int, gated: boo
     L.sas_decode_step(sh, kcache.shape[2], K, q, kbar, L.dtype_code(kbar.dtype), kbar.shape[2],
                       kcache, vcache, gated, o, lse, idx, logg, lse_s, workspace, ws_n, stream)
     return (o, lse, idx, logg, lse_s) if with_selection else (o, lse)
+
+
+def selector_bwd(ds, qbar, kbar, block: int, seqlen: int, hq: int, dq=None, dk=None,
+                 scale: float = 0.0, stream=None):
+    """Stand-in selector backward of training rows: ds [b,hkv,T,T], qbar/kbar
+    fp32 [b,hkv,T,d] -> (dqbar, dkbar) fp32 [b,hkv,T,d]; dq [b,hq,N,d] and
+    dk [b,hkv,N,d], when given, receive the mean pools' adjoints in place."""
+    b, hkv, T, d = qbar.shape
+    dt = dq.dtype if dq is not None else (dk.dtype if dk is not None else torch.float32)
+    sh = Shape(b, hq, hkv, seqlen, d, block, L.dtype_code(dt), scale)
+    dqbar = torch.empty_like(qbar)
+    dkbar = torch.empty_like(kbar)
+    L.sas_selector_bwd(sh, ds, qbar, kbar, dqbar, dkbar, dq, dk, stream)
+    return dqbar, dkbar

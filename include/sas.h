@@ -218,6 +218,30 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Selector backward for the stand-in scores of training rows (picx 'Key Idea:
+ * Differentiable Continuous Gating': the selector learns through the gates,
+ * the hard Top-K carrying no gradient ('Theoretical Foundation'); evolve.pub
+ * review FAQ for the pooled block summaries).  With
+ * s[t][m] = scale * qbar[t] . kbar[m] on the history m < t:
+ *   dqbar[t] = scale * sum_{m<t} ds[t][m] kbar[m]
+ *   dkbar[m] = scale * sum_{t>m} ds[t][m] qbar[t]
+ * and, when dq / dk are given, the mean pools' adjoints are added to them in
+ * place (dq[h][i] += dqbar[t(i)] / (G n_t); dk[j] += dkbar[m(j)] / n_m, n_t the
+ * valid tokens of block t), one rounding to shape->dtype per element.
+ *   T = ceil(seqlen / block); scale = shape->scale or 1/sqrt(head_dim)
+ *   ds           fp32 [b, hkv, T, T] (as sas_attn_bwd returns it; entries
+ *                m >= t are not read)
+ *   qbar, kbar   fp32 [b, hkv, T, d] (the pooled summaries the scores used)
+ *   dqbar, dkbar fp32 [b, hkv, T, d] outputs (caller-allocated)
+ *   dq [b, hq, seqlen, d], dk [b, hkv, seqlen, d] (shape->dtype): optional,
+ *                accumulated into; 16-byte aligned like qbar..dkbar
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+sas_status sas_selector_bwd(const sas_shape* shape, const float* ds, const float* qbar,
+                            const float* kbar, float* dqbar, float* dkbar, void* dq, void* dk,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (not part of the method).  When enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same
  * stream; sas_profiler_read synchronises those events and returns, per kernel

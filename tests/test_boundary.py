@@ -170,3 +170,17 @@ def test_decode_step_checks():
     assert call(shape(seqlen=4097, hq=36, hkv=4)) == L.SAS_ERR_UNSUPPORTED   # G = 9
     big = shape(seqlen=64 * 16385 + 1, hq=4, hkv=1)                          # C = 16385
     assert call(big, kbar_ld=16385, n=1 << 40) == L.SAS_ERR_UNSUPPORTED
+
+
+def test_selector_bwd_checks():
+    sh = shape(seqlen=1000, hq=8, hkv=2)
+    lib = L.lib()
+
+    def call(ds=FAKE, qbar=FAKE, kbar=FAKE, dqbar=FAKE, dkbar=FAKE, dq=None, dk=None, sh_=sh):
+        return lib.sas_selector_bwd(C.byref(sh_), ds, qbar, kbar, dqbar, dkbar, dq, dk, None)
+
+    for name in ("ds", "qbar", "kbar", "dqbar", "dkbar"):
+        assert call(**{name: None}) == L.SAS_ERR_INVALID_ARG
+    assert call(dq=FAKE + 4) == L.SAS_ERR_INVALID_ARG
+    assert call(kbar=FAKE + 8) == L.SAS_ERR_INVALID_ARG
+    assert call(sh_=shape(head_dim=96)) == L.SAS_ERR_UNSUPPORTED
