@@ -33,6 +33,14 @@ Per row r = (batch b, KV head kv, query block t), with valid history length C_t:
   8. the selector's own backward for the stand-in scores: ds to the pooled
      summaries (dqbar, dkbar), and through the mean pools to dq and dk.
 
+Gate variants (the ablation axes of [alanhou] / [cctest] Table 1; [picx] Eq. 4
+and 5): the activation phi of Eq. 4 is "softmax" (Eq. 6, the method), "sigmoid"
+(g = sigmoid(s)) or "raw" (log g = s, the raw selector logit); "outer" gating
+applies g after the softmax, o = sum_j p_j g_m(j) v_j with p ungated (the
+gradient on the right of Eq. 5); "ste" is hard gating with a straight-through
+backward: the forward is ungated (g = 1 on the selected blocks) and ds is the
+soft phi's Jacobian applied to dL/dg taken at g = 1.
+
 Readings taken where the pages leave a step open: the gate softmax runs over
 all C_t history blocks of the row (not only the selected ones); the 1/sqrt(d)
 scale multiplies q . k only, never the log gate; Top-K ranks s (ties to the
@@ -167,6 +175,27 @@ def gate_normaliser(s_row: np.ndarray) -> float:
     return float(mx + math.log(np.exp(s_row - mx).sum()))
 
 
+ACTIVATIONS = ("softmax", "sigmoid", "raw")
+
+
+def gate_log(s_vals, lse: float, act: str = "softmax") -> np.ndarray:
+    """log g_m of history blocks under the gate activation phi ([picx] Eq. 4):
+    softmax: s_m - LSE(s) (Eq. 6); sigmoid: log sigmoid(s_m); raw: s_m."""
+    s_vals = np.asarray(s_vals, dtype=np.float64)
+    if act == "softmax":
+        return s_vals - lse
+    if act == "sigmoid":
+        return -np.logaddexp(0.0, -s_vals)
+    if act == "raw":
+        return s_vals.copy()
+    raise ValueError(f"unknown gate activation {act!r}")
+
+
+def gate_values(s_vals, lse: float, act: str = "softmax") -> np.ndarray:
+    """g_m = phi(s)_m for history blocks (exp of gate_log)."""
+    return np.exp(gate_log(s_vals, lse, act))
+
+
 def topk_history(s_row32: np.ndarray, K: int) -> np.ndarray:
     """Indices of the min(K, C) largest scores, ranked by (score descending,
     index ascending), returned in ascending index order.
@@ -181,11 +210,13 @@ def topk_history(s_row32: np.ndarray, K: int) -> np.ndarray:
     return np.sort(order[:min(K, C)])
 
 
-def select_topk(s, K: int, row_offset: int = 0, C: Optional[int] = None):
+def select_topk(s, K: int, row_offset: int = 0, C: Optional[int] = None, act: str = "softmax"):
     """Selection for every row of s [b,kv,T,>=C] (fp32 values).
 
     Returns idx int64 [b,kv,T,K] (ascending, -1 padded), logg float64
-    [b,kv,T,K] (0 on pads) and lse_s float64 [b,kv,T] (-inf when C_t = 0)."""
+    [b,kv,T,K] (log g of the selected blocks under `act`, 0 on pads) and lse_s
+    float64 [b,kv,T] (the LSE of the row's history scores, -inf when C_t = 0).
+    phi is monotone for every activation, so the selection does not depend on it."""
     s = np.asarray(s.detach().cpu().numpy() if isinstance(s, torch.Tensor) else s,
                    dtype=np.float32)
     b, hkv, T = s.shape[:3]
@@ -204,7 +235,7 @@ def select_topk(s, K: int, row_offset: int = 0, C: Optional[int] = None):
                 sel = topk_history(row, K)
                 lse_s[bb, kv, t] = lse
                 idx[bb, kv, t, :sel.size] = sel
-                logg[bb, kv, t, :sel.size] = row[sel].astype(np.float64) - lse
+                logg[bb, kv, t, :sel.size] = gate_log(row[sel].astype(np.float64), lse, act)
     return idx, logg, lse_s
 
 
@@ -256,8 +287,11 @@ def _softmax_stats(z):
     return p, lse
 
 
-def fwd_row_block(q, k, v, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int):
-    """Forward of one row block: (o [G,rows,d], lse [G,rows], P list, J data)."""
+def fwd_row_block(q, k, v, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int,
+                  outer: bool = False):
+    """Forward of one row block: (o [G,rows,d], lse [G,rows], P list, J data).
+    With outer gating the logits carry no bias and each key's value is scaled by
+    its block's gate g = exp(log g) after the softmax; P and LSE are ungated."""
     hq, n = q.shape[1], q.shape[2]
     g = hq // k.shape[1]
     idx_row = _npint(idx[bb, kv, t])
@@ -268,17 +302,20 @@ def fwd_row_block(q, k, v, idx, logg, bs: int, scale: float, bb: int, kv: int, t
     lo, hi = block_span(t, bs, n)
     pos = np.arange(lo, hi)
     os_, lses, ps = [], [], []
+    zbias = np.zeros_like(bias) if outer else bias
+    vg = vj * np.exp(bias)[:, None] if outer else vj
     for h in range(kv * g, (kv + 1) * g):
-        z = _logits(_np64(q[bb, h, lo:hi]), pos, kj, J, bias, cur, scale)
+        z = _logits(_np64(q[bb, h, lo:hi]), pos, kj, J, zbias, cur, scale)
         p, lse = _softmax_stats(z)
-        os_.append(p @ vj)
+        os_.append(p @ vg)
         lses.append(lse)
         ps.append(p)
     return np.stack(os_), np.stack(lses), ps, (J, bias, slot, cur, kj, vj)
 
 
-def attn_fwd(q, k, v, idx, logg, bs: int, scale: Optional[float] = None):
-    """o [b,hq,N,d] and LSE [b,hq,N] (float64) of gated block-sparse attention."""
+def attn_fwd(q, k, v, idx, logg, bs: int, scale: Optional[float] = None, outer: bool = False):
+    """o [b,hq,N,d] and LSE [b,hq,N] (float64) of gated block-sparse attention
+    (inner gating, Eq. 9; or outer gating)."""
     b, hq, n, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
@@ -289,7 +326,7 @@ def attn_fwd(q, k, v, idx, logg, bs: int, scale: Optional[float] = None):
         for kv in range(hkv):
             for t in range(n_blocks(n, bs)):
                 lo, hi = block_span(t, bs, n)
-                ob, lb, _, _ = fwd_row_block(q, k, v, idx, logg, bs, scale, bb, kv, t)
+                ob, lb, _, _ = fwd_row_block(q, k, v, idx, logg, bs, scale, bb, kv, t, outer)
                 o[bb, kv * g:(kv + 1) * g, lo:hi] = ob
                 lse[bb, kv * g:(kv + 1) * g, lo:hi] = lb
     return o, lse
@@ -334,14 +371,17 @@ def attn_fwd_dense(q, k, v, idx, logg, bs: int, scale: Optional[float] = None):
 
 # --------------------------------------------------------------------------- (6) backward
 
-def bwd_row_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int):
+def bwd_row_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, t: int,
+                  outer: bool = False):
     """Backward of one row block for L = sum dO . o.
 
-    Returns dq [G,rows,d], dlogg [K] (sum of dS over each selected block, all G
-    heads and all rows of the block), and the key-side contributions
-    (J, dk_J, dv_J) to be summed over row blocks."""
+    Returns dq [G,rows,d], dlogg [K] (dL/d(log g_m): with inner gating the sum
+    of dS over each selected block, all G heads and all rows of the block; with
+    outer gating g_m times dL/dg_m = sum p dO . v over the block, Eq. 5 right),
+    and the key-side contributions (J, dk_J, dv_J) to be summed over row blocks."""
     o, lse, ps, (J, bias, slot, cur, kj, vj) = fwd_row_block(q, k, v, idx, logg, bs, scale,
-                                                             bb, kv, t)
+                                                             bb, kv, t, outer)
+    mult = np.exp(bias) if outer else np.ones_like(bias)   # value scale per key
     hq, n = q.shape[1], q.shape[2]
     g = hq // k.shape[1]
     K = idx.shape[3]
@@ -355,38 +395,50 @@ def bwd_row_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: 
         do = _np64(dout[bb, h, lo:hi])
         qh = _np64(q[bb, h, lo:hi])
         D = (do * o[gi]).sum(axis=1)                  # D_i = dO_i . o_i
-        dp = do @ vj.T                                # dP_ij = dO_i . v_j
+        dp = (do @ vj.T) * mult[None, :]              # dP_ij = dO_i . (g v_j)
         ds_ = p * (dp - D[:, None])                   # dS_ij = p_ij (dP_ij - D_i)
         dq[gi] = (ds_ @ kj) * scale
         dk_j += (ds_.T @ qh) * scale
-        dv_j += p.T @ do
-        col = ds_.sum(axis=0)
+        dv_j += (p.T @ do) * mult[:, None]
+        col = (p * dp).sum(axis=0) if outer else ds_.sum(axis=0)
         for sl in range(K):
             dlogg[sl] += col[slot == sl].sum()
     return dq, dlogg, (J, dk_j, dv_j)
 
 
-def ds_row(s_row, lse_s: float, idx_row, dlogg_row) -> np.ndarray:
-    """Selector gradient over the whole valid history of a row:
-    ds_m = 1[m in I] dlogg_m - g_m * sum_{m' in I} dlogg_{m'}, g_m = exp(s_m - lse_s)
-    (derivative of log g_m = s_m - LSE(s), [picx] Eq. 6; Top-K carries none,
-    [picx] 'Theoretical Foundation')."""
+def ds_row(s_row, lse_s: float, idx_row, dlogg_row, act: str = "softmax",
+           ste: bool = False) -> np.ndarray:
+    """Selector gradient over the whole valid history of a row, from
+    dlogg_m = dL/d(log g_m) at the selected blocks (Top-K carries none,
+    [picx] 'Theoretical Foundation'):
+      softmax (Eq. 6): ds_m = 1[m in I] dlogg_m - g_m * sum_{m' in I} dlogg_{m'},
+                       g_m = exp(s_m - lse_s)
+      sigmoid:         ds_m = 1[m in I] dlogg_m (1 - sigmoid(s_m))
+      raw:             ds_m = 1[m in I] dlogg_m
+    With ste the forward was hard (g = 1), so dlogg is dL/dg there; the soft
+    gate's Jacobian then acts on it, which is the same formula applied to
+    g_m dlogg_m."""
     s_row = np.asarray(s_row, dtype=np.float64)
-    gates = np.exp(s_row - lse_s)
-    ds = np.zeros_like(s_row)
-    total = 0.0
+    gates = gate_values(s_row, lse_s, act)
+    own = np.zeros_like(s_row)
     for sl, m in enumerate(np.asarray(idx_row).tolist()):
         if m < 0:
             continue
-        ds[m] += dlogg_row[sl]
-        total += dlogg_row[sl]
-    return ds - gates * total
+        own[m] += dlogg_row[sl] * (gates[m] if ste else 1.0)
+    if act == "softmax":
+        return own - gates * own.sum()
+    if act == "sigmoid":
+        return own * (1.0 - gates)
+    return own
 
 
 def attn_bwd(q, k, v, dout, idx, logg, s, lse_s, bs: int, scale: Optional[float] = None,
-             row_offset: int = 0):
+             row_offset: int = 0, act: str = "softmax", outer: bool = False, ste: bool = False):
     """All gradients: dq [b,hq,N,d], dk/dv [b,hkv,N,d], dlogg [b,kv,T,K],
-    ds [b,kv,T,C] (0 where m >= C_t)."""
+    ds [b,kv,T,C] (0 where m >= C_t).  With ste the attention is the hard
+    (ungated) forward whatever logg holds."""
+    if ste:
+        logg = None
     b, hq, n, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
@@ -407,7 +459,7 @@ def attn_bwd(q, k, v, dout, idx, logg, s, lse_s, bs: int, scale: Optional[float]
             for t in range(T):
                 lo, hi = block_span(t, bs, n)
                 dqb, dl, (J, dkj, dvj) = bwd_row_block(q, k, v, dout, idx, logg, bs, scale,
-                                                       bb, kv, t)
+                                                       bb, kv, t, outer)
                 dq[bb, kv * g:(kv + 1) * g, lo:hi] = dqb
                 dk[bb, kv, J] += dkj
                 dv[bb, kv, J] += dvj
@@ -415,11 +467,12 @@ def attn_bwd(q, k, v, dout, idx, logg, s, lse_s, bs: int, scale: Optional[float]
                 ct = history_len(t, row_offset, C)
                 if ct > 0:
                     ds[bb, kv, t, :ct] = ds_row(s32[bb, kv, t, :ct], lse_s[bb, kv, t],
-                                                _npint(idx[bb, kv, t]), dl)
+                                                _npint(idx[bb, kv, t]), dl, act, ste)
     return {"dq": dq, "dk": dk, "dv": dv, "dlogg": dlogg, "ds": ds}
 
 
-def bwd_key_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, m: int):
+def bwd_key_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: int, m: int,
+                  outer: bool = False):
     """dk, dv on the tokens of key block B_m only: the sum over every row block
     whose key set contains B_m (the blocks that selected m, and m itself)."""
     n = q.shape[2]
@@ -431,7 +484,8 @@ def bwd_key_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: 
     for t in range(m, T):
         if t != m and m not in idx_np[t].tolist():
             continue
-        _, _, (J, dkj, dvj) = bwd_row_block(q, k, v, dout, idx, logg, bs, scale, bb, kv, t)
+        _, _, (J, dkj, dvj) = bwd_row_block(q, k, v, dout, idx, logg, bs, scale, bb, kv, t,
+                                            outer)
         sel = (J >= lo) & (J < hi)
         dk[J[sel] - lo] += dkj[sel]
         dv[J[sel] - lo] += dvj[sel]
@@ -440,10 +494,12 @@ def bwd_key_block(q, k, v, dout, idx, logg, bs: int, scale: float, bb: int, kv: 
 
 # --------------------------------------------------------------------------- (7) decode
 
-def decode(q, kcache, vcache, L: int, idx, logg, bs: int, scale: Optional[float] = None):
+def decode(q, kcache, vcache, L: int, idx, logg, bs: int, scale: Optional[float] = None,
+           outer: bool = False):
     """Single-token attention at position L - 1 over the selected history blocks
     and the current block's prefix.  logg None -> ungated ([picx] Eq. 2, the
-    deployed form in [evolve] 'Summary').  q [b,hq,d] -> o [b,hq,d], lse [b,hq]."""
+    deployed form in [evolve] 'Summary'); outer: gates scale the values after
+    the softmax.  q [b,hq,d] -> o [b,hq,d], lse [b,hq]."""
     b, hq, d = q.shape
     hkv = kcache.shape[1]
     g = hq // hkv
@@ -458,6 +514,9 @@ def decode(q, kcache, vcache, L: int, idx, logg, bs: int, scale: Optional[float]
             J, bias, _, _ = key_set(c, idx_row, logg_row, bs, L, last_pos=L - 1)
             kj = _rows(kcache[bb, kv], J)
             vj = _rows(vcache[bb, kv], J)
+            if outer:
+                vj = vj * np.exp(bias)[:, None]
+                bias = np.zeros_like(bias)
             for h in range(kv * g, (kv + 1) * g):
                 z = (_np64(q[bb, h]) @ kj.T) * scale + bias
                 p, l = _softmax_stats(z[None, :])

@@ -9,7 +9,7 @@ from oracle import sas_oracle as O
 import tests.test_oracle_pins as pins
 
 
-def _ds_row_no_softmax_term(s_row, lse_s, idx_row, dlogg_row):
+def _ds_row_no_softmax_term(s_row, lse_s, idx_row, dlogg_row, act="softmax", ste=False):
     ds = np.zeros(len(s_row))
     for sl, m in enumerate(np.asarray(idx_row).tolist()):
         if m >= 0:
@@ -82,6 +82,30 @@ def _pool_q_bwd_no_group(dqbar, hq, n, bs):
     return _orig_pool_q_bwd(dqbar, hq, n, bs) * (hq // hkv)
 
 
+_orig_ds_row = O.ds_row
+_orig_fwd_row = O.fwd_row_block
+_orig_gate_log = O.gate_log
+
+
+def _ds_row_sigmoid_without_slope(s_row, lse_s, idx_row, dlogg_row, act="softmax", ste=False):
+    return _orig_ds_row(s_row, lse_s, idx_row, dlogg_row, "raw" if act == "sigmoid" else act, ste)
+
+
+def _ds_row_ste_without_gate(s_row, lse_s, idx_row, dlogg_row, act="softmax", ste=False):
+    return _orig_ds_row(s_row, lse_s, idx_row, dlogg_row, act, False)
+
+
+def _fwd_row_outer_ignored(*a, **k):
+    if len(a) > 10:
+        a = a[:10] + (False,)
+    k.pop("outer", None)
+    return _orig_fwd_row(*a, **k)
+
+
+def _gate_log_sigmoid_as_softmax(s_vals, lse, act="softmax"):
+    return _orig_gate_log(s_vals, lse, "softmax" if act == "sigmoid" else act)
+
+
 MUTATIONS = [
     ("ds_row", _ds_row_no_softmax_term),
     ("topk_history", _topk_ties_high_index),
@@ -94,6 +118,10 @@ MUTATIONS = [
     ("selector_bwd", _selector_bwd_no_mask),
     ("selector_bwd", _selector_bwd_untransposed),
     ("pool_queries_bwd", _pool_q_bwd_no_group),
+    ("ds_row", _ds_row_sigmoid_without_slope),
+    ("ds_row", _ds_row_ste_without_gate),
+    ("fwd_row_block", _fwd_row_outer_ignored),
+    ("gate_log", _gate_log_sigmoid_as_softmax),
 ]
 
 PINS = [
@@ -109,6 +137,11 @@ PINS = [
     pins.test_p11_standin_chain_finite_differences,
     pins.test_p12_pool_adjoints,
     pins.test_p13_selector_bwd_matches_autograd,
+    pins.test_p14_gate_activations_closed_forms,
+    pins.test_p15_outer_gating_forward_and_eq5,
+    lambda: pins.test_p16_variant_finite_differences("sigmoid", False),
+    lambda: pins.test_p16_variant_finite_differences("softmax", True),
+    lambda: pins.test_p17_straight_through("softmax"),
 ]
 
 

@@ -570,3 +570,193 @@ def test_p13_selector_bwd_matches_autograd():
                                    rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(O.pool_keys_bwd(dkb, nk, bs), k.grad.numpy(), rtol=1e-12,
                                    atol=1e-13)
+
+
+# ---------------------------------------------------------------- P14-P17: gate variants
+
+def test_p14_gate_activations_closed_forms():
+    """log g under each activation of [picx] Eq. 4 equals its library form
+    (torch log_softmax over the history, logsigmoid, identity); the Top-K set is
+    the same for all three (phi is monotone)."""
+    w, x = small(seed=31, n=64, bs=8, K=3)
+    s32 = x["s"].numpy().astype(np.float32)
+    base_idx = None
+    for act, ref in (("softmax", None), ("sigmoid", F.logsigmoid), ("raw", lambda z: z)):
+        idx, logg, lse = O.select_topk(s32, 3, act=act)
+        if base_idx is None:
+            base_idx = idx
+        assert np.array_equal(idx, base_idx)
+        T = s32.shape[2]
+        for t in range(1, T):
+            row = torch.from_numpy(s32[0, 0, t, :t].astype(np.float64))
+            full = torch.log_softmax(row, 0) if act == "softmax" else ref(row)
+            for sl, m in enumerate(idx[0, 0, t]):
+                if m >= 0:
+                    assert abs(logg[0, 0, t, sl] - float(full[m])) <= 1e-12
+
+
+def _outer_reference(q, k, v, idx, logg, bs):
+    """o = softmax(q K_J^T / sqrt(d), causal on the current block) @ (g * V_J),
+    written with torch ops per query block (outer gating)."""
+    b, hq, n, d = q.shape
+    g_ = hq // k.shape[1]
+    out = torch.zeros(b, hq, n, d, dtype=F64)
+    for t in range(O.n_blocks(n, bs)):
+        lo, hi = O.block_span(t, bs, n)
+        keys, gains = [], []
+        for sl, m in enumerate(idx[0, 0, t].tolist()):
+            if m >= 0:
+                mlo, mhi = O.block_span(m, bs, n)
+                keys += list(range(mlo, mhi))
+                gains += [math.exp(logg[0, 0, t, sl])] * (mhi - mlo)
+        keys += list(range(lo, hi))
+        gains += [1.0] * (hi - lo)
+        J = torch.tensor(keys)
+        for h in range(hq):
+            z = q[0, h, lo:hi] @ k[0, h // g_, J].T / math.sqrt(d)
+            future = (J[None, :] > torch.arange(lo, hi)[:, None]) & (J[None, :] >= lo)
+            z = z.masked_fill(future, -math.inf)
+            out[0, h, lo:hi] = torch.softmax(z, 1) @ (v[0, h // g_, J] *
+                                                     torch.tensor(gains, dtype=F64)[:, None])
+    return out
+
+
+def test_p15_outer_gating_forward_and_eq5():
+    """Outer gating: the forward equals softmax(qK^T)(g V) written with torch
+    ops, and dlogg_m / g_m equals the right-hand side of [picx] Eq. 5,
+    sum over the block's keys of p_i dO . v_i, evaluated from torch's softmax."""
+    bs, n, K = 8, 40, 2
+    w, x = small(seed=17, hq=2, hkv=1, n=n, d=6, bs=bs, K=K)
+    q, k, v, dout = (x[n_].to(F64) for n_ in ("q", "k", "v", "dout"))
+    idx, logg, lse_s = O.select_topk(x["s"].numpy().astype(np.float32), K)
+    o, _ = O.attn_fwd(q, k, v, idx, logg, bs, outer=True)
+    ref = _outer_reference(q, k, v, idx, logg, bs)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+    gr = O.attn_bwd(q, k, v, dout, idx, logg, x["s"].numpy(), lse_s, bs, outer=True)
+    T = O.n_blocks(n, bs)
+    for t in range(1, T):
+        lo, hi = O.block_span(t, bs, n)
+        for sl, m in enumerate(idx[0, 0, t].tolist()):
+            if m < 0:
+                continue
+            mlo, mhi = O.block_span(m, bs, n)
+            # probabilities of the ungated softmax over the row's key set
+            keys = [j for s2, m2 in enumerate(idx[0, 0, t].tolist()) if m2 >= 0
+                    for j in range(*O.block_span(m2, bs, n))] + list(range(lo, hi))
+            J = torch.tensor(keys)
+            dg = 0.0
+            for h in range(2):
+                z = q[0, h, lo:hi] @ k[0, 0, J].T / math.sqrt(6)
+                z = z.masked_fill((J[None, :] > torch.arange(lo, hi)[:, None]) & (J[None, :] >= lo),
+                                  -math.inf)
+                p = torch.softmax(z, 1)
+                sel = (J >= mlo) & (J < mhi)
+                dg += float((p[:, sel] * (dout[0, h, lo:hi] @ v[0, 0, J[sel]].T)).sum())
+            assert abs(gr["dlogg"][0, 0, t, sl] / math.exp(logg[0, 0, t, sl]) - dg) <= \
+                1e-10 * max(1.0, abs(dg))
+
+
+def _variant_loss(x, s64, K, bs, act, outer):
+    s32 = s64.astype(np.float32)
+    idx, _, _ = O.select_topk(s32, K)
+    T = s64.shape[2]
+    logg = np.zeros(idx.shape)
+    for t in range(1, T):
+        lse = O.gate_normaliser(s64[0, 0, t, :t])
+        for sl, m in enumerate(idx[0, 0, t]):
+            if m >= 0:
+                logg[0, 0, t, sl] = O.gate_log(s64[0, 0, t, m:m + 1], lse, act)[0]
+    o, _ = O.attn_fwd(x["q"], x["k"], x["v"], idx, logg, bs, outer=outer)
+    return float((o * O._np64(x["dout"])).sum()), idx, logg
+
+
+@pytest.mark.parametrize("act,outer", [("sigmoid", False), ("raw", False), ("softmax", True),
+                                       ("sigmoid", True)])
+def test_p16_variant_finite_differences(act, outer):
+    """Central differences of L in every valid score (and, for outer gating, in
+    every entry of q, k, v) for the gate variants."""
+    bs, n, K = 6, 20, 2
+    w, x = small(seed=23, hq=2, hkv=1, n=n, d=4, bs=bs, K=K)
+    x = {k_: (v_.to(F64) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in x.items()}
+    s32 = x["s"].numpy().astype(np.float32).astype(np.float64)
+    L0, idx, logg = _variant_loss(x, s32, K, bs, act, outer)
+    lse = np.full(s32.shape[:3], -math.inf)
+    for t in range(1, s32.shape[2]):
+        lse[0, 0, t] = O.gate_normaliser(s32[0, 0, t, :t])
+    gr = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], idx, logg, s32, lse, bs, act=act,
+                    outer=outer)
+    eps = 1e-6
+    T = O.n_blocks(n, bs)
+    for t in range(1, T):
+        for m in range(t):
+            sp, sm = s32.copy(), s32.copy()
+            sp[0, 0, t, m] += eps
+            sm[0, 0, t, m] -= eps
+            lp, ip, _ = _variant_loss(x, sp, K, bs, act, outer)
+            lm, im, _ = _variant_loss(x, sm, K, bs, act, outer)
+            assert np.array_equal(ip, idx) and np.array_equal(im, idx)
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gr["ds"][0, 0, t, m]) <= 1e-8 + 1e-6 * abs(fd), (t, m)
+    if not outer:
+        return
+    for name in ("q", "k", "v"):
+        base = x[name].clone()
+        for pos in itertools.product(*[range(sz) for sz in base.shape]):
+            xp = dict(x)
+            tp, tm = base.clone(), base.clone()
+            tp[pos] += eps
+            tm[pos] -= eps
+            xp[name] = tp
+            lp = _variant_loss(xp, s32, K, bs, act, outer)[0]
+            xp[name] = tm
+            lm = _variant_loss(xp, s32, K, bs, act, outer)[0]
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gr["d" + name][pos]) <= 1e-8 + 1e-6 * abs(fd), (name, pos)
+
+
+@pytest.mark.parametrize("act", ["softmax", "sigmoid", "raw"])
+def test_p17_straight_through(act):
+    """STE: the forward is the hard (ungated) one, and ds = J_phi(s)^T dL/dg with
+    dL/dg taken by central differences of the hard forward's loss in each
+    selected block's gate at g = 1, and J_phi from torch autograd."""
+    bs, n, K = 6, 30, 2
+    w, x = small(seed=29, hq=2, hkv=1, n=n, d=4, bs=bs, K=K)
+    q, k, v, dout = (x[n_].to(F64) for n_ in ("q", "k", "v", "dout"))
+    s32 = x["s"].numpy().astype(np.float32)
+    idx, logg, lse_s = O.select_topk(s32, K, act=act)
+    gr = O.attn_bwd(q, k, v, dout, idx, logg, s32, lse_s, bs, act=act, ste=True)
+    do = O._np64(dout)
+    eps = 1e-6
+    phi = {"softmax": lambda z: torch.softmax(z, 0), "sigmoid": torch.sigmoid,
+           "raw": torch.exp}[act]
+    for t in range(1, O.n_blocks(n, bs)):
+        dLdg = np.zeros(t)
+        for sl, m in enumerate(idx[0, 0, t].tolist()):
+            if m < 0:
+                continue
+            vals = []
+            for sign in (1, -1):
+                lg = np.zeros(idx.shape)
+                lg[0, 0, t, sl] = math.log(1.0 + sign * eps)
+                o, _ = O.attn_fwd(q, k, v, idx, lg, bs)
+                vals.append(float((o * do).sum()))
+            dLdg[m] = (vals[0] - vals[1]) / (2 * eps)
+        row = torch.tensor(s32[0, 0, t, :t].astype(np.float64))
+        Jm = torch.autograd.functional.jacobian(phi, row).numpy()    # [g_m, s_m']
+        ref = Jm.T @ dLdg
+        np.testing.assert_allclose(gr["ds"][0, 0, t, :t], ref, rtol=1e-6, atol=1e-9)
+    # q, k, v gradients under ste are those of the hard forward: central
+    # differences of the ungated loss in a few entries of q and v
+    for name, base in (("q", q), ("v", v)):
+        for pos in ((0, 0, 7, 1), (0, 1, 25, 3), (0, 0, 29, 0)):
+            if name == "v":
+                pos = (0, 0) + pos[2:]
+            tp, tm = base.clone(), base.clone()
+            tp[pos] += eps
+            tm[pos] -= eps
+            lp = float((O.attn_fwd(tp if name == "q" else q, k, tp if name == "v" else v, idx,
+                                   None, bs)[0] * do).sum())
+            lm = float((O.attn_fwd(tm if name == "q" else q, k, tm if name == "v" else v, idx,
+                                   None, bs)[0] * do).sum())
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gr["d" + name][pos]) <= 1e-8 + 1e-6 * abs(fd), (name, pos)
