@@ -18,6 +18,15 @@ LIB_PATH = os.path.join(HERE, "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_LAUNCH = range(5)
 SAS_DTYPE_F32, SAS_DTYPE_BF16 = 0, 1
+SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_RAW = 0, 1, 2
+SAS_GATE_OUTER, SAS_GATE_STE = 4, 8
+GATE_ACTIVATIONS = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID,
+                    "raw": SAS_GATE_RAW}
+
+
+def gate_code(act: str = "softmax", outer: bool = False, ste: bool = False) -> int:
+    """sas_gate bits of a variant (activation name, outer gating, straight-through)."""
+    return GATE_ACTIVATIONS[act] | (SAS_GATE_OUTER if outer else 0) | (SAS_GATE_STE if ste else 0)
 
 EXPORTED = [
     "sas_status_string", "sas_version", "sas_block_pool", "sas_select_topk_workspace_size",
@@ -38,7 +47,7 @@ class SasError(RuntimeError):
 class sas_shape(C.Structure):
     _fields_ = [("batch", C.c_int), ("hq", C.c_int), ("hkv", C.c_int), ("seqlen", C.c_int),
                 ("head_dim", C.c_int), ("block", C.c_int), ("dtype", C.c_int),
-                ("scale", C.c_float)]
+                ("scale", C.c_float), ("gate", C.c_int)]
 
 
 class sas_kernel_time(C.Structure):
@@ -55,10 +64,11 @@ class Shape:
     block: int
     dtype: int = SAS_DTYPE_BF16
     scale: float = 0.0
+    gate: int = 0
 
     def c(self) -> sas_shape:
         return sas_shape(self.batch, self.hq, self.hkv, self.seqlen, self.head_dim, self.block,
-                         self.dtype, self.scale)
+                         self.dtype, self.scale, self.gate)
 
 
 _lib = None

@@ -168,7 +168,9 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
   const int nb = nblk;
   for (int bi = 0; bi < nb; ++bi) {
     const int m = blist[bi];
-    const float bias = bbias[bi];
+    // inner gating adds log g to the logits; outer gating scales P V by g
+    const float bias = dm.outer ? 0.0f : bbias[bi];
+    const float gain = dm.outer ? expf(bbias[bi]) : 1.0f;
     for (int c0 = 0; c0 < BS; c0 += KC) {
       const int lo = m * BS + c0;
       const int nk = min(KC, dm.n - lo);
@@ -194,7 +196,7 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
       for (int j = 0; j < KC; ++j) {
         const float pj = sc[j] == -INFINITY ? 0.0f : expf(sc[j] - mnew);
         lrun += pj;
-        axpy_slice<D>(acc, pj, Vs[j], p);
+        axpy_slice<D>(acc, pj * gain, Vs[j], p);
       }
       mrun = mnew;
       __syncthreads();
@@ -323,7 +325,8 @@ __global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
   }
   for (int bi = 0; bi < nb; ++bi) {
     const int m = blist[bi];
-    const float bias = bbias[bi];
+    const float bias = dm.outer ? 0.0f : bbias[bi];
+    const float gain = dm.outer ? expf(bbias[bi]) : 1.0f;
     float bsum = 0.0f;
     for (int c0 = 0; c0 < BS; c0 += KC) {
       const int lo = m * BS + c0;
@@ -335,12 +338,13 @@ __global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const float z = reduce_p<D>(dot_slice<D>(qv, Ks[j], p)) * dm.scale + bias;
-        const float dp = reduce_p<D>(dot_slice<D>(dov, Vs[j], p));
+        const float dp = reduce_p<D>(dot_slice<D>(dov, Vs[j], p)) * gain;
         const bool valid = active && j < nk && (m != t || lo + j <= i);
         const float pj = valid ? expf(z - lse_i) : 0.0f;
         const float ds = pj * (dp - D_i);
         axpy_slice<D>(acc, ds, Ks[j], p);
-        bsum += ds;
+        // dL/dlog g: the block's dS (inner), or its p dP (outer)
+        bsum += dm.outer ? pj * dp : ds;
       }
       __syncthreads();
     }
@@ -411,8 +415,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
   for (int ei = 0; ei < ne; ++ei) {
     const int t = lst[ei] >> 8;
     const int slot = (lst[ei] & 255) == 0xFE ? -1 : (lst[ei] & 255);
-    const float bias =
-        (slot >= 0 && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] : 0.0f;
+    const float lg = (slot >= 0 && logg) ? logg[(bk * dm.T + t) * (size_t)dm.K + slot] : 0.0f;
+    const float bias = dm.outer ? 0.0f : lg;
+    const float gain = dm.outer ? expf(lg) : 1.0f;
     for (int hh = 0; hh < dm.g; ++hh) {
       const int h = kv * dm.g + hh;
       const size_t rbase = ((size_t)b * dm.hq + h) * dm.n;
@@ -430,11 +435,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
 #pragma unroll 4
         for (int ii = 0; ii < KC; ++ii) {
           const float z = reduce_p<D>(dot_slice<D>(kvk, Qs[ii], p)) * dm.scale + bias;
-          const float dp = reduce_p<D>(dot_slice<D>(kvv, Os[ii], p));
+          const float dp = reduce_p<D>(dot_slice<D>(kvv, Os[ii], p)) * gain;
           const bool valid = kact && ii < nr && (t != m || j <= lo + ii);
           const float pj = valid ? expf(z - Ls[ii]) : 0.0f;
           const float ds = pj * (dp - Dl[ii]);
-          axpy_slice<D>(adv, pj, Os[ii], p);
+          axpy_slice<D>(adv, pj * gain, Os[ii], p);
           axpy_slice<D>(adk, ds, Qs[ii], p);
         }
         __syncthreads();
@@ -449,11 +454,23 @@ __global__ void __launch_bounds__(256) bwd_dkdv_generic_kernel(
 }
 
 // ---------------------------------------------------------------- backward: ds
-// Per row (b, kv, t): dlogg = sum of the per-chunk partials (fixed order),
-// ds_m = [m in I] dlogg_slot(m) - exp(s_m - lse_s) * sum(dlogg) for m < t,
-// 0 for m >= t.
+// g = phi(s) under the gate activation (0 softmax: exp(s - lse); 1 sigmoid;
+// 2 raw logit: exp(s)).
+__device__ __forceinline__ float gate_value(float s, float lse, int act) {
+  if (act == 1) return 1.0f / (1.0f + expf(-s));
+  if (act == 2) return expf(s);
+  return expf(s - lse);
+}
+
+// Per row (b, kv, t): dlogg = sum of the per-chunk partials (fixed order);
+// with ste the forward was hard and dlogg_m is dL/dg_m, so the soft gate's
+// Jacobian acts on e_m = g_m dlogg_m, else e_m = dlogg_m.  For m < t:
+//   softmax: ds_m = [m in I] e_m - g_m sum(e)   (Eq. 6 differentiated)
+//   sigmoid: ds_m = [m in I] e_m (1 - g_m)
+//   raw:     ds_m = [m in I] e_m
+// and 0 for m >= t.
 __global__ void __launch_bounds__(256) bwd_ds_kernel(
-    int T, int K, const int32_t* __restrict__ idx, const float* __restrict__ s,
+    int T, int K, int act, int ste, const int32_t* __restrict__ idx, const float* __restrict__ s,
     const float* __restrict__ lse_s, const float* __restrict__ dlogg_part, int nchunk,
     float* __restrict__ dlogg, float* __restrict__ ds) {
   __shared__ float dl[64];
@@ -461,12 +478,14 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(
   __shared__ float tot;
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
+  const float ls = lse_s ? lse_s[row] : 0.0f;
   if (threadIdx.x < K) {
     float a = 0.0f;
     for (int c = 0; c < nchunk; ++c) a += dlogg_part[(row * nchunk + c) * K + threadIdx.x];
     const int m = idx[row * K + threadIdx.x];
     const bool ok = m >= 0 && m < t;
-    dl[threadIdx.x] = ok ? a : 0.0f;
+    const float e = (ok && ste && s) ? a * gate_value(s[row * T + m], ls, act) : a;
+    dl[threadIdx.x] = ok ? e : 0.0f;
     im[threadIdx.x] = ok ? m : -1;
     if (dlogg) dlogg[row * K + threadIdx.x] = ok ? a : 0.0f;
   }
@@ -478,14 +497,19 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(
   }
   __syncthreads();
   if (!ds) return;
-  const float ls = lse_s ? lse_s[row] : 0.0f;
   for (int m = threadIdx.x; m < T; m += blockDim.x) {
     float val = 0.0f;
     if (m < t) {
       float own = 0.0f;
       for (int sl = 0; sl < K; ++sl)
         if (im[sl] == m) own = dl[sl];
-      val = own - expf(s[row * T + m] - ls) * tot;
+      const float sm = s[row * T + m];
+      if (act == 1)
+        val = own * (1.0f - gate_value(sm, ls, 1));
+      else if (act == 2)
+        val = own;
+      else
+        val = own - expf(sm - ls) * tot;
     }
     ds[row * T + m] = val;
   }
@@ -618,8 +642,8 @@ hipError_t launch_bwd_ds(const Dims& dm, const int32_t* idx, const float* s, con
                          hipStream_t st) {
   const size_t rows = (size_t)dm.b * dm.hkv * dm.T;
   ProfScope ps("bwd_ds", st);
-  hipLaunchKernelGGL(bwd_ds_kernel, dim3((unsigned)rows), dim3(256), 0, st, dm.T, dm.K, idx, s,
-                     lse_s, dlogg_part, nchunk, dlogg, ds);
+  hipLaunchKernelGGL(bwd_ds_kernel, dim3((unsigned)rows), dim3(256), 0, st, dm.T, dm.K, dm.act,
+                     dm.ste ? 1 : 0, idx, s, lse_s, dlogg_part, nchunk, dlogg, ds);
   return hipGetLastError();
 }
 

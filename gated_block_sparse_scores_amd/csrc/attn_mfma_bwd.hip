@@ -384,9 +384,10 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
 
 }  // namespace
 
+// Inner gating only (outer gating runs the portable kernels).
 bool mfma_bwd_supported(const Dims& dm) {
   return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
-         dm.T <= DKV_MAXT;
+         dm.T <= DKV_MAXT && !dm.outer;
 }
 
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,

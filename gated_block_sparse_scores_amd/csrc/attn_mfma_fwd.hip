@@ -212,8 +212,10 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
 
 }  // namespace
 
+// Inner gating only (outer gating runs the portable kernel).
 bool mfma_fwd_supported(const Dims& dm) {
-  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0;
+  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
+         !dm.outer;
 }
 
 hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,

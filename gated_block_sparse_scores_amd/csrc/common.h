@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// log g of a selected history block under the gate activation (picx.dev
+// summary of SAS, Eq. 4 and 6): 0 softmax, s - LSE(s); 1 sigmoid, log sigmoid(s)
+// = -(max(-s, 0) + log1p(exp(-|s|))); 2 raw logit, s.
+__device__ __forceinline__ float gate_log(float s, float lse, int act) {
+  if (act == 1) return -(fmaxf(-s, 0.0f) + log1pf(expf(-fabsf(s))));
+  if (act == 2) return s;
+  return s - lse;
+}
+
 // Inverse of order_key.
 __device__ __forceinline__ float from_order_key(uint32_t k) {
   const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;

@@ -132,7 +132,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   __shared__ float sc[kMaxG][MAXKEYS];
   __shared__ __align__(16) float red[4][kMaxG][D];
   __shared__ int blist[kMaxBps];
-  __shared__ float bbias[kMaxBps];
+  __shared__ float bbias[kMaxBps];  // added to the logits (inner gating)
+  __shared__ float bgain[kMaxBps];  // multiplies the values (outer gating)
   __shared__ float mx_sh[kMaxG], l_sh[kMaxG];
   __shared__ int nb_sh;
 
@@ -151,8 +152,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
       const int m = idx[(size_t)bk * dm.K + s];
       if (m >= 0 && m < c) {
         if (pos >= first && pos < last) {
+          const float lg = logg ? logg[(size_t)bk * dm.K + s] : 0.0f;
           blist[nb] = m;
-          bbias[nb] = logg ? logg[(size_t)bk * dm.K + s] : 0.0f;
+          bbias[nb] = dm.outer ? 0.0f : lg;
+          bgain[nb] = dm.outer ? expf(lg) : 1.0f;
           ++nb;
         }
         ++pos;
@@ -161,6 +164,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
     if (pos >= first && pos < last) {
       blist[nb] = c;
       bbias[nb] = 0.0f;
+      bgain[nb] = 1.0f;
       ++nb;
     }
     nb_sh = nb;
@@ -251,7 +255,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {
         if (h < G) {
-          const float pz = sc[h][kk];
+          const float pz = sc[h][kk] * bgain[kk / BS];
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[h][e] += pz * vr[i].get(e);
         }
@@ -368,7 +372,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 struct SelectChunks {
   const uint64_t* cand;  // [b*hkv][nchunk][K] descending composite keys
   const float2* stats;   // [b*hkv][nchunk] (max, sum of exp) of the chunk's scores
-  int nchunk, C, gated;
+  int nchunk, C, gated, act;
   int32_t* idx_out;  // optional [b*hkv][K]
   float* logg_out;   // optional [b*hkv][K]
   float* lse_out;    // optional [b*hkv]
@@ -448,10 +452,11 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       int rank = 0;
       for (int q2 = 0; q2 < kk; ++q2) rank += widx[q2] < mine;
       sidx[rank] = mine;
-      slg[rank] = wval[tid] - lse_s;
+      const float lg = gate_log(wval[tid], lse_s, sel.act);
+      slg[rank] = lg;
       if (split == 0 && sel.idx_out) {
         sel.idx_out[(size_t)bk * K + rank] = mine;
-        sel.logg_out[(size_t)bk * K + rank] = wval[tid] - lse_s;
+        sel.logg_out[(size_t)bk * K + rank] = lg;
       }
     }
     if (split == 0 && sel.idx_out) {
@@ -482,6 +487,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     } else if (j == nvalid) {
       m = c;
     }
+  }
+  // Outer gating: the logits carry no bias and the block's P V is scaled by g.
+  float gain = 1.0f;
+  if (dm.outer) {
+    gain = expf(bias);
+    bias = 0.0f;
   }
   float mh[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -597,7 +608,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   // The wave's partial into LDS (an empty wave contributes max -inf, sum 0).
 #pragma unroll
   for (int h = 0; h < G; ++h)
-    *reinterpret_cast<float2*>(&wacc[wave][h][2 * lane]) = make_float2(acc[h][0], acc[h][1]);
+    *reinterpret_cast<float2*>(&wacc[wave][h][2 * lane]) =
+        make_float2(acc[h][0] * gain, acc[h][1] * gain);
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -733,7 +745,8 @@ hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int n
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
-  const SelectChunks sel{cand, stats, nchunk, C, gated ? 1 : 0, idx_out, logg_out, lse_s_out};
+  const SelectChunks sel{cand,         stats,   nchunk,   C,        gated ? 1 : 0,
+                         dm.act,       idx_out, logg_out, lse_s_out};
   {
     ProfScope ps("step_decode_split", st);
 #define SAS_DEC_G(G_)                                                                          \

@@ -19,6 +19,9 @@ struct Dims {
   int b, hq, hkv, g, n, d, bs, T, K;
   float scale;
   bool bf16;
+  int act;     // gate activation: 0 softmax, 1 sigmoid, 2 raw logit
+  bool outer;  // gates applied after the softmax
+  bool ste;    // hard forward, straight-through backward
 };
 
 // ---- selection (select.hip)
@@ -28,15 +31,15 @@ hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, 
 // from qbar / kbar first (written to s_out).
 hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
                        int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
-                       int row_offset, int K, int32_t* idx, float* logg, float* lse_s,
+                       int row_offset, int K, int act, int32_t* idx, float* logg, float* lse_s,
                        hipStream_t st);
 // Rows with more than kLongHistory history blocks use the two-stage path.
 constexpr int kLongHistory = 512;
 size_t select_workspace_bytes(int rows_bk, int T, int C, int K);
 hipError_t launch_select_long(const float* s, const float* qbar, const void* kbar,
                               bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
-                              int T, int C, int row_offset, int K, float* s_out, int32_t* idx,
-                              float* logg, float* lse_s, void* ws, hipStream_t st);
+                              int T, int C, int row_offset, int K, int act, float* s_out,
+                              int32_t* idx, float* logg, float* lse_s, void* ws, hipStream_t st);
 
 // ---- attention, portable fp32-arithmetic kernels (attn_generic.hip)
 hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,

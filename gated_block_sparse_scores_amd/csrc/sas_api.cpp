@@ -115,6 +115,9 @@ sas_status check_shape(const sas_shape* s, bool need_seq = true) {
   if (s->hq % s->hkv != 0) return SAS_ERR_INVALID_ARG;
   if (s->dtype != SAS_DTYPE_F32 && s->dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
   if (!(s->scale >= 0.0f) || isinf(s->scale)) return SAS_ERR_INVALID_ARG;
+  if ((s->gate & ~(SAS_GATE_ACTIVATION_MASK | SAS_GATE_OUTER | SAS_GATE_STE)) != 0 ||
+      (s->gate & SAS_GATE_ACTIVATION_MASK) > SAS_GATE_RAW)
+    return SAS_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return SAS_ERR_UNSUPPORTED;
   if (s->block != 16 && s->block != 32 && s->block != 64) return SAS_ERR_UNSUPPORTED;
   return SAS_OK;
@@ -133,6 +136,9 @@ Dims make_dims(const sas_shape* s, int K) {
   d.K = K;
   d.scale = s->scale > 0.0f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
   d.bf16 = s->dtype == SAS_DTYPE_BF16;
+  d.act = s->gate & SAS_GATE_ACTIVATION_MASK;
+  d.outer = (s->gate & SAS_GATE_OUTER) != 0;
+  d.ste = (s->gate & SAS_GATE_STE) != 0;
   return d;
 }
 
@@ -200,6 +206,8 @@ sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset,
   if (T <= 0 || C < 0 || row_offset < 0 || K <= 0) return SAS_ERR_INVALID_ARG;
   if (!idx || !logg || !lse_s) return SAS_ERR_INVALID_ARG;
   if (K > 64 || C > 16384) return SAS_ERR_UNSUPPORTED;
+  if ((shape->gate & SAS_GATE_ACTIVATION_MASK) > SAS_GATE_RAW) return SAS_ERR_INVALID_ARG;
+  const int act = shape->gate & SAS_GATE_ACTIVATION_MASK;
   const hipStream_t st = (hipStream_t)stream;
   const int rows_bk = shape->batch * shape->hkv;
   double scale = 0.0;
@@ -218,10 +226,10 @@ sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset,
   if (C > sas::kLongHistory)
     return launch_status(sas::launch_select_long(
         s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim, scale, rows_bk, T,
-        C, row_offset, K, s_out, idx, logg, lse_s, workspace, st));
+        C, row_offset, K, act, s_out, idx, logg, lse_s, workspace, st));
   return launch_status(sas::launch_topk(s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                         shape->head_dim, scale, s_out, rows_bk, T, C,
-                                        row_offset, K, idx, logg, lse_s, st));
+                                        row_offset, K, act, idx, logg, lse_s, st));
 }
 
 size_t sas_attn_fwd_workspace_size(const sas_shape* shape, int K) {
@@ -243,9 +251,10 @@ sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void
     return SAS_ERR_INVALID_ARG;
   const Dims dm = make_dims(shape, K);
   const hipStream_t st = (hipStream_t)stream;
+  const float* lg = dm.ste ? nullptr : logg;  // hard gating: the forward is ungated
   if (sas::mfma_fwd_supported(dm))
-    return launch_status(sas::launch_fwd_mfma(dm, q, k, v, idx, logg, o, lse, st));
-  return launch_status(sas::launch_fwd_generic(dm, q, k, v, idx, logg, o, lse, st));
+    return launch_status(sas::launch_fwd_mfma(dm, q, k, v, idx, lg, o, lse, st));
+  return launch_status(sas::launch_fwd_generic(dm, q, k, v, idx, lg, o, lse, st));
 }
 
 size_t sas_attn_bwd_workspace_size(const sas_shape* shape, int K) {
@@ -267,20 +276,22 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SAS_ERR_INVALID_ARG;
-  if (!logg && (dlogg || ds || s || lse_s)) return SAS_ERR_INVALID_ARG;
-  if (ds && (!s || !lse_s)) return SAS_ERR_INVALID_ARG;
   const Dims dm = make_dims(shape, K);
+  // selector outputs need the gates (soft) or at least the selection (ste)
+  if (!logg && !dm.ste && (dlogg || ds || s || lse_s)) return SAS_ERR_INVALID_ARG;
+  if (ds && (!s || (!lse_s && dm.act == SAS_GATE_SOFTMAX))) return SAS_ERR_INVALID_ARG;
   const sas::BwdWorkspace ws = sas::bwd_workspace_layout(dm, workspace);
   if (!workspace || ws_bytes < ws.bytes) return SAS_ERR_WORKSPACE;
   const hipStream_t st = (hipStream_t)stream;
   const bool mfma = sas::mfma_bwd_supported(dm);
+  const float* lg = dm.ste ? nullptr : logg;  // hard gating: the attention is ungated
   SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, !mfma, st));
   int nchunk = 0;
   if (mfma)
-    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, logg, dq, dk, dv, ws,
+    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, lg, dq, dk, dv, ws,
                                     &nchunk, st));
   else
-    SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, logg, dq, dk, dv, ws,
+    SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, lg, dq, dk, dv, ws,
                                        &nchunk, st));
   if (dlogg || ds)
     SAS_LAUNCH(sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, nchunk, dlogg, ds, st));
@@ -309,7 +320,8 @@ sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* 
   const Dims dm = make_dims(shape, K);
   const size_t need = sas::decode_workspace_bytes(dm);
   if (!workspace || ws_bytes < need) return SAS_ERR_WORKSPACE;
-  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx, logg, o, lse,
+  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx,
+                                          dm.ste ? nullptr : logg, o, lse,
                                           workspace, (hipStream_t)stream));
 }
 
@@ -398,7 +410,7 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                                               shape->head_dim, scale, rows, lay.C, K, cand, stats,
                                               st));
     return launch_status(sas::launch_decode_step(dm, L, cl, lay.C, lay.nchunk, q, kcache,
-                                                 vcache, cand, stats, gated != 0, idx, logg,
+                                                 vcache, cand, stats, gated && !dm.ste, idx, logg,
                                                  lse_s, o, lse, ws + lay.part, st));
   }
   // Every other shape: the same three stages through the separate calls' kernels.
@@ -412,14 +424,16 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                                     G, 1, shape->head_dim, shape->block, false, qbar, st));
   if (lay.C > sas::kLongHistory)
     SAS_LAUNCH(sas::launch_select_long(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
-                                       shape->head_dim, scale, rows, 1, lay.C, lay.C, K, s_out,
-                                       idx_w, logg_w, lse_s_w, ws + lay.sel + s_bytes, st));
+                                       shape->head_dim, scale, rows, 1, lay.C, lay.C, K, dm.act,
+                                       s_out, idx_w, logg_w, lse_s_w, ws + lay.sel + s_bytes,
+                                       st));
   else
     SAS_LAUNCH(sas::launch_topk(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
-                                shape->head_dim, scale, s_out, rows, 1, lay.C, lay.C, K, idx_w,
-                                logg_w, lse_s_w, st));
+                                shape->head_dim, scale, s_out, rows, 1, lay.C, lay.C, K, dm.act,
+                                idx_w, logg_w, lse_s_w, st));
   return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx_w,
-                                          gated ? logg_w : nullptr, o, lse, ws + lay.dec, st));
+                                          (gated && !dm.ste) ? logg_w : nullptr, o, lse,
+                                          ws + lay.dec, st));
 }
 
 sas_status sas_selector_bwd(const sas_shape* shape, const float* ds, const float* qbar,

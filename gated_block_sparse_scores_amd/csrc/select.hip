@@ -164,7 +164,8 @@ template <typename Tk, bool STANDIN>
 __global__ void __launch_bounds__(256) topk_kernel(
     const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
     int kbar_ld, int d, double scale, float* __restrict__ s_out, int T, int C, int row_offset,
-    int K, int32_t* __restrict__ idx, float* __restrict__ logg, float* __restrict__ lse_s) {
+    int K, int act, int32_t* __restrict__ idx, float* __restrict__ logg,
+    float* __restrict__ lse_s) {
   extern __shared__ uint32_t keys[];  // C keys (then, with STANDIN, C scores)
   __shared__ int hist[256];
   __shared__ int iscr[16];
@@ -286,7 +287,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
       e += eq;
       if (sel) {
         irow[pos] = m;
-        lrow[pos] = srow[m] - lse;
+        lrow[pos] = gate_log(srow[m], lse, act);
         ++pos;
       }
     }
@@ -402,8 +403,8 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
 
 __global__ void __launch_bounds__(256) select_merge_kernel(
     const uint64_t* __restrict__ cand, const float2* __restrict__ stats, int T, int C,
-    int row_offset, int K, int nchunk, int32_t* __restrict__ idx, float* __restrict__ logg,
-    float* __restrict__ lse_s) {
+    int row_offset, int K, int nchunk, int act, int32_t* __restrict__ idx,
+    float* __restrict__ logg, float* __restrict__ lse_s) {
   extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
   __shared__ int widx[64];
   __shared__ float wval[64];
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
     int rank = 0;
     for (int j = 0; j < kk; ++j) rank += widx[j] < mine;
     irow[rank] = mine;
-    lrow[rank] = wval[threadIdx.x] - lse;
+    lrow[rank] = gate_log(wval[threadIdx.x], lse, act);
   }
   for (int p = kk + threadIdx.x; p < K; p += blockDim.x) {
     irow[p] = -1;
@@ -477,8 +478,9 @@ size_t select_workspace_bytes(int rows_bk, int T, int C, int K) {
 
 hipError_t launch_select_long(const float* s, const float* qbar, const void* kbar,
                               bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
-                              int T, int C, int row_offset, int K, float* s_out, int32_t* idx,
-                              float* logg, float* lse_s, void* ws, hipStream_t st) {
+                              int T, int C, int row_offset, int K, int act, float* s_out,
+                              int32_t* idx, float* logg, float* lse_s, void* ws,
+                              hipStream_t st) {
   const size_t rows = (size_t)rows_bk * T;
   const int nchunk = (C + kChunk - 1) / kChunk;
   uint64_t* cand = (uint64_t*)ws;
@@ -502,7 +504,7 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
     ProfScope ps("select_merge", st);
     hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256),
                        (size_t)2 * nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
-                       K, nchunk, idx, logg, lse_s);
+                       K, nchunk, act, idx, logg, lse_s);
   }
   return hipGetLastError();
 }
@@ -528,23 +530,23 @@ hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kb
 
 hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
                        int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
-                       int row_offset, int K, int32_t* idx, float* logg, float* lse_s,
-                       hipStream_t st) {
+                       int row_offset, int K, int act, int32_t* idx, float* logg,
+                       float* lse_s, hipStream_t st) {
   const size_t rows = (size_t)rows_bk * T;
   const size_t lds = (size_t)(C > 0 ? C : 1) * sizeof(uint32_t) * (s ? 1 : 2);
   ProfScope ps("topk", st);
   if (s)
     hipLaunchKernelGGL((topk_kernel<float, false>), dim3((unsigned)rows), dim3(256), lds, st, s,
-                       nullptr, nullptr, 0, 0, 0.0, nullptr, T, C, row_offset, K, idx, logg,
+                       nullptr, nullptr, 0, 0, 0.0, nullptr, T, C, row_offset, K, act, idx, logg,
                        lse_s);
   else if (kbar_bf16)
     hipLaunchKernelGGL((topk_kernel<bf16_t, true>), dim3((unsigned)rows), dim3(256), lds, st,
                        nullptr, qbar, (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, idx, logg, lse_s);
+                       row_offset, K, act, idx, logg, lse_s);
   else
     hipLaunchKernelGGL((topk_kernel<float, true>), dim3((unsigned)rows), dim3(256), lds, st,
                        nullptr, qbar, (const float*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, idx, logg, lse_s);
+                       row_offset, K, act, idx, logg, lse_s);
   return hipGetLastError();
 }
 

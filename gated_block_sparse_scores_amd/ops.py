@@ -23,16 +23,17 @@ def _f32(shape, dev):
 
 
 def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, scale: float = 0.0,
-             seqlen: Optional[int] = None) -> Shape:
+             seqlen: Optional[int] = None, gate: int = 0) -> Shape:
     """Shape of a training call (q [b,hq,N,d], k [b,hkv,N,d]) or, with q of
-    rank 3, of a decode call (seqlen = valid cache length)."""
+    rank 3, of a decode call (seqlen = valid cache length); gate = sas_gate
+    bits (_lib.gate_code)."""
     if q.dim() == 4:
         b, hq, n, d = q.shape
     else:
         b, hq, d = q.shape
         n = seqlen
     return Shape(b, hq, k.shape[1], n if seqlen is None else seqlen, d, block,
-                 L.dtype_code(q.dtype), scale)
+                 L.dtype_code(q.dtype), scale, gate)
 
 
 def block_pool(x: torch.Tensor, block: int, group: int = 1,
@@ -50,7 +51,8 @@ def block_pool(x: torch.Tensor, block: int, group: int = 1,
 def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int = 0,
                 s: Optional[torch.Tensor] = None, qbar: Optional[torch.Tensor] = None,
                 kbar: Optional[torch.Tensor] = None, head_dim: int = 0, scale: float = 0.0,
-                stream=None, device=None, workspace: Optional[torch.Tensor] = None):
+                stream=None, device=None, workspace: Optional[torch.Tensor] = None,
+                gate: int = 0):
     """Returns (idx, logg, lse_s, s_used).  With s None the stand-in score from
     qbar/kbar is formed on the device and returned as s_used."""
     dev = device or (s.device if s is not None else qbar.device)
@@ -64,7 +66,7 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
         kdt = L.dtype_code(kbar.dtype)
         kld = kbar.shape[2]
         head_dim = qbar.shape[-1]
-    sh = Shape(batch, hkv, hkv, 1, head_dim or 1, 1, L.SAS_DTYPE_F32, scale)
+    sh = Shape(batch, hkv, hkv, 1, head_dim or 1, 1, L.SAS_DTYPE_F32, scale, gate)
     ws_n = L.sas_select_topk_workspace_size(sh, T, C, K)
     if ws_n and (workspace is None or workspace.numel() < ws_n):
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
@@ -73,8 +75,8 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
     return idx, logg, lse_s, (s if s is not None else s_out)
 
 
-def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None):
-    sh = shape_of(q, k, block, scale)
+def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None, gate: int = 0):
+    sh = shape_of(q, k, block, scale, gate=gate)
     K = idx.shape[-1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:3], q.device)
@@ -85,13 +87,15 @@ def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None):
 
 
 def attn_bwd(q, k, v, o, dout, lse, idx, logg, s, lse_s, block: int, scale: float = 0.0,
-             want_ds: bool = True, stream=None, workspace: Optional[torch.Tensor] = None):
-    sh = shape_of(q, k, block, scale)
+             want_ds: bool = True, stream=None, workspace: Optional[torch.Tensor] = None,
+             gate: int = 0):
+    sh = shape_of(q, k, block, scale, gate=gate)
     K = idx.shape[-1]
     T = idx.shape[2]
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dlogg = _f32(idx.shape, q.device) if logg is not None else None
-    ds = _f32((q.shape[0], k.shape[1], T, T), q.device) if (want_ds and logg is not None) else None
+    selector = logg is not None or bool(gate & L.SAS_GATE_STE)
+    dlogg = _f32(idx.shape, q.device) if selector else None
+    ds = _f32((q.shape[0], k.shape[1], T, T), q.device) if (want_ds and selector) else None
     ws_n = L.sas_attn_bwd_workspace_size(sh, K)
     if workspace is None or workspace.numel() < ws_n:
         workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
@@ -102,9 +106,9 @@ def attn_bwd(q, k, v, o, dout, lse, idx, logg, s, lse_s, block: int, scale: floa
 
 
 def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0,
-           stream=None, workspace: Optional[torch.Tensor] = None):
+           stream=None, workspace: Optional[torch.Tensor] = None, gate: int = 0):
     """q [b,hq,d]; caches [b,hkv,cache_len,d]; idx/logg [b,hkv,K]."""
-    sh = shape_of(q, kcache, block, scale, seqlen=L_)
+    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate)
     K = idx.shape[-1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:2], q.device)
@@ -118,11 +122,11 @@ def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0
 
 def decode_step(q, kbar, kcache, vcache, L_: int, K: int, block: int, gated: bool = True,
                 scale: float = 0.0, with_selection: bool = True, stream=None,
-                workspace: Optional[torch.Tensor] = None):
+                workspace: Optional[torch.Tensor] = None, gate: int = 0):
     """One fused decode step with the stand-in selector: q [b,hq,d]; kbar the
     pooled-key cache [b,hkv,>=C,d]; caches [b,hkv,cache_len,d].  Returns
     (o, lse) or, with with_selection, (o, lse, idx, logg, lse_s)."""
-    sh = shape_of(q, kcache, block, scale, seqlen=L_)
+    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate)
     b, hkv = kcache.shape[0], kcache.shape[1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:2], q.device)

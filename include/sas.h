@@ -64,6 +64,33 @@ typedef enum {
 
 typedef enum { SAS_DTYPE_F32 = 0, SAS_DTYPE_BF16 = 1 } sas_dtype;
 
+/* Gate variants, the ablation axes the pages report (the 'Gradient Analysis'
+ * and Eq. 4 of the picx.dev summary; Table 1 of the alanhou.org and cctest.ai
+ * pages).  sas_shape.gate = one activation | optional flags; 0 is SAS itself
+ * (softmax activation, inner gating, soft gates).
+ *   activation phi of Eq. 4, the log gate of a selected history block m:
+ *     SAS_GATE_SOFTMAX  log g_m = s_m - LSE(s) over the row's history (Eq. 6)
+ *     SAS_GATE_SIGMOID  log g_m = log sigmoid(s_m)
+ *     SAS_GATE_RAW      log g_m = s_m (the raw selector logit)
+ *   SAS_GATE_OUTER  gates applied after the softmax: o = sum_j p_j g_m(j) v_j
+ *                   with p the ungated softmax (the right-hand gradient of Eq. 5);
+ *                   dlogg_m = g_m dL/dg_m = sum over block m of p dO . (g v)
+ *   SAS_GATE_STE    hard gating with a straight-through backward: the attention
+ *                   ignores logg (g = 1 on the selected blocks), dlogg is
+ *                   dL/dg there, and ds applies the soft phi's Jacobian to it.
+ * sas_select_topk reads the activation (logg); sas_attn_fwd / sas_decode read
+ * OUTER and STE; sas_attn_bwd reads all three; sas_decode_step reads the
+ * activation and OUTER.  The bf16 MFMA forward and backward run inner gating
+ * only: with OUTER they run the portable kernels. */
+typedef enum {
+  SAS_GATE_SOFTMAX = 0,
+  SAS_GATE_SIGMOID = 1,
+  SAS_GATE_RAW = 2,
+  SAS_GATE_ACTIVATION_MASK = 3,
+  SAS_GATE_OUTER = 4,
+  SAS_GATE_STE = 8
+} sas_gate;
+
 typedef struct {
   int batch;
   int hq;        /* query heads */
@@ -73,6 +100,7 @@ typedef struct {
   int block;     /* tokens per block */
   sas_dtype dtype;
   float scale;   /* logit scale; 0 selects 1/sqrt(head_dim) */
+  int gate;      /* sas_gate bits; 0 = SAS (softmax, inner, soft) */
 } sas_shape;
 
 /* Human-readable name of a status code (static string). */

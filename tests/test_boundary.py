@@ -184,3 +184,15 @@ def test_selector_bwd_checks():
     assert call(dq=FAKE + 4) == L.SAS_ERR_INVALID_ARG
     assert call(kbar=FAKE + 8) == L.SAS_ERR_INVALID_ARG
     assert call(sh_=shape(head_dim=96)) == L.SAS_ERR_UNSUPPORTED
+
+
+def test_gate_bits_are_validated():
+    for bad in (3, 16, 0x13):
+        assert fwd(shape(gate=bad)) == L.SAS_ERR_INVALID_ARG
+    assert L.gate_code("sigmoid", outer=True, ste=True) == 1 | 4 | 8
+    sh = shape(seqlen=8192, hq=32, hkv=8)
+    n = L.lib().sas_attn_bwd_workspace_size(C.byref(sh), 31)
+    args = [FAKE] * 13
+    args[9] = None   # lse_s: the softmax gate's ds needs it
+    st = L.lib().sas_attn_bwd(C.byref(sh), 31, *args, FAKE, FAKE, FAKE, n, None)
+    assert st == L.SAS_ERR_INVALID_ARG

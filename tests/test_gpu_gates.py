@@ -1,0 +1,123 @@
+"""GPU parity of the gate variants (sas_gate bits: sigmoid and raw-logit
+activations, outer gating, straight-through hard gating) against the oracle:
+selection, forward, backward (dq, dk, dv, dlogg, ds), decode and the fused
+decode step, on the portable fp32 kernels and the bf16 MFMA shapes."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import sas_oracle as O
+from tests._gpu_helpers import GATE_ATOL, max_abs, rel_l2, say, tols
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+VARIANTS = [
+    # act,      outer, ste
+    ("sigmoid", False, False),
+    ("raw", False, False),
+    ("softmax", True, False),
+    ("sigmoid", True, False),
+    ("softmax", False, True),
+    ("raw", False, True),
+]
+SHAPES = [
+    # b, hq, hkv, n,  d,  bs, K, dtype
+    (1, 2, 1, 96, 64, 16, 2, torch.float32),
+    (2, 4, 2, 200, 64, 32, 3, torch.float32),
+    (1, 8, 2, 640, 128, 64, 3, torch.bfloat16),
+]
+
+
+def vid(v):
+    return f"{v[0]}{'-outer' if v[1] else ''}{'-ste' if v[2] else ''}"
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s[:7]) for s in SHAPES])
+@pytest.mark.parametrize("variant", VARIANTS, ids=[vid(v) for v in VARIANTS])
+def test_gate_variant_training(variant, shape):
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    act, outer, ste = variant
+    b, hq, hkv, n, d, bs, K, dtype = shape
+    gate = L.gate_code(act, outer, ste)
+    say(f"gates {vid(variant)} {shape[:7]}")
+    w = synth.workload(1, batch=b, hq=hq, hkv=hkv, seqlen=n, head_dim=d, block=bs, topk=K,
+                       dtype="f32" if dtype == torch.float32 else "bf16")
+    x = synth.train_inputs(w, seed=n + K)
+    T = O.n_blocks(n, bs)
+    s = synth.random_scores((b, hkv, T, T), seed=n + 7)
+    s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
+    xd = {k_: v_.to(DEV) for k_, v_ in x.items() if v_ is not None}
+    sd = s.to(DEV)
+    idx, logg, lse_s, _ = ops.select_topk(b, hkv, T, T, K, s=sd, gate=gate)
+    o, lse = ops.attn_fwd(xd["q"], xd["k"], xd["v"], idx, logg, bs, gate=gate)
+    gr = ops.attn_bwd(xd["q"], xd["k"], xd["v"], o, xd["dout"], lse, idx, logg, sd, lse_s, bs,
+                      gate=gate)
+    torch.cuda.synchronize()
+    # oracle
+    s_np = s.numpy()
+    oi, ol, ols = O.select_topk(s_np, K, act=act)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    assert max_abs(logg.cpu(), ol) <= GATE_ATOL
+    np.testing.assert_allclose(lse_s.cpu().numpy(), ols, rtol=0, atol=GATE_ATOL)  # -inf at t=0
+    oo, olse = O.attn_fwd(x["q"], x["k"], x["v"], oi, None if ste else ol, bs, outer=outer)
+    atol, rtol = tols(dtype)
+    eo, el = max_abs(o.cpu(), oo), max_abs(lse.cpu(), olse)
+    ref = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], oi, ol, s_np, ols, bs, act=act,
+                     outer=outer, ste=ste)
+    errs = {k_: rel_l2(gr[k_].cpu(), ref[k_]) for k_ in ("dq", "dk", "dv", "dlogg", "ds")}
+    say(f"  o {eo:.2e} lse {el:.2e} " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
+    assert eo <= atol and el <= atol
+    for k_, v_ in errs.items():
+        assert v_ <= rtol, k_
+
+
+DECODE_SHAPES = [
+    # b, hq, hkv, L,    d,  bs, K,  dtype
+    (2, 8, 2, 1000, 128, 64, 5, torch.bfloat16),     # MFMA decode / fused step
+    (1, 4, 4, 300, 64, 16, 4, torch.float32),        # portable decode
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[str(s[:7]) for s in DECODE_SHAPES])
+@pytest.mark.parametrize("variant", [v for v in VARIANTS if not v[2]] + [("softmax", True, True)],
+                         ids=[vid(v) for v in VARIANTS if not v[2]] + ["softmax-outer-ste"])
+def test_gate_variant_decode(variant, shape):
+    """sas_decode with the variant's gates, and the fused step (pooled-query
+    selection with the variant's activation) against the oracle."""
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    act, outer, ste = variant
+    b, hq, hkv, Lc, d, bs, K, dtype = shape
+    gate = L.gate_code(act, outer, ste)
+    say(f"decode gates {vid(variant)} {shape[:7]}")
+    w = synth.workload(4, batch=b, hq=hq, hkv=hkv, seqlen=Lc, head_dim=d, block=bs, topk=K,
+                       dtype="f32" if dtype == torch.float32 else "bf16")
+    x = synth.decode_inputs(w, seed=Lc + K)
+    C = (Lc - 1) // bs
+    kbar = torch.from_numpy(O.to_f32(O.pool_keys(x["kcache"][:, :, :C * bs], bs)))
+    kbar = kbar.to(torch.bfloat16)
+    qbar32 = O.to_f32(O.decode_qbar(x["q"], hkv))
+    so = O.standin_scores(qbar32, kbar.float().numpy(), O.default_scale(d), C, row_offset=C)
+    oi, ol, ols = O.select_topk(so, K, row_offset=C, C=C, act=act)
+    lg = None if ste else ol[:, :, 0]
+    oo, olse = O.decode(x["q"], x["kcache"], x["vcache"], Lc, oi[:, :, 0], lg, bs, outer=outer)
+    xd = {k_: v_.to(DEV) for k_, v_ in x.items()}
+    atol, _ = tols(dtype)
+    # decode with the oracle's selection as input
+    o, lse = ops.decode(xd["q"], xd["kcache"], xd["vcache"], Lc,
+                        torch.from_numpy(oi[:, :, 0].astype(np.int32)).to(DEV),
+                        torch.from_numpy(ol[:, :, 0].astype(np.float32)).to(DEV), bs, gate=gate)
+    torch.cuda.synchronize()
+    assert max_abs(o.cpu(), oo) <= atol and max_abs(lse.cpu(), olse) <= atol
+    # the fused step forms the selection itself
+    fo, flse, fidx, flogg, flse_s = ops.decode_step(xd["q"], kbar.to(DEV), xd["kcache"],
+                                                    xd["vcache"], Lc, K, bs, gate=gate)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fidx.cpu().numpy().astype(np.int64), oi[:, :, 0])
+    assert max_abs(flogg.cpu(), ol[:, :, 0]) <= GATE_ATOL
+    eo, el = max_abs(fo.cpu(), oo), max_abs(flse.cpu(), olse)
+    say(f"  decode o {max_abs(o.cpu(), oo):.2e}; step o {eo:.2e} lse {el:.2e}")
+    assert eo <= atol and el <= atol
