@@ -56,20 +56,55 @@ def selected_pairs_device(idx, n, bs, g):
     return (hist + cur) * g
 
 
-def train_step_fn(w, x, ws):
+def train_step_fn(w, x, ws, gate=0, K=None):
     import torch
     from gated_block_sparse_scores_amd import ops
     T = w.nblocks
+    K = w.topk if K is None else K
 
     def step():
         qb = ops.block_pool(x["q"], w.block, w.group)
         kb = ops.block_pool(x["k"], w.block, 1)
-        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, w.topk, qbar=qb, kbar=kb)
-        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block)
+        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, K, qbar=qb, kbar=kb,
+                                              gate=gate)
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block, gate=gate)
         gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s,
-                          w.block, workspace=ws)
+                          w.block, workspace=ws, gate=gate)
         return idx, gr, qb, kb
     return step
+
+
+def bench_gate_variants(args, w, x):
+    """The same training step under each gate variant (sas_shape.gate) and under
+    the dense scope (K = T - 1: every history block selected and gated); a few
+    steps each.  Outer gating runs the portable kernels."""
+    import torch
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    out = {}
+    sh = ops.shape_of(x["q"], x["k"], w.block)
+    for name, gate, K in (("sigmoid", L.gate_code("sigmoid"), w.topk),
+                          ("raw-logit", L.gate_code("raw"), w.topk),
+                          ("ste", L.gate_code("softmax", ste=True), w.topk),
+                          ("outer", L.gate_code("softmax", outer=True), w.topk),
+                          ("dense-scope", 0, w.nblocks - 1)):
+        ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, K), dtype=torch.uint8,
+                         device=x["q"].device)
+        step = train_step_fn(w, x, ws, gate=gate, K=K)
+        idx, _, _, _ = step()
+        torch.cuda.synchronize()
+        pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
+        steps = 3
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out[name] = {"gate": gate, "topk": K, "ms_per_step": round(ms, 3),
+                     "TFLOPs": round(12 * w.head_dim * pairs / (ms * 1e-3) / 1e12, 2),
+                     "selected_pairs": int(pairs)}
+        del ws
+    return out
 
 
 def kernel_flops(name, pairs, d):
@@ -158,18 +193,28 @@ def bench_train(args):
     pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
     flops = 12 * w.head_dim * pairs
 
-    L.sas_profiler_reset()
-    L.sas_profiler_enable(True)
+    # Step time with nothing but the step on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    L.sas_profiler_enable(False)
-    kt = L.sas_profiler_read()
     ms = (t1 - t0) * 1e3 / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
+    # Kernel durations: the same steps again with a HIP event pair recorded
+    # around every launch on its stream (the events add a little time between
+    # kernels, so this pass is not the step time).
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    L.sas_profiler_enable(False)
+    kt = L.sas_profiler_read()
+    ms_events = (t3 - t2) * 1e3 / args.steps
     # dominant kernel
     name, (n, tot) = max(kt.items(), key=lambda kv: kv[1][1])
     avg_ms = tot / n
@@ -184,7 +229,9 @@ def bench_train(args):
                 "traffic": recorded_traffic(name, w.name), "avg_launch_ms": round(avg_ms, 4)}
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
     return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
-                kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb))
+                ms_with_kernel_events=ms_events,
+                kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb),
+                gate_variants=None if args.no_variants else bench_gate_variants(args, w, x))
 
 
 def bench_selector_bwd(args, w, gr, qb, kb):
@@ -262,19 +309,28 @@ def bench_decode(wl, steps, layers=12):
                                           kbar=kb)
         return ops.decode(q, kc, vc, Lc, idx[:, :, 0], logg[:, :, 0], w.block, workspace=ws)
 
+    def timed(fn, profile):
+        """Wall time per call of the timed calls; with profile, kernel times
+        from HIP events around every launch (a separate pass)."""
+        if profile:
+            L.sas_profiler_reset()
+            L.sas_profiler_enable(True)
+        t0 = time.perf_counter()
+        for c in range(calls):
+            fn(qs[c], c % layers)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kt_ = None
+        if profile:
+            L.sas_profiler_enable(False)
+            kt_ = L.sas_profiler_read()
+        return (t1 - t0) * 1e6 / calls, kt_
+
     for layer in range(layers):               # warm-up: one call per layer
         one(qs[calls + layer], layer)
     torch.cuda.synchronize()
-    L.sas_profiler_reset()
-    L.sas_profiler_enable(True)
-    t0 = time.perf_counter()
-    for c in range(calls):
-        one(qs[c], c % layers)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    L.sas_profiler_enable(False)
-    kt = L.sas_profiler_read()
-    us_step = (t1 - t0) * 1e6 / calls
+    us_step, _ = timed(one, False)
+    _, kt = timed(one, True)
     sel_bytes = w.batch * w.hkv * (w.topk + 1) * w.block * w.head_dim * 2 * 2
     kbar_bytes = w.batch * w.hkv * C * w.head_dim * 2
 
@@ -305,20 +361,13 @@ def bench_decode(wl, steps, layers=12):
     for layer in range(layers):
         one_step(qs[calls + layer], layer)
     torch.cuda.synchronize()
-    L.sas_profiler_reset()
-    L.sas_profiler_enable(True)
-    t0 = time.perf_counter()
-    for c in range(calls):
-        one_step(qs[c], c % layers)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    L.sas_profiler_enable(False)
-    kt2 = L.sas_profiler_read()
+    step_wall_us, _ = timed(one_step, False)
+    _, kt2 = timed(one_step, True)
     step_gpu_us = sum(v[1] / v[0] * 1e3 for v in kt2.values())
     fused = {
         "gpu_us_per_call": round(step_gpu_us, 2),
         "gpu_GBps_per_call": round((sel_bytes + kbar_bytes) / (step_gpu_us * 1e-6) / 1e9, 1),
-        "wall_us_per_call": round((t1 - t0) * 1e6 / calls, 2),
+        "wall_us_per_call": round(step_wall_us, 2),
         "kernels": {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)}
                     for k, v in kt2.items()},
     }
@@ -394,6 +443,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the gate-variant and dense-scope training steps")
     ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
     ap.add_argument("--decode-workloads", default="4,5")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -432,7 +483,9 @@ def main():
             "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
             "roofline": res["roofline"],
             "kernels": res["kernels"],
+            "ms_per_step_with_kernel_events": round(res["ms_with_kernel_events"], 4),
             "selector_bwd": res["selector_bwd"],
+            "gate_variants": res["gate_variants"],
         })
     if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")

@@ -134,8 +134,8 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
   constexpr int KC = BS < 32 ? BS : 32;
   __shared__ __align__(16) float Ks[KC][D];
   __shared__ __align__(16) float Vs[KC][D];
-  __shared__ int blist[65], bslot[65];
-  __shared__ float bbias[65];
+  __shared__ int blist[kMaxTrainK + 1], bslot[kMaxTrainK + 1];
+  __shared__ float bbias[kMaxTrainK + 1];
   __shared__ int nblk;
 
   int b, kv, t, chunk;
@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
   constexpr int KC = BS < 32 ? BS : 32;
   __shared__ __align__(16) float Ks[KC][D];
   __shared__ __align__(16) float Vs[KC][D];
-  __shared__ int blist[65], bslot[65];
-  __shared__ float bbias[65];
+  __shared__ int blist[kMaxTrainK + 1], bslot[kMaxTrainK + 1];
+  __shared__ float bbias[kMaxTrainK + 1];
   __shared__ float fscr[16];
   __shared__ int nblk;
 
@@ -318,10 +318,10 @@ __global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
   const T* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const int nb = nblk;
   // slots without a valid block get 0
-  if (threadIdx.x < dm.K) {
+  for (int sl = threadIdx.x; sl < dm.K; sl += blockDim.x) {
     bool used = false;
-    for (int bi = 0; bi + 1 < nb; ++bi) used |= bslot[bi] == (int)threadIdx.x;
-    if (!used) dpart[threadIdx.x] = 0.0f;
+    for (int bi = 0; bi + 1 < nb; ++bi) used |= bslot[bi] == sl;
+    if (!used) dpart[sl] = 0.0f;
   }
   for (int bi = 0; bi < nb; ++bi) {
     const int m = blist[bi];
@@ -473,8 +473,8 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(
     int T, int K, int act, int ste, const int32_t* __restrict__ idx, const float* __restrict__ s,
     const float* __restrict__ lse_s, const float* __restrict__ dlogg_part, int nchunk,
     float* __restrict__ dlogg, float* __restrict__ ds) {
-  __shared__ float dl[64];
-  __shared__ int im[64];
+  __shared__ float dl[kMaxTrainK];
+  __shared__ int im[kMaxTrainK];
   __shared__ float tot;
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);

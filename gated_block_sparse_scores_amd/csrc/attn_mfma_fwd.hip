@@ -59,8 +59,8 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   __shared__ __align__(16) bf16_t V0[BS * TILE_LD];
   __shared__ __align__(16) bf16_t K1[BS * TILE_LD];
   __shared__ __align__(16) bf16_t V1[BS * TILE_LD];
-  __shared__ int blist[65];
-  __shared__ float bbias[65];
+  __shared__ int blist[kMaxTrainK + 1];
+  __shared__ float bbias[kMaxTrainK + 1];
   __shared__ int nblk;
 
   const int nchunk = dm.g / HPW;

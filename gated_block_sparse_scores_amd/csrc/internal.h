@@ -33,6 +33,10 @@ hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool
                        int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
                        int row_offset, int K, int act, int32_t* idx, float* logg, float* lse_s,
                        hipStream_t st);
+// Largest Top-K of the training path (selection with C <= kLongHistory, forward,
+// backward): slots are stored as uint8 in the inverse map, 0xFE and 0xFF being
+// markers.  Decode and the two-stage selection take K <= 64.
+constexpr int kMaxTrainK = 254;
 // Rows with more than kLongHistory history blocks use the two-stage path.
 constexpr int kLongHistory = 512;
 size_t select_workspace_bytes(int rows_bk, int T, int C, int K);

@@ -191,8 +191,8 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
 }
 
 size_t sas_select_topk_workspace_size(const sas_shape* shape, int T, int C, int K) {
-  if (!shape || shape->batch <= 0 || shape->hkv <= 0 || T <= 0 || C < 0 || K <= 0 || K > 64 ||
-      C > 16384)
+  if (!shape || shape->batch <= 0 || shape->hkv <= 0 || T <= 0 || C < 0 || K <= 0 ||
+      K > sas::kMaxTrainK || C > 16384 || (C > sas::kLongHistory && K > 64))
     return 0;
   return sas::select_workspace_bytes(shape->batch * shape->hkv, T, C, K);
 }
@@ -205,7 +205,8 @@ sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset,
   if (!shape || shape->batch <= 0 || shape->hkv <= 0) return SAS_ERR_INVALID_ARG;
   if (T <= 0 || C < 0 || row_offset < 0 || K <= 0) return SAS_ERR_INVALID_ARG;
   if (!idx || !logg || !lse_s) return SAS_ERR_INVALID_ARG;
-  if (K > 64 || C > 16384) return SAS_ERR_UNSUPPORTED;
+  if (K > sas::kMaxTrainK || C > 16384 || (C > sas::kLongHistory && K > 64))
+    return SAS_ERR_UNSUPPORTED;
   if ((shape->gate & SAS_GATE_ACTIVATION_MASK) > SAS_GATE_RAW) return SAS_ERR_INVALID_ARG;
   const int act = shape->gate & SAS_GATE_ACTIVATION_MASK;
   const hipStream_t st = (hipStream_t)stream;
@@ -245,7 +246,7 @@ sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void
   (void)ws_bytes;
   SAS_TRY(check_shape(shape));
   if (K <= 0) return SAS_ERR_INVALID_ARG;
-  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  if (K > sas::kMaxTrainK) return SAS_ERR_UNSUPPORTED;
   if (!q || !k || !v || !idx || !o || !lse) return SAS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return SAS_ERR_INVALID_ARG;
@@ -258,7 +259,7 @@ sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void
 }
 
 size_t sas_attn_bwd_workspace_size(const sas_shape* shape, int K) {
-  if (check_shape(shape) != SAS_OK || K <= 0 || K > 64) return 0;
+  if (check_shape(shape) != SAS_OK || K <= 0 || K > sas::kMaxTrainK) return 0;
   const Dims dm = make_dims(shape, K);
   return sas::bwd_workspace_layout(dm, nullptr).bytes;
 }
@@ -270,7 +271,7 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
                         float* ds, void* workspace, size_t ws_bytes, void* stream) {
   SAS_TRY(check_shape(shape));
   if (K <= 0) return SAS_ERR_INVALID_ARG;
-  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  if (K > sas::kMaxTrainK) return SAS_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !dout || !lse || !idx || !dq || !dk || !dv)
     return SAS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||

@@ -39,8 +39,12 @@
  *     can never make a kernel read outside the tensors).
  *   - Supported: head_dim in {64, 128}; block in {16, 32, 64}; dtype fp32
  *     (all tensors fp32) or bf16 (q, k, v, o, dout, dq, dk, dv bf16; scores,
- *     gates, LSE, ds fp32); 1 <= K <= 64; hq a multiple of hkv.  Anything
- *     else returns SAS_ERR_UNSUPPORTED.
+ *     gates, LSE, ds fp32); hq a multiple of hkv; 1 <= K <= 254 for the
+ *     training calls (sas_select_topk with C <= 512, sas_attn_fwd,
+ *     sas_attn_bwd), so that K >= C_t -- every history block selected and
+ *     gated, the dense scope of the pages' ablations -- is expressible for
+ *     up to 255 blocks; 1 <= K <= 64 for sas_select_topk with C > 512 and the
+ *     decode calls.  Anything else returns SAS_ERR_UNSUPPORTED.
  *   - Calls are thread-safe.  Calls that share output buffers must not
  *     overlap.
  */

@@ -70,7 +70,7 @@ def test_fwd_rejects_null_and_misaligned_pointers_and_bad_K():
         assert fwd(sh, **{name: None}) == L.SAS_ERR_INVALID_ARG
     assert fwd(sh, q=FAKE + 2) == L.SAS_ERR_INVALID_ARG
     assert fwd(sh, K=0) == L.SAS_ERR_INVALID_ARG
-    assert fwd(sh, K=65) == L.SAS_ERR_UNSUPPORTED
+    assert fwd(sh, K=255) == L.SAS_ERR_UNSUPPORTED     # training calls take K <= 254
 
 
 def test_bwd_workspace_query_and_checks():
@@ -117,6 +117,12 @@ def test_select_checks():
                                                                             31) == 0
     assert lib.sas_select_topk(C.byref(sh), 1, 8191, 8191, 31, FAKE, None, None, 0, 0, None,
                                FAKE, FAKE, FAKE, None, 0, None) == L.SAS_ERR_WORKSPACE
+    # K > 64 only for histories of at most 512 blocks (the one-pass selection)
+    assert lib.sas_select_topk(C.byref(sh), 1, 600, 600, 65, FAKE, None, None, 0, 0, None,
+                               FAKE, FAKE, FAKE, None, 0, None) == L.SAS_ERR_UNSUPPORTED
+    assert lib.sas_select_topk(C.byref(sh), 4, 4, 0, 255, FAKE, None, None, 0, 0, None,
+                               FAKE, FAKE, FAKE, None, 0, None) == L.SAS_ERR_UNSUPPORTED
+    assert lib.sas_select_topk_workspace_size(C.byref(sh), 1, 600, 65) == 0
 
 
 def test_decode_checks():

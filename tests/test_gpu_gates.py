@@ -121,3 +121,47 @@ def test_gate_variant_decode(variant, shape):
     eo, el = max_abs(fo.cpu(), oo), max_abs(flse.cpu(), olse)
     say(f"  decode o {max_abs(o.cpu(), oo):.2e}; step o {eo:.2e} lse {el:.2e}")
     assert eo <= atol and el <= atol
+
+
+DENSE_SHAPES = [
+    # b, hq, hkv, n,    d,  bs, K,   dtype         (K >= every row's history)
+    (1, 2, 1, 160, 64, 16, 12, torch.float32),
+    (1, 8, 2, 1024, 128, 64, 15, torch.bfloat16),
+    (1, 8, 2, 4096, 128, 64, 70, torch.bfloat16),     # K > 64: 64 history blocks + pads
+    (1, 4, 1, 8192, 128, 64, 127, torch.bfloat16),    # 8K tokens, all 127 history blocks
+]
+
+
+@pytest.mark.parametrize("shape", DENSE_SHAPES, ids=[str(s[:7]) for s in DENSE_SHAPES])
+def test_dense_scope(shape):
+    """Dense scope: K >= C_t, so every history block is selected and gated (the
+    sparse-versus-dense scope axis of the ablations); selection, forward and
+    backward against the oracle."""
+    from gated_block_sparse_scores_amd import ops
+    b, hq, hkv, n, d, bs, K, dtype = shape
+    say(f"dense scope {shape[:7]}")
+    w = synth.workload(1, batch=b, hq=hq, hkv=hkv, seqlen=n, head_dim=d, block=bs, topk=K,
+                       dtype="f32" if dtype == torch.float32 else "bf16")
+    x = synth.train_inputs(w, seed=K)
+    T = O.n_blocks(n, bs)
+    s = synth.random_scores((b, hkv, T, T), seed=K + 1)
+    s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
+    xd = {k_: v_.to(DEV) for k_, v_ in x.items() if v_ is not None}
+    sd = s.to(DEV)
+    idx, logg, lse_s, _ = ops.select_topk(b, hkv, T, T, K, s=sd)
+    o, lse = ops.attn_fwd(xd["q"], xd["k"], xd["v"], idx, logg, bs)
+    gr = ops.attn_bwd(xd["q"], xd["k"], xd["v"], o, xd["dout"], lse, idx, logg, sd, lse_s, bs)
+    torch.cuda.synchronize()
+    oi, ol, ols = O.select_topk(s.numpy(), K)
+    assert all((oi[0, :, t] >= 0).sum(-1).min() == t for t in range(T))   # all history
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    assert max_abs(logg.cpu(), ol) <= GATE_ATOL
+    oo, olse = O.attn_fwd(x["q"], x["k"], x["v"], oi, ol, bs)
+    atol, rtol = tols(dtype)
+    eo, el = max_abs(o.cpu(), oo), max_abs(lse.cpu(), olse)
+    ref = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], oi, ol, s.numpy(), ols, bs)
+    errs = {k_: rel_l2(gr[k_].cpu(), ref[k_]) for k_ in ("dq", "dk", "dv", "dlogg", "ds")}
+    say(f"  o {eo:.2e} lse {el:.2e} " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
+    assert eo <= atol and el <= atol
+    for k_, v_ in errs.items():
+        assert v_ <= rtol, k_
