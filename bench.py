@@ -440,7 +440,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the first few tens of milliseconds on a fresh GPU run slower (clocks
+    # ramping); 25 untimed steps of the 8K workload cover about 40 ms
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true",

@@ -27,6 +27,9 @@
 //    four waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
 //    selected block and accumulating dQ^T += K^T dS^T, with K and V staged
 //    row-major in LDS (K^T read with ds_read_b64_tr_b16).
+// With OUTER (gates applied after the softmax, the right-hand gradient of
+// Eq. 5) the logits carry no bias, dP = g dO . v, dV takes g P, and the gate
+// gradient of a block is the sum of P dP instead of dS.
 #include <math.h>
 
 #include "common.h"
@@ -55,6 +58,7 @@ constexpr int DKV_MAXT = 4096;  // longest inverse list (query blocks) held in L
 // owns its part of dK and dV outright, with no reduction at the end.  The next
 // item's q / dout rows, LSE, D and log gate are copied global -> LDS (direct-to-
 // LDS loads) once every wave is done with the current tiles.
+template <bool OUTER>
 __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
@@ -151,7 +155,8 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     const int t = (int)(ent & 0xFFFF);
     const int slot = (int)(ent >> 16);
     const bool diag = t == m;
-    const float bias2 = cur_bias * LOG2E;
+    const float bias2 = OUTER ? 0.0f : cur_bias * LOG2E;
+    const float gain = OUTER ? expf(cur_bias) : 1.0f;
 
     // S[q][key], dP[q][key] for this wave's 32 query rows and 32 keys.
     f32x16 sa, pa;
@@ -168,10 +173,11 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
       const int qi = qh * 32 + acc_row(r, g);
       float p = fast_exp2(fmaf(sa[r], sc2, bias2) - Ls[qi] * LOG2E);
       if (diag && key > qi) p = 0.0f;
-      const float ds = p * (pa[r] - Dl[qi]);
-      sa[r] = p;
+      const float dp = OUTER ? pa[r] * gain : pa[r];
+      const float ds = p * (dp - Dl[qi]);
+      sa[r] = OUTER ? p * gain : p;
       pa[r] = ds;
-      dlsum += ds;
+      dlsum += OUTER ? p * dp : ds;
     }
     const bf16x8 p0 = pack8(sa, 0), p1 = pack8(sa, 8);
     const bf16x8 d0 = pack8(pa, 0), d1 = pack8(pa, 8);
@@ -241,6 +247,7 @@ constexpr int HPW = 2;   // heads per dQ workgroup
 constexpr int DQ_NW = 4;  // waves: two 32-row halves per head
 constexpr int DQ_NT = 64 * DQ_NW;
 
+template <bool OUTER>
 __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
@@ -278,13 +285,14 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     for (int s = 0; s < dm.K; ++s) {
       const int mm = ir[s];
       if (mm >= 0 && mm < t) {
+        const float lg = logg ? logg[rowbk * dm.K + s] : 0.0f;
         blist[cnt] = mm;
-        bbias[cnt] = logg ? logg[rowbk * dm.K + s] * LOG2E : 0.0f;
+        bbias[cnt] = OUTER ? expf(lg) : lg * LOG2E;  // gate (OUTER) or log2 gate
         ++cnt;
       }
     }
     blist[cnt] = t;
-    bbias[cnt] = 0.0f;
+    bbias[cnt] = OUTER ? 1.0f : 0.0f;
     nblk = cnt + 1;
   }
 
@@ -325,7 +333,8 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
   auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
     const int m = blist[bi];
-    const float off2 = bbias[bi] - l2;
+    const float off2 = (OUTER ? 0.0f : bbias[bi]) - l2;
+    const float gain = OUTER ? bbias[bi] : 1.0f;
     const bool diag = m == t;
     if (bi + 1 < nb) {
       tile_load_lds<DQ_NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
@@ -349,7 +358,7 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(sa[r], sc2, off2));
         if (diag && kt * 32 + acc_row(r, g) > qi) p = 0.0f;
-        pa[r] = p * (pa[r] - dval);
+        pa[r] = p * ((OUTER ? pa[r] * gain : pa[r]) - dval);
       }
       db[2 * kt] = pack8(pa, 0);
       db[2 * kt + 1] = pack8(pa, 8);
@@ -384,10 +393,9 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
 
 }  // namespace
 
-// Inner gating only (outer gating runs the portable kernels).
 bool mfma_bwd_supported(const Dims& dm) {
   return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
-         dm.T <= DKV_MAXT && !dm.outer;
+         dm.T <= DKV_MAXT;
 }
 
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
@@ -400,8 +408,9 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
     // dQ first: it also forms D = rowsum(dO o), which dK / dV reads.
     const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
     ProfScope ps("bwd_dq_mfma", st);
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
+    auto kern = dm.outer ? bwd_dq_mfma_kernel<true> : bwd_dq_mfma_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
                        (const bf16_t*)dout, lse, ws.D, idx, logg, (bf16_t*)dq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -409,10 +418,10 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
   {
     const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
     ProfScope ps("bwd_dkdv_mfma", st);
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                       (const bf16_t*)dout, lse, ws.D, logg, ws.slotmap, (bf16_t*)dk,
-                       (bf16_t*)dv, ws.dlogg_part);
+    auto kern = dm.outer ? bwd_dkdv_mfma_kernel<true> : bwd_dkdv_mfma_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout, lse, ws.D, logg,
+                       ws.slotmap, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part);
   }
   return hipGetLastError();
 }

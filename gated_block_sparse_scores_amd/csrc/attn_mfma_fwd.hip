@@ -25,6 +25,8 @@
 // running max is a reference that is only moved (and O, l rescaled) when a
 // block's max exceeds it by more than 2^8; the final normalisation uses the
 // same reference, so the result is unchanged.
+// With OUTER (gates applied after the softmax) the logits carry no bias and P
+// is scaled by the block's gate g after the row sum, before the P V product.
 // Workgroups are issued longest-row-first (query block descending), KV head
 // fastest, so consecutive workgroups (spread over the 8 XCDs) share K/V.
 #include <math.h>
@@ -47,6 +49,7 @@ constexpr int HPW = 2;   // heads per workgroup
 constexpr int NW = 4;    // waves per workgroup (two 32-row halves per head)
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
+template <bool OUTER>
 __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -60,7 +63,7 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   __shared__ __align__(16) bf16_t K1[BS * TILE_LD];
   __shared__ __align__(16) bf16_t V1[BS * TILE_LD];
   __shared__ int blist[kMaxTrainK + 1];
-  __shared__ float bbias[kMaxTrainK + 1];
+  __shared__ float bbias[kMaxTrainK + 1];  // log2 gate (inner) or gate (OUTER)
   __shared__ int nblk;
 
   const int nchunk = dm.g / HPW;
@@ -83,13 +86,14 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     for (int s = 0; s < dm.K; ++s) {
       const int m = ir[s];
       if (m >= 0 && m < t) {
+        const float lg = logg ? logg[rowbk * dm.K + s] : 0.0f;
         blist[cnt] = m;
-        bbias[cnt] = logg ? logg[rowbk * dm.K + s] * LOG2E : 0.0f;
+        bbias[cnt] = OUTER ? expf(lg) : lg * LOG2E;
         ++cnt;
       }
     }
     blist[cnt] = t;
-    bbias[cnt] = 0.0f;
+    bbias[cnt] = OUTER ? 1.0f : 0.0f;
     nblk = cnt + 1;
   }
 
@@ -122,7 +126,7 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
   auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
     const int m = blist[bi];
-    const float bias2 = bbias[bi];
+    const float bias2 = OUTER ? 0.0f : bbias[bi];
     const bool diag = m == t;
     if (bi + 1 < nb) {
       tile_load_lds<NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
@@ -172,7 +176,7 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(sacc[kt][r], sc2, off2));
-        sacc[kt][r] = p;
+        sacc[kt][r] = OUTER ? p * bbias[bi] : p;
         lsum += p;
       }
 
@@ -212,10 +216,8 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
 
 }  // namespace
 
-// Inner gating only (outer gating runs the portable kernel).
 bool mfma_fwd_supported(const Dims& dm) {
-  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
-         !dm.outer;
+  return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0;
 }
 
 hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
@@ -223,9 +225,14 @@ hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const v
                            hipStream_t st) {
   const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
   ProfScope ps("fwd_mfma", st);
-  hipLaunchKernelGGL(fwd_mfma_kernel, dim3((unsigned)tiles), dim3(64 * NW), 0, st, dm,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
-                     (bf16_t*)o, lse);
+  if (dm.outer)
+    hipLaunchKernelGGL(fwd_mfma_kernel<true>, dim3((unsigned)tiles), dim3(64 * NW), 0, st, dm,
+                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
+                       (bf16_t*)o, lse);
+  else
+    hipLaunchKernelGGL(fwd_mfma_kernel<false>, dim3((unsigned)tiles), dim3(64 * NW), 0, st, dm,
+                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, idx, logg,
+                       (bf16_t*)o, lse);
   return hipGetLastError();
 }
 

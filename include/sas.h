@@ -84,8 +84,8 @@ typedef enum { SAS_DTYPE_F32 = 0, SAS_DTYPE_BF16 = 1 } sas_dtype;
  *                   dL/dg there, and ds applies the soft phi's Jacobian to it.
  * sas_select_topk reads the activation (logg); sas_attn_fwd / sas_decode read
  * OUTER and STE; sas_attn_bwd reads all three; sas_decode_step reads the
- * activation and OUTER.  The bf16 MFMA forward and backward run inner gating
- * only: with OUTER they run the portable kernels. */
+ * activation and OUTER.  Every kernel (bf16 MFMA and portable) runs both
+ * inner and outer gating. */
 typedef enum {
   SAS_GATE_SOFTMAX = 0,
   SAS_GATE_SIGMOID = 1,
