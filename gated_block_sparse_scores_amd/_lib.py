@@ -33,7 +33,8 @@ EXPORTED = [
     "sas_select_topk",
     "sas_attn_fwd_workspace_size", "sas_attn_fwd", "sas_attn_bwd_workspace_size",
     "sas_attn_bwd", "sas_decode_workspace_size", "sas_decode", "sas_decode_step_workspace_size",
-    "sas_decode_step", "sas_selector_bwd", "sas_profiler_enable",
+    "sas_decode_step", "sas_decode_paged", "sas_decode_step_paged", "sas_selector_bwd",
+    "sas_profiler_enable",
     "sas_profiler_reset", "sas_profiler_read",
 ]
 
@@ -103,6 +104,10 @@ def lib():
     L.sas_decode_workspace_size.restype = C.c_size_t
     L.sas_decode.argtypes = [sp, C.c_int, C.c_int, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.sas_selector_bwd.argtypes = [sp, P, P, P, P, P, P, P, P]
+    L.sas_decode_paged.argtypes = [sp, C.c_int, P, P, P, C.c_int, P, C.c_int, P, P, P, P, P, P,
+                                   C.c_size_t, P]
+    L.sas_decode_step_paged.argtypes = [sp, C.c_int, P, P, C.c_int, C.c_int, P, P, C.c_int, P,
+                                        C.c_int, P, C.c_int, P, P, P, P, P, P, C.c_size_t, P]
     L.sas_decode_step_workspace_size.argtypes = [sp, C.c_int]
     L.sas_decode_step_workspace_size.restype = C.c_size_t
     L.sas_decode_step.argtypes = [sp, C.c_int, C.c_int, P, P, C.c_int, C.c_int, P, P, C.c_int,
@@ -112,7 +117,8 @@ def lib():
     L.sas_profiler_read.argtypes = [C.POINTER(sas_kernel_time), C.c_int]
     L.sas_profiler_read.restype = C.c_int
     for name in ("sas_block_pool", "sas_select_topk", "sas_attn_fwd", "sas_attn_bwd",
-                 "sas_decode", "sas_decode_step", "sas_selector_bwd"):
+                 "sas_decode", "sas_decode_step", "sas_decode_paged", "sas_decode_step_paged",
+                 "sas_selector_bwd"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -224,6 +230,26 @@ def sas_decode_step(shape: Shape, cache_len: int, K: int, q, kbar, kbar_dtype: i
         C.byref(shape.c()), cache_len, K, _ptr(q), _ptr(kbar), kbar_dtype, kbar_ld, _ptr(kcache),
         _ptr(vcache), 1 if gated else 0, _ptr(o), _ptr(lse), _ptr(idx), _ptr(logg), _ptr(lse_s),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sas_decode_paged(shape: Shape, K: int, q, kpages, vpages, num_pages: int, block_table,
+                     bt_ld: int, seq_lens, idx, logg, o, lse, workspace, ws_bytes: int,
+                     stream=None):
+    _check("sas_decode_paged", lib().sas_decode_paged(
+        C.byref(shape.c()), K, _ptr(q), _ptr(kpages), _ptr(vpages), num_pages, _ptr(block_table),
+        bt_ld, _ptr(seq_lens), _ptr(idx), _ptr(logg), _ptr(o), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def sas_decode_step_paged(shape: Shape, K: int, q, kbar, kbar_dtype: int, kbar_ld: int, kpages,
+                          vpages, num_pages: int, block_table, bt_ld: int, seq_lens,
+                          gated: bool, o, lse, idx, logg, lse_s, workspace, ws_bytes: int,
+                          stream=None):
+    _check("sas_decode_step_paged", lib().sas_decode_step_paged(
+        C.byref(shape.c()), K, _ptr(q), _ptr(kbar), kbar_dtype, kbar_ld, _ptr(kpages),
+        _ptr(vpages), num_pages, _ptr(block_table), bt_ld, _ptr(seq_lens), 1 if gated else 0,
+        _ptr(o), _ptr(lse), _ptr(idx), _ptr(logg), _ptr(lse_s), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def sas_selector_bwd(shape: Shape, ds, qbar, kbar, dqbar, dkbar, dq=None, dk=None, stream=None):

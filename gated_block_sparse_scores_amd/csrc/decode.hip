@@ -32,6 +32,25 @@ constexpr int kMaxG = 8;
 constexpr int kMaxBps = 2;
 constexpr int kMaxSplit = 65;  // K + 1 blocks at one block per split
 
+// Valid length of sequence b (its own, clamped, in a ragged batch).
+__device__ __forceinline__ int view_len(const KvView& kvv, int b, int L) {
+  if (!kvv.seq_lens) return L;
+  return min(max(kvv.seq_lens[b], 1), L);
+}
+
+// First row of logical block m of (b, kv) in the K or V cache, or nullptr when
+// its page number is out of range (the block is then empty).
+template <typename T>
+__device__ __forceinline__ const T* view_block(const KvView& kvv, const void* base, int b,
+                                               int kv, int hkv, int m, int BS, int D) {
+  if (kvv.table) {
+    const int page = kvv.table[(size_t)b * kvv.bt_ld + m];
+    if (page < 0 || page >= kvv.num_pages) return nullptr;
+    return (const T*)base + ((size_t)page * hkv + kv) * (size_t)BS * D;
+  }
+  return (const T*)base + (((size_t)b * hkv + kv) * kvv.cache_len + (size_t)m * BS) * D;
+}
+
 template <typename T, int N> struct VecLoad;
 template <> struct VecLoad<bf16_t, 8> {
   static __device__ __forceinline__ void load(const bf16_t* p, float* o) {
@@ -123,15 +142,17 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(256) decode_split_kernel(
-    Dims dm, int L, int cache_len, int bps, int nsplit, const T* __restrict__ q,
-    const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ idx,
-    const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc) {
+    Dims dm, int Lmax, KvView kvv, int bps, int nsplit, const T* __restrict__ q,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg, float* __restrict__ part_ml,
+    float* __restrict__ part_acc) {
   constexpr int DPL = D / 16;                  // dims per lane (one vector load)
   constexpr int MAXKEYS = kMaxBps * BS;
   constexpr int KPT = MAXKEYS / 16;            // keys per thread (16 key groups)
   __shared__ float sc[kMaxG][MAXKEYS];
   __shared__ __align__(16) float red[4][kMaxG][D];
   __shared__ int blist[kMaxBps];
+  __shared__ const T* bk_ptr[kMaxBps];  // first K row of each listed block
+  __shared__ const T* bv_ptr[kMaxBps];
   __shared__ float bbias[kMaxBps];  // added to the logits (inner gating)
   __shared__ float bgain[kMaxBps];  // multiplies the values (outer gating)
   __shared__ float mx_sh[kMaxG], l_sh[kMaxG];
@@ -141,31 +162,32 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int bk = blockIdx.x / nsplit;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
   const int G = dm.g;
+  const int L = view_len(kvv, b, Lmax);
   const int c = (L - 1) / BS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = tid & 15, grp = tid >> 4;
 
   if (tid == 0) {
+    // entries: the valid selected blocks (slot order), then the current block;
+    // a block whose page is out of range is left out
     int pos = 0, nb = 0;
     const int first = split * bps, last = first + bps;
-    for (int s = 0; s < dm.K; ++s) {
-      const int m = idx[(size_t)bk * dm.K + s];
-      if (m >= 0 && m < c) {
-        if (pos >= first && pos < last) {
-          const float lg = logg ? logg[(size_t)bk * dm.K + s] : 0.0f;
-          blist[nb] = m;
-          bbias[nb] = dm.outer ? 0.0f : lg;
-          bgain[nb] = dm.outer ? expf(lg) : 1.0f;
-          ++nb;
-        }
-        ++pos;
+    for (int s = 0; s <= dm.K; ++s) {
+      const int m = s < dm.K ? idx[(size_t)bk * dm.K + s] : c;
+      if (s < dm.K && !(m >= 0 && m < c)) continue;
+      const T* kp = view_block<T>(kvv, kvv.k, b, kv, dm.hkv, m, BS, D);
+      const T* vp = view_block<T>(kvv, kvv.v, b, kv, dm.hkv, m, BS, D);
+      if (!kp || !vp) continue;
+      if (pos >= first && pos < last) {
+        const float lg = (s < dm.K && logg) ? logg[(size_t)bk * dm.K + s] : 0.0f;
+        blist[nb] = m;
+        bk_ptr[nb] = kp;
+        bv_ptr[nb] = vp;
+        bbias[nb] = dm.outer ? 0.0f : lg;
+        bgain[nb] = dm.outer ? expf(lg) : 1.0f;
+        ++nb;
       }
-    }
-    if (pos >= first && pos < last) {
-      blist[nb] = c;
-      bbias[nb] = 0.0f;
-      bgain[nb] = 1.0f;
-      ++nb;
+      ++pos;
     }
     nb_sh = nb;
   }
@@ -185,7 +207,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   }
   __syncthreads();
   const int nkeys = nb_sh * BS;
-  const size_t kvbase = ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
 
   // Issue every K and V row load of this split before any arithmetic.
   RawSlice<T, DPL> kr[KPT], vr[KPT];
@@ -194,8 +215,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
     const int kk = grp + 16 * i;
     const int pos = kk < nkeys ? blist[kk / BS] * BS + (kk % BS) : L;
     if (pos < L) {
-      kr[i].load(kc + kvbase + (size_t)pos * D + sub * DPL);
-      vr[i].load(vc + kvbase + (size_t)pos * D + sub * DPL);
+      kr[i].load(bk_ptr[kk / BS] + (size_t)(kk % BS) * D + sub * DPL);
+      vr[i].load(bv_ptr[kk / BS] + (size_t)(kk % BS) * D + sub * DPL);
     } else {
       kr[i].zero();
       vr[i].zero();
@@ -317,7 +338,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(int nsplit, int D,
   }
   Ls = wave_sum(Ls);
   __syncthreads();
-  const float inv = 1.0f / Ls;
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;  // no key at all: o = 0, lse = -inf
   const float* acc = part_acc + row * nsplit * D;
   for (int dd = lane; dd < D; dd += 64) {
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -330,7 +351,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(int nsplit, int D,
     const float tot = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     Elem<T>::store(o, row * D + dd, tot * inv);
   }
-  if (lane == 0) lse[row] = M + logf(Ls);
+  if (lane == 0) lse[row] = Ls > 0.0f ? M + logf(Ls) : -INFINITY;
 }
 
 // ---------------------------------------------------------------- bf16, d 128, block 64
@@ -380,10 +401,9 @@ struct SelectChunks {
 
 template <int G, int kDecWaves, bool SEL>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
-    Dims dm, int L, int cache_len, int nsplit, const bf16_t* __restrict__ q,
-    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const int32_t* __restrict__ idx,
-    const float* __restrict__ logg, float* __restrict__ part_ml, float* __restrict__ part_acc,
-    SelectChunks sel) {
+    Dims dm, int Lmax, KvView kvv, int nsplit, const bf16_t* __restrict__ q,
+    const int32_t* __restrict__ idx, const float* __restrict__ logg,
+    float* __restrict__ part_ml, float* __restrict__ part_acc, SelectChunks sel) {
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
   __shared__ __align__(16) uint32_t Pb[kDecWaves][BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
@@ -392,6 +412,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
+  const int L = view_len(kvv, b, Lmax);
   const int c = (L - 1) / BS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t prow = (size_t)b * dm.hq + (size_t)kv * G;
@@ -422,7 +443,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       S += st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0;
     }
     S = block_sum_d(S, dscr);
-    const float lse_s = sel.C > 0 ? (float)((double)M + log(S)) : -INFINITY;
+    const int Crow = kvv.seq_lens ? min(sel.C, c) : sel.C;  // this sequence's history
+    const float lse_s = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
     uint64_t* src = lists;
     uint64_t* dst = lists + nc;
     int nl = sel.nchunk;
@@ -440,7 +462,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       dst = tmp;
       nl = np + (nl & 1);
     }
-    const int kk = min(K, sel.C);
+    const int kk = min(K, Crow);
     if (tid < kk) {
       const uint64_t key = src[tid];
       widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
@@ -488,6 +510,14 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       m = c;
     }
   }
+  // The block's rows (a block on an out-of-range page is skipped).
+  const bf16_t* kblk = nullptr;
+  const bf16_t* vblk = nullptr;
+  if (m >= 0) {
+    kblk = view_block<bf16_t>(kvv, kvv.k, b, kv, dm.hkv, m, BS, D);
+    vblk = view_block<bf16_t>(kvv, kvv.v, b, kv, dm.hkv, m, BS, D);
+    if (!kblk || !vblk) m = -1;
+  }
   // Outer gating: the logits carry no bias and the block's P V is scaled by g.
   float gain = 1.0f;
   if (dm.outer) {
@@ -500,8 +530,6 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
   if (m >= 0) {
-    const bf16_t* kbase = kc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
-    const bf16_t* vbase = vc + ((size_t)b * dm.hkv + kv) * (size_t)cache_len * D;
     const int pos0 = m * BS;
     const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
 
@@ -509,8 +537,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     bf16x8_t kf[4][4];
     uint32_t vr[BS];
     if (pos0 + BS <= L) {  // full block (every history block): plain offsets
-      const bf16_t* krow = kbase + ((size_t)pos0 + (lane & 15)) * D + (lane >> 4) * 8;
-      const bf16_t* vrow = vbase + (size_t)pos0 * D + 2 * lane;
+      const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
+      const bf16_t* vrow = vblk + 2 * lane;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -521,15 +549,15 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     } else {  // the current block: rows past L - 1 are read clamped, then masked
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const int pos = min(pos0 + kt * 16 + (lane & 15), last);
+        const int rr = min(kt * 16 + (lane & 15), last - pos0);
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch)
-          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kbase + (size_t)pos * D + ch * 32 +
+          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kblk + (size_t)rr * D + ch * 32 +
                                                           (lane >> 4) * 8);
       }
 #pragma unroll
       for (int r = 0; r < BS; ++r)
-        vr[r] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)min(pos0 + r, last) * D +
+        vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
                                                    2 * lane);
     }
     bf16x8_t qf[4];
@@ -645,28 +673,25 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
 }
 
 template <int G, bool SEL>
-void launch_decode_block4(const Dims& dm, int L, int cache_len, int nsplit, int waves,
-                          const void* q, const void* kc, const void* vc, const int32_t* idx,
-                          const float* logg, float* part_ml, float* part_acc,
-                          const SelectChunks& sel, hipStream_t st) {
+void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, int waves,
+                          const void* q, const int32_t* idx, const float* logg, float* part_ml,
+                          float* part_acc, const SelectChunks& sel, hipStream_t st) {
   const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
   const size_t lds = SEL ? (size_t)2 * sel.nchunk * dm.K * sizeof(uint64_t) : 0;
   if (waves == 4)
     hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL>), dim3((unsigned)wgs), dim3(256), lds, st,
-                       dm, L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
-                       (const bf16_t*)vc, idx, logg, part_ml, part_acc, sel);
+                       dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc, sel);
   else
     hipLaunchKernelGGL((decode_block4_kernel<G, 1, SEL>), dim3((unsigned)wgs), dim3(64), lds, st,
-                       dm, L, cache_len, nsplit, (const bf16_t*)q, (const bf16_t*)kc,
-                       (const bf16_t*)vc, idx, logg, part_ml, part_acc, sel);
+                       dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc, sel);
 }
 
 // Workspace: [partials (max, sum) per (b, h, split)][partial outputs per
 // (b, h, split, d)].
 template <typename T, int D, int BS>
-hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
-                        const void* vc, const int32_t* idx, const float* logg, void* o,
-                        float* lse, void* ws, hipStream_t st) {
+hipError_t decode_typed(const Dims& dm, int L, const KvView& kvv, const void* q,
+                        const int32_t* idx, const float* logg, void* o, float* lse, void* ws,
+                        hipStream_t st) {
   const int bps = decode_blocks_per_split(dm);
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
@@ -676,8 +701,8 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
     if constexpr (std::is_same<T, bf16_t>::value && D == 128 && BS == 64) {
 #define SAS_DEC_G(G_)                                                                     \
   case G_:                                                                                \
-    launch_decode_block4<G_, false>(dm, L, cache_len, nsplit, bps, q, kc, vc, idx, logg,  \
-                                    part_ml, part_acc, SelectChunks{}, st);               \
+    launch_decode_block4<G_, false>(dm, L, kvv, nsplit, bps, q, idx, logg, part_ml,       \
+                                    part_acc, SelectChunks{}, st);                        \
     break;
       switch (dm.g) {
         SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4)
@@ -688,8 +713,7 @@ hipError_t decode_typed(const Dims& dm, int L, int cache_len, const void* q, con
     } else {
       const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
       hipLaunchKernelGGL((decode_split_kernel<T, D, BS>), dim3((unsigned)wgs), dim3(256), 0, st,
-                         dm, L, cache_len, bps, nsplit, (const T*)q, (const T*)kc,
-                         (const T*)vc, idx, logg, part_ml, part_acc);
+                         dm, L, kvv, bps, nsplit, (const T*)q, idx, logg, part_ml, part_acc);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -719,12 +743,12 @@ size_t decode_workspace_bytes(const Dims& dm) {
   return (size_t)dm.b * dm.hq * nsplit * (2 + dm.d) * sizeof(float);
 }
 
-hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
-                         const void* vc, const int32_t* idx, const float* logg, void* o,
-                         float* lse, void* ws, hipStream_t st) {
+hipError_t launch_decode(const Dims& dm, int L, const KvView& kvv, const void* q,
+                         const int32_t* idx, const float* logg, void* o, float* lse, void* ws,
+                         hipStream_t st) {
 #define SAS_DEC(T_, D_, BS_)                                                            \
   if ((dm.bf16 == std::is_same<T_, bf16_t>::value) && dm.d == D_ && dm.bs == BS_)    \
-    return decode_typed<T_, D_, BS_>(dm, L, cache_len, q, kc, vc, idx, logg, o, lse, ws, st);
+    return decode_typed<T_, D_, BS_>(dm, L, kvv, q, idx, logg, o, lse, ws, st);
   SAS_DEC(float, 64, 16) SAS_DEC(float, 64, 32) SAS_DEC(float, 64, 64)
   SAS_DEC(float, 128, 16) SAS_DEC(float, 128, 32) SAS_DEC(float, 128, 64)
   SAS_DEC(bf16_t, 64, 16) SAS_DEC(bf16_t, 64, 32) SAS_DEC(bf16_t, 64, 64)
@@ -735,11 +759,10 @@ hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, co
 
 size_t decode_step_partial_bytes(const Dims& dm) { return decode_workspace_bytes(dm); }
 
-hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int nchunk,
-                              const void* q, const void* kc, const void* vc,
-                              const uint64_t* cand, const float2* stats, bool gated,
-                              int32_t* idx_out, float* logg_out, float* lse_s_out, void* o,
-                              float* lse, void* ws, hipStream_t st) {
+hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, int nchunk,
+                              const void* q, const uint64_t* cand, const float2* stats,
+                              bool gated, int32_t* idx_out, float* logg_out, float* lse_s_out,
+                              void* o, float* lse, void* ws, hipStream_t st) {
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
   const int bps = decode_blocks_per_split(dm);
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
@@ -751,8 +774,8 @@ hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int n
     ProfScope ps("step_decode_split", st);
 #define SAS_DEC_G(G_)                                                                          \
   case G_:                                                                                     \
-    launch_decode_block4<G_, true>(dm, L, cache_len, nsplit, bps, q, kc, vc, nullptr, nullptr, \
-                                   part_ml, part_acc, sel, st);                                \
+    launch_decode_block4<G_, true>(dm, L, kvv, nsplit, bps, q, nullptr, nullptr, part_ml,      \
+                                   part_acc, sel, st);                                         \
     break;
     switch (dm.g) {
       SAS_DEC_G(1) SAS_DEC_G(2) SAS_DEC_G(3) SAS_DEC_G(4)

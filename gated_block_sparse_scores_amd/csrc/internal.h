@@ -15,6 +15,20 @@ struct ProfScope {
   hipStream_t stream;
 };
 
+// Where a decode reads its K / V cache.  Dense: [b, hkv, cache_len, d] per
+// tensor.  Paged (table != nullptr): pages [num_pages, hkv, bs, d], logical
+// block m of sequence b in page table[b * bt_ld + m]; a page number outside
+// [0, num_pages) makes that block empty.  seq_lens (optional, device) gives each
+// sequence its own valid length, clamped to [1, L] (L = the call's seqlen).
+struct KvView {
+  const void* k;
+  const void* v;
+  int cache_len;
+  const int32_t* table;
+  int bt_ld, num_pages;
+  const int32_t* seq_lens;
+};
+
 struct Dims {
   int b, hq, hkv, g, n, d, bs, T, K;
   float scale;
@@ -78,19 +92,20 @@ size_t decode_workspace_bytes(const Dims& dm);
 // cache with the query pooled in-kernel, then the decode kernel merging the
 // chunk candidates itself, then the LSE merge.
 constexpr int kSelectChunk = 256;  // history blocks per selection chunk
+// Decode rows (T = 1): with seq_lens, row r = b * hkv + kv has history
+// min(C, (clamp(seq_lens[b], 1, L) - 1) / bs) blocks.
 hipError_t launch_select_chunks_rawq(const uint16_t* q, int qgroup, const void* kbar,
                                      bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
-                                     int C, int K, uint64_t* cand, float2* stats,
-                                     hipStream_t st);
+                                     int C, int K, const int32_t* seq_lens, int L, int bs,
+                                     int hkv, uint64_t* cand, float2* stats, hipStream_t st);
 bool decode_mfma_path(const Dims& dm);
-hipError_t launch_decode_step(const Dims& dm, int L, int cache_len, int C, int nchunk,
-                              const void* q, const void* kc, const void* vc,
-                              const uint64_t* cand, const float2* stats, bool gated,
-                              int32_t* idx_out, float* logg_out, float* lse_s_out, void* o,
-                              float* lse, void* ws, hipStream_t st);
-hipError_t launch_decode(const Dims& dm, int L, int cache_len, const void* q, const void* kc,
-                         const void* vc, const int32_t* idx, const float* logg, void* o,
-                         float* lse, void* ws, hipStream_t st);
+hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, int nchunk,
+                              const void* q, const uint64_t* cand, const float2* stats,
+                              bool gated, int32_t* idx_out, float* logg_out, float* lse_s_out,
+                              void* o, float* lse, void* ws, hipStream_t st);
+hipError_t launch_decode(const Dims& dm, int L, const KvView& kvv, const void* q,
+                         const int32_t* idx, const float* logg, void* o, float* lse, void* ws,
+                         hipStream_t st);
 
 // ---- selector backward for the stand-in scores (selector_bwd.hip)
 hipError_t launch_selector_bwd(const Dims& dm, const float* ds, const float* qbar,

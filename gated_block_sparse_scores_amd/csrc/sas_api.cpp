@@ -321,8 +321,8 @@ sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* 
   const Dims dm = make_dims(shape, K);
   const size_t need = sas::decode_workspace_bytes(dm);
   if (!workspace || ws_bytes < need) return SAS_ERR_WORKSPACE;
-  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx,
-                                          dm.ste ? nullptr : logg, o, lse,
+  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, nullptr};
+  return launch_status(sas::launch_decode(dm, L, kvv, q, idx, dm.ste ? nullptr : logg, o, lse,
                                           workspace, (hipStream_t)stream));
 }
 
@@ -373,28 +373,25 @@ size_t sas_decode_step_workspace_size(const sas_shape* shape, int K) {
   return step_layout(shape, K).bytes;
 }
 
-sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const void* q,
-                           const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
-                           const void* kcache, const void* vcache, int gated, void* o,
-                           float* lse, int32_t* idx, float* logg, float* lse_s,
-                           void* workspace, size_t ws_bytes, void* stream) {
-  SAS_TRY(check_shape(shape));
-  if (K <= 0 || cache_len < 0) return SAS_ERR_INVALID_ARG;
-  if (K > 64) return SAS_ERR_UNSUPPORTED;
+namespace {
+
+// One decode step (pool + stand-in select + decode) over a dense or paged view
+// of the cache.  Ragged (seq_lens) views take the fused path only.
+sas_status decode_step_impl(const sas_shape* shape, int K, const void* q, const void* kbar,
+                            sas_dtype kbar_dtype, int kbar_ld, const sas::KvView& kvv,
+                            int gated, void* o, float* lse, int32_t* idx, float* logg,
+                            float* lse_s, void* workspace, size_t ws_bytes, void* stream) {
   const int L = shape->seqlen;
-  const int cl = cache_len == 0 ? L : cache_len;
-  if (cl < L) return SAS_ERR_INVALID_ARG;
-  if (!q || !kbar || !kcache || !vcache || !o || !lse) return SAS_ERR_INVALID_ARG;
+  if (!q || !kbar || !o || !lse) return SAS_ERR_INVALID_ARG;
   if ((idx == nullptr) != (logg == nullptr) || (idx == nullptr) != (lse_s == nullptr))
     return SAS_ERR_INVALID_ARG;
   if (kbar_dtype != SAS_DTYPE_F32 && kbar_dtype != SAS_DTYPE_BF16) return SAS_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kbar) || !aligned16(kcache) || !aligned16(vcache) ||
-      !aligned16(o))
-    return SAS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kbar) || !aligned16(o)) return SAS_ERR_INVALID_ARG;
   if (shape->hq / shape->hkv > 8) return SAS_ERR_UNSUPPORTED;
   const StepLayout lay = step_layout(shape, K);
   if (kbar_ld < lay.C) return SAS_ERR_INVALID_ARG;
   if (lay.C > 16384) return SAS_ERR_UNSUPPORTED;
+  if (kvv.seq_lens && !lay.fused) return SAS_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < lay.bytes) return SAS_ERR_WORKSPACE;
   const Dims dm = make_dims(shape, K);
   const hipStream_t st = (hipStream_t)stream;
@@ -406,13 +403,12 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
   if (lay.fused) {
     uint64_t* cand = (uint64_t*)(ws + lay.cand);
     float2* stats = (float2*)(ws + lay.stats);
-    SAS_LAUNCH(sas::launch_select_chunks_rawq((const uint16_t*)q, G, kbar,
-                                              kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
-                                              shape->head_dim, scale, rows, lay.C, K, cand, stats,
-                                              st));
-    return launch_status(sas::launch_decode_step(dm, L, cl, lay.C, lay.nchunk, q, kcache,
-                                                 vcache, cand, stats, gated && !dm.ste, idx, logg,
-                                                 lse_s, o, lse, ws + lay.part, st));
+    SAS_LAUNCH(sas::launch_select_chunks_rawq(
+        (const uint16_t*)q, G, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim,
+        scale, rows, lay.C, K, kvv.seq_lens, L, shape->block, shape->hkv, cand, stats, st));
+    return launch_status(sas::launch_decode_step(dm, L, kvv, lay.C, lay.nchunk, q, cand, stats,
+                                                 gated && !dm.ste, idx, logg, lse_s, o, lse,
+                                                 ws + lay.part, st));
   }
   // Every other shape: the same three stages through the separate calls' kernels.
   float* qbar = (float*)(ws + lay.qbar);
@@ -432,9 +428,74 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
     SAS_LAUNCH(sas::launch_topk(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                 shape->head_dim, scale, s_out, rows, 1, lay.C, lay.C, K, dm.act,
                                 idx_w, logg_w, lse_s_w, st));
-  return launch_status(sas::launch_decode(dm, L, cl, q, kcache, vcache, idx_w,
+  return launch_status(sas::launch_decode(dm, L, kvv, q, idx_w,
                                           (gated && !dm.ste) ? logg_w : nullptr, o, lse,
                                           ws + lay.dec, st));
+}
+
+// Checks of a paged view: pages, table and lengths present and the table wide
+// enough for seqlen tokens.
+sas_status check_paged(const sas_shape* shape, const void* kpages, const void* vpages,
+                       int num_pages, const int32_t* block_table, int bt_ld,
+                       const int32_t* seq_lens) {
+  if (!kpages || !vpages || !block_table || !seq_lens || num_pages <= 0) return SAS_ERR_INVALID_ARG;
+  if (!aligned16(kpages) || !aligned16(vpages)) return SAS_ERR_INVALID_ARG;
+  const int need = (shape->seqlen + shape->block - 1) / shape->block;
+  if (bt_ld < need) return SAS_ERR_INVALID_ARG;
+  return SAS_OK;
+}
+
+}  // namespace
+
+sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const void* q,
+                           const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                           const void* kcache, const void* vcache, int gated, void* o,
+                           float* lse, int32_t* idx, float* logg, float* lse_s,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0 || cache_len < 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  const int L = shape->seqlen;
+  const int cl = cache_len == 0 ? L : cache_len;
+  if (cl < L) return SAS_ERR_INVALID_ARG;
+  if (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)) return SAS_ERR_INVALID_ARG;
+  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, nullptr};
+  return decode_step_impl(shape, K, q, kbar, kbar_dtype, kbar_ld, kvv, gated, o, lse, idx, logg,
+                          lse_s, workspace, ws_bytes, stream);
+}
+
+sas_status sas_decode_paged(const sas_shape* shape, int K, const void* q, const void* kpages,
+                            const void* vpages, int num_pages, const int32_t* block_table,
+                            int bt_ld, const int32_t* seq_lens, const int32_t* idx,
+                            const float* logg, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  SAS_TRY(check_paged(shape, kpages, vpages, num_pages, block_table, bt_ld, seq_lens));
+  if (!q || !idx || !o || !lse || !aligned16(q) || !aligned16(o)) return SAS_ERR_INVALID_ARG;
+  if (shape->hq / shape->hkv > 8) return SAS_ERR_UNSUPPORTED;
+  const Dims dm = make_dims(shape, K);
+  if (!workspace || ws_bytes < sas::decode_workspace_bytes(dm)) return SAS_ERR_WORKSPACE;
+  const sas::KvView kvv{kpages, vpages, 0, block_table, bt_ld, num_pages, seq_lens};
+  return launch_status(sas::launch_decode(dm, shape->seqlen, kvv, q, idx,
+                                          dm.ste ? nullptr : logg, o, lse, workspace,
+                                          (hipStream_t)stream));
+}
+
+sas_status sas_decode_step_paged(const sas_shape* shape, int K, const void* q,
+                                 const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                                 const void* kpages, const void* vpages, int num_pages,
+                                 const int32_t* block_table, int bt_ld, const int32_t* seq_lens,
+                                 int gated, void* o, float* lse, int32_t* idx, float* logg,
+                                 float* lse_s, void* workspace, size_t ws_bytes, void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  SAS_TRY(check_paged(shape, kpages, vpages, num_pages, block_table, bt_ld, seq_lens));
+  const sas::KvView kvv{kpages, vpages, 0, block_table, bt_ld, num_pages, seq_lens};
+  return decode_step_impl(shape, K, q, kbar, kbar_dtype, kbar_ld, kvv, gated, o, lse, idx, logg,
+                          lse_s, workspace, ws_bytes, stream);
 }
 
 sas_status sas_selector_bwd(const sas_shape* shape, const float* ds, const float* qbar,

@@ -320,7 +320,8 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     const float* __restrict__ s, const float* __restrict__ qbar, const bf16_t* __restrict__ qraw,
     int qgroup, const Tk* __restrict__ kbar, int kbar_ld, int d, double scale, int T, int C,
     int row_offset, int K, int nchunk, float* __restrict__ s_out, uint64_t* __restrict__ cand,
-    float2* __restrict__ stats) {
+    float2* __restrict__ stats, const int32_t* __restrict__ seq_lens, int len_max, int len_bs,
+    int len_hkv) {
   __shared__ uint64_t keys[kChunk];
   __shared__ float sval[kChunk];
   __shared__ float fscr[16];
@@ -329,7 +330,11 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   const size_t row = blockIdx.y;
   const int t = (int)(row % T);
   const size_t bk = row / T;
-  const int ct = min(t + row_offset, C);
+  int ct = min(t + row_offset, C);
+  if (seq_lens) {  // ragged decode batch: this sequence's own history
+    const int lb = min(max(seq_lens[bk / len_hkv], 1), len_max);
+    ct = min(ct, (lb - 1) / len_bs);
+  }
   const int m0 = chunk * kChunk;
   const int tid = threadIdx.x;
   const int m = m0 + tid;
@@ -492,11 +497,13 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
     if (kbar_bf16)
       hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, s, qbar,
                          (const bf16_t*)nullptr, 0, (const bf16_t*)kbar, kbar_ld, d, scale, T, C,
-                         row_offset, K, nchunk, s_out, cand, stats);
+                         row_offset, K, nchunk, s_out, cand, stats, (const int32_t*)nullptr, 0,
+                         1, 1);
     else
       hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, s, qbar,
                          (const bf16_t*)nullptr, 0, (const float*)kbar, kbar_ld, d, scale, T, C,
-                         row_offset, K, nchunk, s_out, cand, stats);
+                         row_offset, K, nchunk, s_out, cand, stats, (const int32_t*)nullptr, 0,
+                         1, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -511,8 +518,8 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
 
 hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kbar,
                                      bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
-                                     int C, int K, uint64_t* cand, float2* stats,
-                                     hipStream_t st) {
+                                     int C, int K, const int32_t* seq_lens, int L, int bs,
+                                     int hkv, uint64_t* cand, float2* stats, hipStream_t st) {
   const int nchunk = (C + kChunk - 1) / kChunk;
   if (nchunk == 0) return hipSuccess;
   ProfScope ps("step_select_chunk", st);
@@ -520,11 +527,11 @@ hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kb
   if (kbar_bf16)
     hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, (const float*)nullptr,
                        (const float*)nullptr, q, qgroup, (const bf16_t*)kbar, kbar_ld, d, scale,
-                       1, C, C, K, nchunk, (float*)nullptr, cand, stats);
+                       1, C, C, K, nchunk, (float*)nullptr, cand, stats, seq_lens, L, bs, hkv);
   else
     hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, (const float*)nullptr,
                        (const float*)nullptr, q, qgroup, (const float*)kbar, kbar_ld, d, scale, 1,
-                       C, C, K, nchunk, (float*)nullptr, cand, stats);
+                       C, C, K, nchunk, (float*)nullptr, cand, stats, seq_lens, L, bs, hkv);
   return hipGetLastError();
 }
 

@@ -155,3 +155,50 @@ def selector_bwd(ds, qbar, kbar, block: int, seqlen: int, hq: int, dq=None, dk=N
     dkbar = torch.empty_like(kbar)
     L.sas_selector_bwd(sh, ds, qbar, kbar, dqbar, dkbar, dq, dk, stream)
     return dqbar, dkbar
+
+
+def decode_paged(q, kpages, vpages, block_table, seq_lens, idx, logg, block: int,
+                 max_len: Optional[int] = None, scale: float = 0.0, stream=None,
+                 workspace: Optional[torch.Tensor] = None, gate: int = 0):
+    """Ragged decode over a paged cache: q [b,hq,d]; pages [num_pages,hkv,block,d];
+    block_table int32 [b,bt_ld]; seq_lens int32 [b] (device); idx/logg [b,hkv,K].
+    max_len (the longest sequence) defaults to bt_ld * block."""
+    b, hq, d = q.shape
+    hkv = kpages.shape[1]
+    K = idx.shape[-1]
+    L_ = max_len if max_len is not None else block_table.shape[1] * block
+    sh = Shape(b, hq, hkv, L_, d, block, L.dtype_code(q.dtype), scale, gate)
+    o = torch.empty_like(q)
+    lse = _f32((b, hq), q.device)
+    ws_n = L.sas_decode_workspace_size(sh, K)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_decode_paged(sh, K, q, kpages, vpages, kpages.shape[0], block_table,
+                       block_table.shape[1], seq_lens, idx, logg, o, lse, workspace, ws_n, stream)
+    return o, lse
+
+
+def decode_step_paged(q, kbar, kpages, vpages, block_table, seq_lens, K: int, block: int,
+                      max_len: Optional[int] = None, gated: bool = True, scale: float = 0.0,
+                      with_selection: bool = True, stream=None,
+                      workspace: Optional[torch.Tensor] = None, gate: int = 0):
+    """Fused decode step of a ragged batch over a paged cache (kbar dense
+    [b,hkv,>=C,d]).  Returns (o, lse) or (o, lse, idx, logg, lse_s)."""
+    b, hq, d = q.shape
+    hkv = kpages.shape[1]
+    L_ = max_len if max_len is not None else block_table.shape[1] * block
+    sh = Shape(b, hq, hkv, L_, d, block, L.dtype_code(q.dtype), scale, gate)
+    o = torch.empty_like(q)
+    lse = _f32((b, hq), q.device)
+    idx = logg = lse_s = None
+    if with_selection:
+        idx = _i32((b, hkv, K), q.device)
+        logg = _f32((b, hkv, K), q.device)
+        lse_s = _f32((b, hkv), q.device)
+    ws_n = L.sas_decode_step_workspace_size(sh, K)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    L.sas_decode_step_paged(sh, K, q, kbar, L.dtype_code(kbar.dtype), kbar.shape[2], kpages,
+                            vpages, kpages.shape[0], block_table, block_table.shape[1], seq_lens,
+                            gated, o, lse, idx, logg, lse_s, workspace, ws_n, stream)
+    return (o, lse, idx, logg, lse_s) if with_selection else (o, lse)

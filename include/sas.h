@@ -250,6 +250,42 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Paged cache, ragged batch: the serving setting of the pages' decode
+ * measurements (picx 'Decode Efficiency (Figure 7)': batch 8 at 64K, batch 1
+ * up to 512K).  Sequence b has its own valid length L_b = seq_lens[b] (its new
+ * token at L_b - 1, current block c_b = (L_b - 1) / block, history blocks
+ * m < c_b), and its K / V rows live in pages of one block each:
+ *   kpages, vpages  [num_pages, hkv, block, d] (shape->dtype); page p holds
+ *                   the `block` consecutive tokens of one logical block for
+ *                   every KV head
+ *   block_table     int32 [b, bt_ld] (device): logical block m of sequence b
+ *                   is page block_table[b * bt_ld + m]; bt_ld >= ceil(seqlen /
+ *                   block).  A page number outside [0, num_pages) makes that
+ *                   block empty (nothing is read from it).
+ *   seq_lens        int32 [b] (device); entries are clamped to [1, seqlen],
+ *                   shape->seqlen being the longest sequence of the batch
+ * sas_decode_paged: as sas_decode with the selection given (idx, logg
+ *   [b, hkv, K]; entries outside [0, c_b) ignored); workspace size as
+ *   sas_decode_workspace_size.
+ * sas_decode_step_paged: as sas_decode_step (kbar [b, hkv, kbar_ld, d] stays a
+ *   dense per-sequence cache, rows m < C_b read); each sequence ranks its own
+ *   C_b history blocks.  Supported where sas_decode_step takes its fused path
+ *   (bf16, head_dim 128, block 64, ceil(C / 256) * K <= 2048 for C of seqlen);
+ *   workspace size as sas_decode_step_workspace_size.
+ * ---------------------------------------------------------------------- */
+sas_status sas_decode_paged(const sas_shape* shape, int K, const void* q, const void* kpages,
+                            const void* vpages, int num_pages, const int32_t* block_table,
+                            int bt_ld, const int32_t* seq_lens, const int32_t* idx,
+                            const float* logg, void* o, float* lse, void* workspace,
+                            size_t ws_bytes, void* stream);
+sas_status sas_decode_step_paged(const sas_shape* shape, int K, const void* q,
+                                 const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                                 const void* kpages, const void* vpages, int num_pages,
+                                 const int32_t* block_table, int bt_ld, const int32_t* seq_lens,
+                                 int gated, void* o, float* lse, int32_t* idx, float* logg,
+                                 float* lse_s, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Selector backward for the stand-in scores of training rows (picx 'Key Idea:
  * Differentiable Continuous Gating': the selector learns through the gates,
  * the hard Top-K carrying no gradient ('Theoretical Foundation'); evolve.pub

@@ -525,6 +525,33 @@ def decode(q, kcache, vcache, L: int, idx, logg, bs: int, scale: Optional[float]
     return o, lse
 
 
+def gather_pages(pages, table_row, L: int, bs: int) -> np.ndarray:
+    """Dense cache [hkv, L, d] (float64) of one sequence whose logical block m
+    sits in page table_row[m] of pages [num_pages, hkv, bs, d] (page = block)."""
+    blocks = [_np64(pages[int(table_row[m])]) for m in range(n_blocks(L, bs))]
+    return np.concatenate(blocks, axis=1)[:, :L]
+
+
+def decode_paged(q, kpages, vpages, block_table, seq_lens, idx, logg, bs: int,
+                 scale: Optional[float] = None, outer: bool = False):
+    """Decode of a ragged batch over a paged cache ([picx] 'Decode Efficiency':
+    the serving setting): sequence b has its own length L_b = seq_lens[b] (new
+    token at L_b - 1, C_b = (L_b - 1) // bs history blocks) and its cache is
+    read through its block table.  Each sequence is exactly `decode` of its
+    gathered dense cache."""
+    b, hq, d = q.shape
+    o = np.zeros((b, hq, d))
+    lse = np.zeros((b, hq))
+    for bb in range(b):
+        L = int(seq_lens[bb])
+        kc = gather_pages(kpages, block_table[bb], L, bs)[None]
+        vc = gather_pages(vpages, block_table[bb], L, bs)[None]
+        ob, lb = decode(_np64(q[bb:bb + 1]), kc, vc, L, _npint(idx[bb:bb + 1]),
+                        None if logg is None else _np64(logg[bb:bb + 1]), bs, scale, outer)
+        o[bb], lse[bb] = ob[0], lb[0]
+    return o, lse
+
+
 def decode_qbar(q, hkv: int) -> np.ndarray:
     """Decode-mode pooled query: mean over the G query heads of each KV head,
     shaped [b,kv,1,d] (float64)."""

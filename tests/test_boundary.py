@@ -202,3 +202,28 @@ def test_gate_bits_are_validated():
     args[9] = None   # lse_s: the softmax gate's ds needs it
     st = L.lib().sas_attn_bwd(C.byref(sh), 31, *args, FAKE, FAKE, FAKE, n, None)
     assert st == L.SAS_ERR_INVALID_ARG
+
+
+def test_paged_decode_checks():
+    sh = shape(seqlen=1000, hq=8, hkv=2)     # 16 blocks of 64
+    lib = L.lib()
+    ws = lib.sas_decode_workspace_size(C.byref(sh), 8)
+
+    def call(kp=FAKE, table=FAKE, bt_ld=16, lens=FAKE, npages=40, K=8, n=ws):
+        return lib.sas_decode_paged(C.byref(sh), K, FAKE, kp, FAKE, npages, table, bt_ld, lens,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, n, None)
+
+    assert call(table=None) == L.SAS_ERR_INVALID_ARG
+    assert call(lens=None) == L.SAS_ERR_INVALID_ARG
+    assert call(kp=FAKE + 4) == L.SAS_ERR_INVALID_ARG
+    assert call(npages=0) == L.SAS_ERR_INVALID_ARG
+    assert call(bt_ld=15) == L.SAS_ERR_INVALID_ARG          # table narrower than seqlen
+    assert call(K=65) == L.SAS_ERR_UNSUPPORTED
+    assert call(n=ws - 1) == L.SAS_ERR_WORKSPACE
+    # the fused paged step needs the fused shapes (here block 32)
+    sh32 = shape(seqlen=1000, hq=8, hkv=2, block=32)
+    n = lib.sas_decode_step_workspace_size(C.byref(sh32), 8)
+    st = lib.sas_decode_step_paged(C.byref(sh32), 8, FAKE, FAKE, L.SAS_DTYPE_BF16, 64, FAKE,
+                                   FAKE, 40, FAKE, 32, FAKE, 1, FAKE, FAKE, None, None, None,
+                                   FAKE, n, None)
+    assert st == L.SAS_ERR_UNSUPPORTED

@@ -760,3 +760,42 @@ def test_p17_straight_through(act):
                                    None, bs)[0] * do).sum())
             fd = (lp - lm) / (2 * eps)
             assert abs(fd - gr["d" + name][pos]) <= 1e-8 + 1e-6 * abs(fd), (name, pos)
+
+
+# ---------------------------------------------------------------- P18: paged, ragged decode
+
+def test_p18_paged_decode_equals_dense():
+    """A dense cache scattered into randomly permuted pages and read back through
+    its block table gives the dense cache and the dense decode, sequence by
+    sequence, for a ragged batch (different lengths, one with no history)."""
+    rng = np.random.default_rng(3)
+    b, hq, hkv, d, bs, K = 3, 4, 2, 8, 4, 3
+    lens = [29, 4, 17]
+    maxb = O.n_blocks(max(lens), bs)
+    q = rng.standard_normal((b, hq, d))
+    kd = rng.standard_normal((b, hkv, maxb * bs, d))
+    vd = rng.standard_normal((b, hkv, maxb * bs, d))
+    npages = b * maxb + 5
+    perm = rng.permutation(npages)[:b * maxb].reshape(b, maxb)
+    kp = rng.standard_normal((npages, hkv, bs, d))    # unused pages hold other data
+    vp = rng.standard_normal((npages, hkv, bs, d))
+    for bb in range(b):
+        for m in range(maxb):
+            kp[perm[bb, m]] = kd[bb, :, m * bs:(m + 1) * bs]
+            vp[perm[bb, m]] = vd[bb, :, m * bs:(m + 1) * bs]
+    idx = np.full((b, hkv, K), -1)
+    logg = rng.standard_normal((b, hkv, K)) - 2.0
+    for bb, L in enumerate(lens):
+        C = (L - 1) // bs
+        for kv in range(hkv):
+            sel = np.sort(rng.choice(C, size=min(K, C), replace=False)) if C else []
+            idx[bb, kv, :len(sel)] = sel
+    for bb, L in enumerate(lens):
+        np.testing.assert_array_equal(O.gather_pages(kp, perm[bb], L, bs), kd[bb, :, :L])
+    for outer in (False, True):
+        o, lse = O.decode_paged(q, kp, vp, perm, lens, idx, logg, bs, outer=outer)
+        for bb, L in enumerate(lens):
+            od, ld = O.decode(q[bb:bb + 1], kd[bb:bb + 1, :, :L], vd[bb:bb + 1, :, :L], L,
+                              idx[bb:bb + 1], logg[bb:bb + 1], bs, outer=outer)
+            np.testing.assert_array_equal(o[bb], od[0])
+            np.testing.assert_array_equal(lse[bb], ld[0])
