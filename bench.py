@@ -394,6 +394,101 @@ def bench_decode(wl, steps, layers=12):
     }
 
 
+def bench_decode_paged(steps=10, layers=12):
+    """Serving-style decode: batch 8 of ragged lengths (16K to 64K tokens, 32/8
+    heads, d 128, block 64, K 63) over a paged cache (pages of one block, pages
+    of each sequence scattered at random), rotating over `layers` caches.  Times
+    the fused paged step (sas_decode_step_paged) and the paged decode with the
+    selection given (sas_decode_paged)."""
+    import numpy as np
+    import torch
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+
+    dev = "cuda"
+    b, hq, hkv, d, bs, K = 8, 32, 8, 128, 64, 63
+    lens = [65536, 61457, 57349, 49152, 40993, 32769, 24585, 16386]
+    maxlen = max(lens)
+    bt_ld = -(-maxlen // bs)
+    nblk = [-(-x // bs) for x in lens]
+    npages = sum(nblk)
+    rng = np.random.default_rng(8)
+    gen = torch.Generator(device=dev).manual_seed(8)
+    caches = []
+    for layer in range(layers):
+        perm = rng.permutation(npages)
+        table = np.full((b, bt_ld), -1, dtype=np.int32)
+        pos = 0
+        for bb in range(b):
+            table[bb, :nblk[bb]] = perm[pos:pos + nblk[bb]]
+            pos += nblk[bb]
+        kp = torch.randn((npages, hkv, bs, d), generator=gen, device=dev).to(torch.bfloat16)
+        vp = torch.randn((npages, hkv, bs, d), generator=gen, device=dev).to(torch.bfloat16)
+        kbar = torch.randn((b, hkv, bt_ld, d), generator=gen, device=dev).mul_(0.125)
+        caches.append((kp, vp, torch.from_numpy(table).to(dev), kbar.to(torch.bfloat16)))
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    calls = steps * layers
+    qs = [torch.randn((b, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+          for _ in range(calls + layers)]
+    sh = L.Shape(b, hq, hkv, maxlen, d, bs, L.SAS_DTYPE_BF16)
+    ws_step = torch.empty(L.sas_decode_step_workspace_size(sh, K), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(L.sas_decode_workspace_size(sh, K), dtype=torch.uint8, device=dev)
+    sels = []
+    for layer in range(layers):   # one selection per layer for the given-selection timing
+        kp, vp, tb, kb = caches[layer]
+        _, _, idx, logg, _ = ops.decode_step_paged(qs[layer], kb, kp, vp, tb, seq, K, bs,
+                                                   max_len=maxlen, workspace=ws_step)
+        sels.append((idx, logg))
+
+    def step(q, layer):
+        kp, vp, tb, kb = caches[layer]
+        return ops.decode_step_paged(q, kb, kp, vp, tb, seq, K, bs, max_len=maxlen,
+                                     with_selection=False, workspace=ws_step)
+
+    def dec(q, layer):
+        kp, vp, tb, _ = caches[layer]
+        idx, logg = sels[layer]
+        return ops.decode_paged(q, kp, vp, tb, seq, idx, logg, bs, max_len=maxlen,
+                                workspace=ws_dec)
+
+    out = {"workload": "paged-ragged-decode-8x16k-64k", "batch": b, "seq_lens": lens,
+           "hq": hq, "hkv": hkv, "topk": K, "layers_rotated": layers, "calls": calls}
+    sel_bytes = sum(hkv * (min(K, (x - 1) // bs) + 1) * bs * d * 2 * 2 for x in lens)
+    kbar_bytes = sum(hkv * ((x - 1) // bs) * d * 2 for x in lens)
+    out["selected_kv_bytes"] = sel_bytes
+    for name, fn in (("decode_step_paged", step), ("decode_paged", dec)):
+        for layer in range(layers):
+            fn(qs[calls + layer], layer)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for c in range(calls):
+            fn(qs[c], c % layers)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e6 / calls
+        L.sas_profiler_reset()
+        L.sas_profiler_enable(True)
+        for c in range(calls):
+            fn(qs[c], c % layers)
+        torch.cuda.synchronize()
+        L.sas_profiler_enable(False)
+        kt = L.sas_profiler_read()
+        kern = {k: round(v[1] / v[0] * 1e3, 2) for k, v in kt.items()}
+        gpu = sum(kern.values())
+        rec = {"wall_us_per_call": round(wall, 2), "gpu_us_per_call": round(gpu, 2),
+               "kernels_avg_us": kern}
+        split = kern.get("step_decode_split" if name == "decode_step_paged" else "decode_split")
+        if name == "decode_paged" and split:
+            gbs = sel_bytes / ((split + kern.get("decode_merge", 0.0)) * 1e-6) / 1e9
+            rec["decode_GBps"] = round(gbs, 1)
+            rec["decode_frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        else:
+            rec["step_GBps"] = round((sel_bytes + kbar_bytes) / (gpu * 1e-6) / 1e9, 1)
+        out[name] = rec
+    del caches
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(res, budget_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     its own selection over every row, then forward + backward of sampled
@@ -445,6 +540,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged ragged decode")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the gate-variant and dense-scope training steps")
     ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
@@ -494,6 +590,9 @@ def main():
         steps = {4: 10, 5: 25}
         out["decode"] = [bench_decode(int(wl), steps=steps.get(int(wl), 10))
                          for wl in args.decode_workloads.split(",") if wl]
+        if not args.no_paged:
+            log("paged ragged decode ...")
+            out["decode_paged"] = bench_decode_paged()
     if res is not None and not args.no_cpu_baseline:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(res)
