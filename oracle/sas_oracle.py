@@ -31,7 +31,9 @@ Per row r = (batch b, KV head kv, query block t), with valid history length C_t:
      ([picx] Eq. 5, inner gating), and ds through the gate softmax of step 2;
   7. decode: the same for a single query token at position L - 1;
   8. the selector's own backward for the stand-in scores: ds to the pooled
-     summaries (dqbar, dkbar), and through the mean pools to dq and dk.
+     summaries (dqbar, dkbar), and through the mean pools to dq and dk;
+  9. ragged batches: each sequence of a padded batch is the dense method on
+     its own tokens (training), or decodes at its own length over a paged cache.
 
 Gate variants (the ablation axes of [alanhou] / [cctest] Table 1; [picx] Eq. 4
 and 5): the activation phi of Eq. 4 is "softmax" (Eq. 6, the method), "sigmoid"
@@ -610,6 +612,54 @@ def pool_keys_bwd(dkbar, n: int, bs: int) -> np.ndarray:
         lo, hi = block_span(m, bs, n)
         dk[:, :, lo:hi] = dkbar[:, :, m, None, :] / (hi - lo)
     return dk
+
+
+# --------------------------------------------------------------------------- (9) ragged batches
+
+def ragged_train(q, k, v, dout, seq_lens, K: int, bs: int, s=None, act: str = "softmax",
+                 outer: bool = False, ste: bool = False, standin: bool = False):
+    """A ragged training batch in the padded layout [b, h, Nmax, d]: sequence b
+    is its first n_b = seq_lens[b] tokens and is exactly the dense method run on
+    those alone (selection, forward, backward, ds; with standin the scores are
+    the pooled stand-in of its own tokens, else s[b, :, :T_b, :T_b]).
+    Rows past a sequence's end carry no result: o = 0, lse = +inf (no mass),
+    every gradient 0; selection rows t >= T_b = ceil(n_b / bs) hold idx -1,
+    logg 0, lse_s -inf and ds 0."""
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    T = n_blocks(n, bs)
+    out = {"o": np.zeros((b, hq, n, d)), "lse": np.full((b, hq, n), np.inf),
+           "idx": np.full((b, hkv, T, K), -1, dtype=np.int64), "logg": np.zeros((b, hkv, T, K)),
+           "lse_s": np.full((b, hkv, T), -np.inf), "s": np.zeros((b, hkv, T, T), dtype=np.float32),
+           "dq": np.zeros((b, hq, n, d)), "dk": np.zeros((b, hkv, n, d)),
+           "dv": np.zeros((b, hkv, n, d)), "dlogg": np.zeros((b, hkv, T, K)),
+           "ds": np.zeros((b, hkv, T, T)), "qbar": np.zeros((b, hkv, T, d)),
+           "kbar": np.zeros((b, hkv, T, d))}
+    for bb in range(b):
+        nb = int(seq_lens[bb])
+        if nb == 0:
+            continue
+        Tb = n_blocks(nb, bs)
+        qs, ks, vs, ds_ = (x[bb:bb + 1, :, :nb] for x in (q, k, v, dout))
+        if standin:
+            qb = to_f32(pool_queries(qs, hkv, bs))
+            kb = to_f32(pool_keys(ks, bs))
+            out["qbar"][bb, :, :Tb], out["kbar"][bb, :, :Tb] = qb[0], kb[0]
+            sb = standin_scores(qb, kb, default_scale(d), Tb)
+        else:
+            sb = np.asarray(s[bb:bb + 1, :, :Tb, :Tb], dtype=np.float32)
+        idx, logg, lse_s = select_topk(sb, K, act=act)
+        o, lse = attn_fwd(qs, ks, vs, idx, None if ste else logg, bs, outer=outer)
+        gr = attn_bwd(qs, ks, vs, ds_, idx, logg, sb, lse_s, bs, act=act, outer=outer, ste=ste)
+        out["o"][bb, :, :nb], out["lse"][bb, :, :nb] = o[0], lse[0]
+        out["idx"][bb, :, :Tb], out["logg"][bb, :, :Tb] = idx[0], logg[0]
+        out["lse_s"][bb, :, :Tb] = lse_s[0]
+        out["s"][bb, :, :Tb, :Tb] = sb[0]
+        for key in ("dq", "dk", "dv"):
+            out[key][bb, :, :nb] = gr[key][0]
+        out["dlogg"][bb, :, :Tb] = gr["dlogg"][0]
+        out["ds"][bb, :, :Tb, :Tb] = gr["ds"][0]
+    return out
 
 
 # --------------------------------------------------------------------------- work counts

@@ -799,3 +799,38 @@ def test_p18_paged_decode_equals_dense():
                               idx[bb:bb + 1], logg[bb:bb + 1], bs, outer=outer)
             np.testing.assert_array_equal(o[bb], od[0])
             np.testing.assert_array_equal(lse[bb], ld[0])
+
+
+# ---------------------------------------------------------------- P19: ragged training batch
+
+def test_p19_ragged_batch():
+    """A ragged batch whose sequences all have the full length is the dense
+    batch, and a shorter sequence's results depend only on its own tokens:
+    changing the padding (and every other sequence) leaves them unchanged, and
+    its rows past the end carry no result."""
+    bs, n, K = 8, 40, 2
+    w, x = small(seed=41, b=2, hq=2, hkv=1, n=n, d=6, bs=bs, K=K)
+    q, k, v, dout = (x[n_].to(F64) for n_ in ("q", "k", "v", "dout"))
+    s = x["s"].numpy()
+    full = O.ragged_train(q, k, v, dout, [n, n], K, bs, s=s)
+    idx, logg, lse_s = O.select_topk(s, K)
+    o, lse = O.attn_fwd(q, k, v, idx, logg, bs)
+    gr = O.attn_bwd(q, k, v, dout, idx, logg, s, lse_s, bs)
+    np.testing.assert_allclose(full["o"], o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(full["lse"], lse, rtol=0, atol=1e-13)
+    for key in ("dq", "dk", "dv", "dlogg", "ds"):
+        np.testing.assert_allclose(full[key], gr[key], rtol=0, atol=1e-12)
+    lens = [n, 21]
+    r1 = O.ragged_train(q, k, v, dout, lens, K, bs, standin=True)
+    q2, k2, v2, d2 = (t.clone() for t in (q, k, v, dout))
+    for t in (q2, k2, v2, d2):
+        t[1, :, 21:] = 123.0
+        t[0] = torch.randn(t[0].shape, dtype=F64)
+    r2 = O.ragged_train(q2, k2, v2, d2, lens, K, bs, standin=True)
+    for key in ("o", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(r1[key][1], r2[key][1])
+    assert np.all(r1["o"][1, :, 21:] == 0) and np.all(np.isinf(r1["lse"][1, :, 21:]))
+    assert np.all(r1["idx"][1, :, O.n_blocks(21, bs):] == -1)
+    # and the short sequence alone is the dense method on its 21 tokens
+    alone = O.ragged_train(q[1:], k[1:], v[1:], dout[1:], [21], K, bs, standin=True)
+    np.testing.assert_array_equal(alone["o"][0], r1["o"][1])
