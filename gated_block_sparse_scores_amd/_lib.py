@@ -48,7 +48,7 @@ class SasError(RuntimeError):
 class sas_shape(C.Structure):
     _fields_ = [("batch", C.c_int), ("hq", C.c_int), ("hkv", C.c_int), ("seqlen", C.c_int),
                 ("head_dim", C.c_int), ("block", C.c_int), ("dtype", C.c_int),
-                ("scale", C.c_float), ("gate", C.c_int)]
+                ("scale", C.c_float), ("gate", C.c_int), ("seq_lens", C.c_void_p)]
 
 
 class sas_kernel_time(C.Structure):
@@ -66,10 +66,11 @@ class Shape:
     dtype: int = SAS_DTYPE_BF16
     scale: float = 0.0
     gate: int = 0
+    seq_lens: int = 0        # device address of int32 [batch] lengths, 0 = uniform
 
     def c(self) -> sas_shape:
         return sas_shape(self.batch, self.hq, self.hkv, self.seqlen, self.head_dim, self.block,
-                         self.dtype, self.scale, self.gate)
+                         self.dtype, self.scale, self.gate, self.seq_lens or None)
 
 
 _lib = None

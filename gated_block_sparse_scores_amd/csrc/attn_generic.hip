@@ -203,8 +203,10 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
     }
   }
   if (active) {
-    store_row_slice<T, D>(o + qoff, p, acc, 1.0f / lrun);
-    if (p == 0) lse[((size_t)b * dm.hq + h) * dm.n + i] = mrun + logf(lrun);
+    // ragged batch: rows at or past this sequence's end carry no result
+    const bool pad = dm.seq_lens && i >= min(max(dm.seq_lens[b], 0), dm.n);
+    store_row_slice<T, D>(o + qoff, p, acc, pad ? 0.0f : 1.0f / lrun);
+    if (p == 0) lse[((size_t)b * dm.hq + h) * dm.n + i] = pad ? INFINITY : mrun + logf(lrun);
   }
 }
 
@@ -499,7 +501,7 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(
   if (!ds) return;
   for (int m = threadIdx.x; m < T; m += blockDim.x) {
     float val = 0.0f;
-    if (m < t) {
+    if (m < t && ls > -INFINITY) {  // rows without history (or past a sequence's end): 0
       float own = 0.0f;
       for (int sl = 0; sl < K; ++sl)
         if (im[sl] == m) own = dl[sl];

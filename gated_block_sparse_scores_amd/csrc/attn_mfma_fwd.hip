@@ -78,6 +78,19 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   const int g = lane >> 5, c = lane & 31;
   const int h = kv * dm.g + chunk * HPW + (wave >> 1);
   const int qt = wave & 1;  // which 32-row half of the query block
+  const int qi = qt * 32 + c;  // query row within the block
+  // ragged batch: rows at or past this sequence's end carry no result
+  const int nlen = dm.seq_lens ? min(max(dm.seq_lens[b], 0), dm.n) : dm.n;
+  const size_t row = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
+  if (t * BS >= nlen) {  // the whole tile (uniform over the workgroup)
+    if (g == 0) lse[row] = INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<uint2*>(o + row * D + dt * 32 + r4 * 8 + g * 4) = make_uint2(0u, 0u);
+    return;
+  }
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
   if (threadIdx.x == 0) {
@@ -112,7 +125,6 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   float mref = -INFINITY;  // reference max (log2 units) of this lane's query
   float lsum = 0.0f;       // sum of 2^(z - mref) over this lane's keys
   const float sc2 = dm.scale * LOG2E;
-  const int qi = qt * 32 + c;  // query row within the block
 
   __syncthreads();
   const int nb = nblk;
@@ -196,11 +208,11 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     if (bi + 1 < nb) step(bi + 1, K1, V1, K0, V0);
   }
 
-  // Normalise and store o (bf16) and LSE (natural log).
-  const size_t row = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
+  // Normalise and store o (bf16) and LSE (natural log); padding rows: 0, +inf.
+  const bool pad = t * BS + qi >= nlen;
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv = 1.0f / ltot;
-  if (g == 0) lse[row] = (mref + log2f(ltot)) * LN2;
+  const float inv = pad ? 0.0f : 1.0f / ltot;
+  if (g == 0) lse[row] = pad ? INFINITY : (mref + log2f(ltot)) * LN2;
   bf16_t* op = o + row * D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)

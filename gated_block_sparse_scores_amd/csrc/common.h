@@ -1,6 +1,8 @@
 // Device helpers shared by the HIP kernels (gfx950, wave64).
 #pragma once
 
+#include "internal.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,6 +56,18 @@ __device__ __forceinline__ float gate_log(float s, float lse, int act) {
   if (act == 1) return -(fmaxf(-s, 0.0f) + log1pf(expf(-fabsf(s))));
   if (act == 2) return s;
   return s - lse;
+}
+
+// History length of selection row t of (batch, KV head) row bk.  Training rows
+// (row_offset 0) past the sequence's last block have none; decode rows see the
+// sequence's own (L_b - 1) / bs history blocks.
+__device__ __forceinline__ int row_history(int t, int row_offset, int C, const RowLens& rl,
+                                           size_t bk) {
+  const int ct = min(t + row_offset, C);
+  if (!rl.lens) return ct;
+  const int lb = min(max(rl.lens[bk / rl.hkv], 0), rl.lmax);
+  if (row_offset == 0) return t < (lb + rl.bs - 1) / rl.bs ? ct : 0;
+  return min(ct, max(lb - 1, 0) / rl.bs);
 }
 
 // Inverse of order_key.

@@ -29,6 +29,13 @@ struct KvView {
   const int32_t* seq_lens;
 };
 
+// Per-sequence lengths of a ragged batch for the selection kernels: (batch,
+// KV head) row bk belongs to sequence bk / hkv.
+struct RowLens {
+  const int32_t* lens;  // nullptr: every sequence is full
+  int lmax, bs, hkv;
+};
+
 struct Dims {
   int b, hq, hkv, g, n, d, bs, T, K;
   float scale;
@@ -36,17 +43,21 @@ struct Dims {
   int act;     // gate activation: 0 softmax, 1 sigmoid, 2 raw logit
   bool outer;  // gates applied after the softmax
   bool ste;    // hard forward, straight-through backward
+  const int32_t* seq_lens;  // ragged batch: per-sequence lengths (device), or nullptr
 };
 
 // ---- selection (select.hip)
+// lens (optional): sequence b pools only its first lens[b] tokens (blocks past
+// them are 0).
 hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, int group,
-                             int n, int d, int bs, bool out_bf16, void* out, hipStream_t st);
+                             int n, int d, int bs, bool out_bf16, void* out, hipStream_t st,
+                             const int32_t* lens = nullptr);
 // Gate LSE + Top-K per row; with s == NULL the stand-in scores are formed
 // from qbar / kbar first (written to s_out).
 hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
                        int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
                        int row_offset, int K, int act, int32_t* idx, float* logg, float* lse_s,
-                       hipStream_t st);
+                       hipStream_t st, const RowLens& rl = RowLens{});
 // Largest Top-K of the training path (selection with C <= kLongHistory, forward,
 // backward): slots are stored as uint8 in the inverse map, 0xFE and 0xFF being
 // markers.  Decode and the two-stage selection take K <= 64.
@@ -57,7 +68,8 @@ size_t select_workspace_bytes(int rows_bk, int T, int C, int K);
 hipError_t launch_select_long(const float* s, const float* qbar, const void* kbar,
                               bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
                               int T, int C, int row_offset, int K, int act, float* s_out,
-                              int32_t* idx, float* logg, float* lse_s, void* ws, hipStream_t st);
+                              int32_t* idx, float* logg, float* lse_s, void* ws, hipStream_t st,
+                              const RowLens& rl = RowLens{});
 
 // ---- attention, portable fp32-arithmetic kernels (attn_generic.hip)
 hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
@@ -92,12 +104,12 @@ size_t decode_workspace_bytes(const Dims& dm);
 // cache with the query pooled in-kernel, then the decode kernel merging the
 // chunk candidates itself, then the LSE merge.
 constexpr int kSelectChunk = 256;  // history blocks per selection chunk
-// Decode rows (T = 1): with seq_lens, row r = b * hkv + kv has history
-// min(C, (clamp(seq_lens[b], 1, L) - 1) / bs) blocks.
+// Decode rows (T = 1, row offset C); with rl.lens each sequence ranks its own
+// (L_b - 1) / bs history blocks.
 hipError_t launch_select_chunks_rawq(const uint16_t* q, int qgroup, const void* kbar,
                                      bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
-                                     int C, int K, const int32_t* seq_lens, int L, int bs,
-                                     int hkv, uint64_t* cand, float2* stats, hipStream_t st);
+                                     int C, int K, const RowLens& rl, uint64_t* cand,
+                                     float2* stats, hipStream_t st);
 bool decode_mfma_path(const Dims& dm);
 hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, int nchunk,
                               const void* q, const uint64_t* cand, const float2* stats,

@@ -139,6 +139,7 @@ Dims make_dims(const sas_shape* s, int K) {
   d.act = s->gate & SAS_GATE_ACTIVATION_MASK;
   d.outer = (s->gate & SAS_GATE_OUTER) != 0;
   d.ste = (s->gate & SAS_GATE_STE) != 0;
+  d.seq_lens = s->seq_lens;
   return d;
 }
 
@@ -187,7 +188,8 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
   if (!aligned16(x)) return SAS_ERR_INVALID_ARG;  // 16-byte vector loads
   return launch_status(sas::launch_block_pool(
       x, shape->dtype == SAS_DTYPE_BF16, shape->batch, heads, group, shape->seqlen,
-      shape->head_dim, shape->block, out_dtype == SAS_DTYPE_BF16, out, (hipStream_t)stream));
+      shape->head_dim, shape->block, out_dtype == SAS_DTYPE_BF16, out, (hipStream_t)stream,
+      shape->seq_lens));
 }
 
 size_t sas_select_topk_workspace_size(const sas_shape* shape, int T, int C, int K) {
@@ -222,15 +224,20 @@ sas_status sas_select_topk(const sas_shape* shape, int T, int C, int row_offset,
     if (!aligned16(qbar) || !aligned16(kbar)) return SAS_ERR_INVALID_ARG;
     scale = shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
   }
+  sas::RowLens rl{};
+  if (shape->seq_lens) {  // ragged batch: shape->seqlen and ->block describe the tokens
+    if (shape->seqlen <= 0 || shape->block <= 0) return SAS_ERR_INVALID_ARG;
+    rl = sas::RowLens{shape->seq_lens, shape->seqlen, shape->block, shape->hkv};
+  }
   const size_t need = sas::select_workspace_bytes(rows_bk, T, C, K);
   if (need > 0 && (!workspace || ws_bytes < need)) return SAS_ERR_WORKSPACE;
   if (C > sas::kLongHistory)
     return launch_status(sas::launch_select_long(
         s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim, scale, rows_bk, T,
-        C, row_offset, K, act, s_out, idx, logg, lse_s, workspace, st));
+        C, row_offset, K, act, s_out, idx, logg, lse_s, workspace, st, rl));
   return launch_status(sas::launch_topk(s, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                         shape->head_dim, scale, s_out, rows_bk, T, C,
-                                        row_offset, K, act, idx, logg, lse_s, st));
+                                        row_offset, K, act, idx, logg, lse_s, st, rl));
 }
 
 size_t sas_attn_fwd_workspace_size(const sas_shape* shape, int K) {
@@ -321,7 +328,7 @@ sas_status sas_decode(const sas_shape* shape, int cache_len, int K, const void* 
   const Dims dm = make_dims(shape, K);
   const size_t need = sas::decode_workspace_bytes(dm);
   if (!workspace || ws_bytes < need) return SAS_ERR_WORKSPACE;
-  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, nullptr};
+  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, shape->seq_lens};
   return launch_status(sas::launch_decode(dm, L, kvv, q, idx, dm.ste ? nullptr : logg, o, lse,
                                           workspace, (hipStream_t)stream));
 }
@@ -391,7 +398,6 @@ sas_status decode_step_impl(const sas_shape* shape, int K, const void* q, const 
   const StepLayout lay = step_layout(shape, K);
   if (kbar_ld < lay.C) return SAS_ERR_INVALID_ARG;
   if (lay.C > 16384) return SAS_ERR_UNSUPPORTED;
-  if (kvv.seq_lens && !lay.fused) return SAS_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < lay.bytes) return SAS_ERR_WORKSPACE;
   const Dims dm = make_dims(shape, K);
   const hipStream_t st = (hipStream_t)stream;
@@ -400,12 +406,13 @@ sas_status decode_step_impl(const sas_shape* shape, int K, const void* q, const 
       shape->scale > 0.0f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
   const int rows = shape->batch * shape->hkv;
   const int G = shape->hq / shape->hkv;
+  const sas::RowLens rl{kvv.seq_lens, L, shape->block, shape->hkv};
   if (lay.fused) {
     uint64_t* cand = (uint64_t*)(ws + lay.cand);
     float2* stats = (float2*)(ws + lay.stats);
     SAS_LAUNCH(sas::launch_select_chunks_rawq(
         (const uint16_t*)q, G, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld, shape->head_dim,
-        scale, rows, lay.C, K, kvv.seq_lens, L, shape->block, shape->hkv, cand, stats, st));
+        scale, rows, lay.C, K, rl, cand, stats, st));
     return launch_status(sas::launch_decode_step(dm, L, kvv, lay.C, lay.nchunk, q, cand, stats,
                                                  gated && !dm.ste, idx, logg, lse_s, o, lse,
                                                  ws + lay.part, st));
@@ -423,11 +430,11 @@ sas_status decode_step_impl(const sas_shape* shape, int K, const void* q, const 
     SAS_LAUNCH(sas::launch_select_long(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                        shape->head_dim, scale, rows, 1, lay.C, lay.C, K, dm.act,
                                        s_out, idx_w, logg_w, lse_s_w, ws + lay.sel + s_bytes,
-                                       st));
+                                       st, rl));
   else
     SAS_LAUNCH(sas::launch_topk(nullptr, qbar, kbar, kbar_dtype == SAS_DTYPE_BF16, kbar_ld,
                                 shape->head_dim, scale, s_out, rows, 1, lay.C, lay.C, K, dm.act,
-                                idx_w, logg_w, lse_s_w, st));
+                                idx_w, logg_w, lse_s_w, st, rl));
   return launch_status(sas::launch_decode(dm, L, kvv, q, idx_w,
                                           (gated && !dm.ste) ? logg_w : nullptr, o, lse,
                                           ws + lay.dec, st));
@@ -459,7 +466,7 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
   const int cl = cache_len == 0 ? L : cache_len;
   if (cl < L) return SAS_ERR_INVALID_ARG;
   if (!kcache || !vcache || !aligned16(kcache) || !aligned16(vcache)) return SAS_ERR_INVALID_ARG;
-  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, nullptr};
+  const sas::KvView kvv{kcache, vcache, cl, nullptr, 0, 0, shape->seq_lens};
   return decode_step_impl(shape, K, q, kbar, kbar_dtype, kbar_ld, kvv, gated, o, lse, idx, logg,
                           lse_s, workspace, ws_bytes, stream);
 }

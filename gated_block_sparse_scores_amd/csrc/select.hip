@@ -20,14 +20,16 @@ namespace sas {
 template <typename Tin, int D>
 __global__ void __launch_bounds__(256) pool_kernel(const Tin* __restrict__ x, int heads,
                                                    int group, int n, int bs, int out_bf16,
-                                                   void* __restrict__ out) {
+                                                   void* __restrict__ out,
+                                                   const int32_t* __restrict__ lens) {
   constexpr int E = 16 / (int)sizeof(Tin);  // values per 16-byte load
   constexpr int LPR = D / E;                // lanes per row
   constexpr int RPP = 256 / LPR;            // rows per pass
   __shared__ double red[RPP][D];
   const int t = blockIdx.x, ho = blockIdx.y, b = blockIdx.z;
   const int T = gridDim.x, hout = gridDim.y;
-  const int lo = t * bs, hi = min(lo + bs, n);
+  const int nb = lens ? min(max(lens[b], 0), n) : n;  // this sequence's tokens
+  const int lo = t * bs, hi = min(lo + bs, nb);
   const int li = threadIdx.x % LPR, ri = threadIdx.x / LPR;
   double acc[E];
 #pragma unroll
@@ -64,7 +66,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const Tin* __restrict__ x, in
     double sum = 0.0;
 #pragma unroll
     for (int r = 0; r < RPP; ++r) sum += red[r][col];
-    const double mean = sum / (double)((hi - lo) * group);
+    const double mean = hi > lo ? sum / (double)((hi - lo) * group) : 0.0;
     const float f = (float)mean;
     const size_t o = (((size_t)b * hout + ho) * T + t) * D + col;
     if (out_bf16)
@@ -75,13 +77,14 @@ __global__ void __launch_bounds__(256) pool_kernel(const Tin* __restrict__ x, in
 }
 
 hipError_t launch_block_pool(const void* x, bool in_bf16, int batch, int heads, int group,
-                             int n, int d, int bs, bool out_bf16, void* out, hipStream_t st) {
+                             int n, int d, int bs, bool out_bf16, void* out, hipStream_t st,
+                             const int32_t* lens) {
   const int T = (n + bs - 1) / bs;
   dim3 grid(T, heads / group, batch);
   ProfScope ps("block_pool", st);
 #define SAS_POOL(TIN, DD)                                                                 \
   hipLaunchKernelGGL((pool_kernel<TIN, DD>), grid, dim3(256), 0, st, (const TIN*)x, heads, \
-                     group, n, bs, (int)out_bf16, out)
+                     group, n, bs, (int)out_bf16, out, lens)
   if (in_bf16 && d == 128)
     SAS_POOL(bf16_t, 128);
   else if (in_bf16)
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
     const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
     int kbar_ld, int d, double scale, float* __restrict__ s_out, int T, int C, int row_offset,
     int K, int act, int32_t* __restrict__ idx, float* __restrict__ logg,
-    float* __restrict__ lse_s) {
+    float* __restrict__ lse_s, RowLens rl) {
   extern __shared__ uint32_t keys[];  // C keys (then, with STANDIN, C scores)
   __shared__ int hist[256];
   __shared__ int iscr[16];
@@ -177,7 +180,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
   const int tid = threadIdx.x, nth = blockDim.x;
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
-  const int ct = min(t + row_offset, C);
+  const int ct = row_history(t, row_offset, C, rl, row / T);
   const float* srow = s + row * (size_t)C;
   if constexpr (STANDIN) {
     float* sv = reinterpret_cast<float*>(keys + C);
@@ -320,8 +323,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     const float* __restrict__ s, const float* __restrict__ qbar, const bf16_t* __restrict__ qraw,
     int qgroup, const Tk* __restrict__ kbar, int kbar_ld, int d, double scale, int T, int C,
     int row_offset, int K, int nchunk, float* __restrict__ s_out, uint64_t* __restrict__ cand,
-    float2* __restrict__ stats, const int32_t* __restrict__ seq_lens, int len_max, int len_bs,
-    int len_hkv) {
+    float2* __restrict__ stats, RowLens rl) {
   __shared__ uint64_t keys[kChunk];
   __shared__ float sval[kChunk];
   __shared__ float fscr[16];
@@ -330,11 +332,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   const size_t row = blockIdx.y;
   const int t = (int)(row % T);
   const size_t bk = row / T;
-  int ct = min(t + row_offset, C);
-  if (seq_lens) {  // ragged decode batch: this sequence's own history
-    const int lb = min(max(seq_lens[bk / len_hkv], 1), len_max);
-    ct = min(ct, (lb - 1) / len_bs);
-  }
+  const int ct = row_history(t, row_offset, C, rl, bk);
   const int m0 = chunk * kChunk;
   const int tid = threadIdx.x;
   const int m = m0 + tid;
@@ -409,7 +407,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
 __global__ void __launch_bounds__(256) select_merge_kernel(
     const uint64_t* __restrict__ cand, const float2* __restrict__ stats, int T, int C,
     int row_offset, int K, int nchunk, int act, int32_t* __restrict__ idx,
-    float* __restrict__ logg, float* __restrict__ lse_s) {
+    float* __restrict__ logg, float* __restrict__ lse_s, RowLens rl) {
   extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
   __shared__ int widx[64];
   __shared__ float wval[64];
@@ -418,7 +416,7 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
   __shared__ double dscr[16];
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
-  const int ct = min(t + row_offset, C);
+  const int ct = row_history(t, row_offset, C, rl, row / T);
   const int nc = nchunk * K;
   const uint64_t* crow = cand + row * (size_t)nc;
   for (int i = threadIdx.x; i < nc; i += blockDim.x) lists[i] = crow[i];
@@ -485,7 +483,7 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
                               bool kbar_bf16, int kbar_ld, int d, double scale, int rows_bk,
                               int T, int C, int row_offset, int K, int act, float* s_out,
                               int32_t* idx, float* logg, float* lse_s, void* ws,
-                              hipStream_t st) {
+                              hipStream_t st, const RowLens& rl) {
   const size_t rows = (size_t)rows_bk * T;
   const int nchunk = (C + kChunk - 1) / kChunk;
   uint64_t* cand = (uint64_t*)ws;
@@ -497,13 +495,11 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
     if (kbar_bf16)
       hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, s, qbar,
                          (const bf16_t*)nullptr, 0, (const bf16_t*)kbar, kbar_ld, d, scale, T, C,
-                         row_offset, K, nchunk, s_out, cand, stats, (const int32_t*)nullptr, 0,
-                         1, 1);
+                         row_offset, K, nchunk, s_out, cand, stats, rl);
     else
       hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, s, qbar,
                          (const bf16_t*)nullptr, 0, (const float*)kbar, kbar_ld, d, scale, T, C,
-                         row_offset, K, nchunk, s_out, cand, stats, (const int32_t*)nullptr, 0,
-                         1, 1);
+                         row_offset, K, nchunk, s_out, cand, stats, rl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -511,15 +507,15 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
     ProfScope ps("select_merge", st);
     hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256),
                        (size_t)2 * nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
-                       K, nchunk, act, idx, logg, lse_s);
+                       K, nchunk, act, idx, logg, lse_s, rl);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kbar,
                                      bool kbar_bf16, int kbar_ld, int d, double scale, int rows,
-                                     int C, int K, const int32_t* seq_lens, int L, int bs,
-                                     int hkv, uint64_t* cand, float2* stats, hipStream_t st) {
+                                     int C, int K, const RowLens& rl, uint64_t* cand,
+                                     float2* stats, hipStream_t st) {
   const int nchunk = (C + kChunk - 1) / kChunk;
   if (nchunk == 0) return hipSuccess;
   ProfScope ps("step_select_chunk", st);
@@ -527,33 +523,33 @@ hipError_t launch_select_chunks_rawq(const bf16_t* q, int qgroup, const void* kb
   if (kbar_bf16)
     hipLaunchKernelGGL(select_chunk_kernel<bf16_t>, grid, dim3(256), 0, st, (const float*)nullptr,
                        (const float*)nullptr, q, qgroup, (const bf16_t*)kbar, kbar_ld, d, scale,
-                       1, C, C, K, nchunk, (float*)nullptr, cand, stats, seq_lens, L, bs, hkv);
+                       1, C, C, K, nchunk, (float*)nullptr, cand, stats, rl);
   else
     hipLaunchKernelGGL(select_chunk_kernel<float>, grid, dim3(256), 0, st, (const float*)nullptr,
                        (const float*)nullptr, q, qgroup, (const float*)kbar, kbar_ld, d, scale, 1,
-                       C, C, K, nchunk, (float*)nullptr, cand, stats, seq_lens, L, bs, hkv);
+                       C, C, K, nchunk, (float*)nullptr, cand, stats, rl);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool kbar_bf16,
                        int kbar_ld, int d, double scale, float* s_out, int rows_bk, int T, int C,
                        int row_offset, int K, int act, int32_t* idx, float* logg,
-                       float* lse_s, hipStream_t st) {
+                       float* lse_s, hipStream_t st, const RowLens& rl) {
   const size_t rows = (size_t)rows_bk * T;
   const size_t lds = (size_t)(C > 0 ? C : 1) * sizeof(uint32_t) * (s ? 1 : 2);
   ProfScope ps("topk", st);
   if (s)
     hipLaunchKernelGGL((topk_kernel<float, false>), dim3((unsigned)rows), dim3(256), lds, st, s,
                        nullptr, nullptr, 0, 0, 0.0, nullptr, T, C, row_offset, K, act, idx, logg,
-                       lse_s);
+                       lse_s, rl);
   else if (kbar_bf16)
     hipLaunchKernelGGL((topk_kernel<bf16_t, true>), dim3((unsigned)rows), dim3(256), lds, st,
                        nullptr, qbar, (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, act, idx, logg, lse_s);
+                       row_offset, K, act, idx, logg, lse_s, rl);
   else
     hipLaunchKernelGGL((topk_kernel<float, true>), dim3((unsigned)rows), dim3(256), lds, st,
                        nullptr, qbar, (const float*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, act, idx, logg, lse_s);
+                       row_offset, K, act, idx, logg, lse_s, rl);
   return hipGetLastError();
 }
 

@@ -124,12 +124,15 @@ __device__ __forceinline__ void store8(Tx* p, const float (&v)[8]) {
 template <typename Tx, int D>
 __global__ void __launch_bounds__(256) pool_spread_kernel(Tx* __restrict__ x,
                                                           const float* __restrict__ xbar,
-                                                          int heads, int group, int n, int bs) {
+                                                          int heads, int group, int n, int bs,
+                                                          const int32_t* __restrict__ lens) {
   constexpr int VPR = D / 8;  // vectors per row
   const int bh = blockIdx.y;
   const int h = bh % heads, b = bh / heads;
   const int T = (n + bs - 1) / bs;
-  const int nvec = n * VPR;
+  // ragged batch: only this sequence's own rows, n_t counted within them
+  const int nlen = lens ? min(max(lens[b], 0), n) : n;
+  const int nvec = nlen * VPR;
   Tx* plane = x + (size_t)bh * n * D;
   const float* sbase = xbar + ((size_t)b * (heads / group) + h / group) * (size_t)T * D;
   float v[kSpreadVec][8], a[kSpreadVec][8];
@@ -154,7 +157,7 @@ __global__ void __launch_bounds__(256) pool_spread_kernel(Tx* __restrict__ x,
     if (e < nvec) {
       const int i = e / VPR, c = (e % VPR) * 8;
       const int t = i / bs;
-      const float den = (float)(group * min(bs, n - t * bs));
+      const float den = (float)(group * min(bs, nlen - t * bs));
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[k][q] += a[k][q] / den;
       store8(plane + (size_t)i * D + c, v[k]);
@@ -189,7 +192,7 @@ hipError_t launch_selector_bwd(const Dims& dm, const float* ds, const float* qba
     const float* xb = which ? dkbar : dqbar;
 #define SAS_SPREAD(TX, DD)                                                                    \
   hipLaunchKernelGGL((pool_spread_kernel<TX, DD>), grid, dim3(256), 0, st, (TX*)x, xb, heads, \
-                     group, dm.n, dm.bs)
+                     group, dm.n, dm.bs, dm.seq_lens)
     if (dm.bf16 && dm.d == 128)
       SAS_SPREAD(bf16_t, 128);
     else if (dm.bf16)

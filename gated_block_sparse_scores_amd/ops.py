@@ -22,8 +22,15 @@ def _f32(shape, dev):
     return torch.empty(shape, dtype=torch.float32, device=dev)
 
 
+def _lens_ptr(seq_lens) -> int:
+    if seq_lens is None:
+        return 0
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous()
+    return seq_lens.data_ptr()
+
+
 def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, scale: float = 0.0,
-             seqlen: Optional[int] = None, gate: int = 0) -> Shape:
+             seqlen: Optional[int] = None, gate: int = 0, seq_lens=None) -> Shape:
     """Shape of a training call (q [b,hq,N,d], k [b,hkv,N,d]) or, with q of
     rank 3, of a decode call (seqlen = valid cache length); gate = sas_gate
     bits (_lib.gate_code)."""
@@ -33,17 +40,17 @@ def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, scale: float = 0.0,
         b, hq, d = q.shape
         n = seqlen
     return Shape(b, hq, k.shape[1], n if seqlen is None else seqlen, d, block,
-                 L.dtype_code(q.dtype), scale, gate)
+                 L.dtype_code(q.dtype), scale, gate, _lens_ptr(seq_lens))
 
 
 def block_pool(x: torch.Tensor, block: int, group: int = 1,
-               out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+               out_dtype: torch.dtype = torch.float32, stream=None, seq_lens=None) -> torch.Tensor:
     """Mean of x [b,H,N,d] over each block's tokens and over groups of `group`
     heads -> [b, H/group, ceil(N/block), d]."""
     b, H, n, d = x.shape
     T = -(-n // block)
     out = torch.empty((b, H // group, T, d), dtype=out_dtype, device=x.device)
-    sh = Shape(b, H, H, n, d, block, L.dtype_code(x.dtype))
+    sh = Shape(b, H, H, n, d, block, L.dtype_code(x.dtype), seq_lens=_lens_ptr(seq_lens))
     L.sas_block_pool(sh, x, H, group, L.dtype_code(out_dtype), out, stream)
     return out
 
@@ -52,7 +59,7 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
                 s: Optional[torch.Tensor] = None, qbar: Optional[torch.Tensor] = None,
                 kbar: Optional[torch.Tensor] = None, head_dim: int = 0, scale: float = 0.0,
                 stream=None, device=None, workspace: Optional[torch.Tensor] = None,
-                gate: int = 0):
+                gate: int = 0, seq_lens=None, seqlen: int = 1, block: int = 1):
     """Returns (idx, logg, lse_s, s_used).  With s None the stand-in score from
     qbar/kbar is formed on the device and returned as s_used."""
     dev = device or (s.device if s is not None else qbar.device)
@@ -66,7 +73,9 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
         kdt = L.dtype_code(kbar.dtype)
         kld = kbar.shape[2]
         head_dim = qbar.shape[-1]
-    sh = Shape(batch, hkv, hkv, 1, head_dim or 1, 1, L.SAS_DTYPE_F32, scale, gate)
+    # a ragged batch (seq_lens) needs the token count seqlen and the block size
+    sh = Shape(batch, hkv, hkv, seqlen, head_dim or 1, block, L.SAS_DTYPE_F32, scale, gate,
+               _lens_ptr(seq_lens))
     ws_n = L.sas_select_topk_workspace_size(sh, T, C, K)
     if ws_n and (workspace is None or workspace.numel() < ws_n):
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
@@ -75,8 +84,9 @@ def select_topk(batch: int, hkv: int, T: int, C: int, K: int, *, row_offset: int
     return idx, logg, lse_s, (s if s is not None else s_out)
 
 
-def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None, gate: int = 0):
-    sh = shape_of(q, k, block, scale, gate=gate)
+def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None, gate: int = 0,
+             seq_lens=None):
+    sh = shape_of(q, k, block, scale, gate=gate, seq_lens=seq_lens)
     K = idx.shape[-1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:3], q.device)
@@ -88,8 +98,8 @@ def attn_fwd(q, k, v, idx, logg, block: int, scale: float = 0.0, stream=None, ga
 
 def attn_bwd(q, k, v, o, dout, lse, idx, logg, s, lse_s, block: int, scale: float = 0.0,
              want_ds: bool = True, stream=None, workspace: Optional[torch.Tensor] = None,
-             gate: int = 0):
-    sh = shape_of(q, k, block, scale, gate=gate)
+             gate: int = 0, seq_lens=None):
+    sh = shape_of(q, k, block, scale, gate=gate, seq_lens=seq_lens)
     K = idx.shape[-1]
     T = idx.shape[2]
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -106,9 +116,11 @@ def attn_bwd(q, k, v, o, dout, lse, idx, logg, s, lse_s, block: int, scale: floa
 
 
 def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0,
-           stream=None, workspace: Optional[torch.Tensor] = None, gate: int = 0):
-    """q [b,hq,d]; caches [b,hkv,cache_len,d]; idx/logg [b,hkv,K]."""
-    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate)
+           stream=None, workspace: Optional[torch.Tensor] = None, gate: int = 0,
+           seq_lens=None):
+    """q [b,hq,d]; caches [b,hkv,cache_len,d]; idx/logg [b,hkv,K]; seq_lens
+    (ragged batch) the valid length of each sequence, L_ the longest."""
+    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate, seq_lens=seq_lens)
     K = idx.shape[-1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:2], q.device)
@@ -122,11 +134,11 @@ def decode(q, kcache, vcache, L_: int, idx, logg, block: int, scale: float = 0.0
 
 def decode_step(q, kbar, kcache, vcache, L_: int, K: int, block: int, gated: bool = True,
                 scale: float = 0.0, with_selection: bool = True, stream=None,
-                workspace: Optional[torch.Tensor] = None, gate: int = 0):
+                workspace: Optional[torch.Tensor] = None, gate: int = 0, seq_lens=None):
     """One fused decode step with the stand-in selector: q [b,hq,d]; kbar the
     pooled-key cache [b,hkv,>=C,d]; caches [b,hkv,cache_len,d].  Returns
     (o, lse) or, with with_selection, (o, lse, idx, logg, lse_s)."""
-    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate)
+    sh = shape_of(q, kcache, block, scale, seqlen=L_, gate=gate, seq_lens=seq_lens)
     b, hkv = kcache.shape[0], kcache.shape[1]
     o = torch.empty_like(q)
     lse = _f32(q.shape[:2], q.device)
@@ -144,13 +156,14 @@ def decode_step(q, kbar, kcache, vcache, L_: int, K: int, block: int, gated: boo
 
 
 def selector_bwd(ds, qbar, kbar, block: int, seqlen: int, hq: int, dq=None, dk=None,
-                 scale: float = 0.0, stream=None):
+                 scale: float = 0.0, stream=None, seq_lens=None):
     """Stand-in selector backward of training rows: ds [b,hkv,T,T], qbar/kbar
     fp32 [b,hkv,T,d] -> (dqbar, dkbar) fp32 [b,hkv,T,d]; dq [b,hq,N,d] and
     dk [b,hkv,N,d], when given, receive the mean pools' adjoints in place."""
     b, hkv, T, d = qbar.shape
     dt = dq.dtype if dq is not None else (dk.dtype if dk is not None else torch.float32)
-    sh = Shape(b, hq, hkv, seqlen, d, block, L.dtype_code(dt), scale)
+    sh = Shape(b, hq, hkv, seqlen, d, block, L.dtype_code(dt), scale,
+               seq_lens=_lens_ptr(seq_lens))
     dqbar = torch.empty_like(qbar)
     dkbar = torch.empty_like(kbar)
     L.sas_selector_bwd(sh, ds, qbar, kbar, dqbar, dkbar, dq, dk, stream)

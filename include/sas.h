@@ -105,6 +105,15 @@ typedef struct {
   sas_dtype dtype;
   float scale;   /* logit scale; 0 selects 1/sqrt(head_dim) */
   int gate;      /* sas_gate bits; 0 = SAS (softmax, inner, soft) */
+  /* Ragged batch (optional, device int32 [batch]; NULL: every sequence has
+   * length seqlen).  Training calls: sequence b is its first seq_lens[b]
+   * tokens of the padded [.., seqlen, d] tensors (clamped to [0, seqlen]) and
+   * is computed exactly as if alone; rows past its end are padding, which must
+   * hold finite values and carry no result (o = 0, lse = +inf, gradients 0;
+   * selection rows past its last block: idx -1, logg 0, lse_s -inf, ds 0).
+   * Decode calls: the valid cache length of sequence b (clamped to
+   * [1, seqlen]), its new token at seq_lens[b] - 1. */
+  const int32_t* seq_lens;
 } sas_shape;
 
 /* Human-readable name of a status code (static string). */
@@ -269,9 +278,7 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
  *   sas_decode_workspace_size.
  * sas_decode_step_paged: as sas_decode_step (kbar [b, hkv, kbar_ld, d] stays a
  *   dense per-sequence cache, rows m < C_b read); each sequence ranks its own
- *   C_b history blocks.  Supported where sas_decode_step takes its fused path
- *   (bf16, head_dim 128, block 64, ceil(C / 256) * K <= 2048 for C of seqlen);
- *   workspace size as sas_decode_step_workspace_size.
+ *   C_b history blocks; workspace size as sas_decode_step_workspace_size.
  * ---------------------------------------------------------------------- */
 sas_status sas_decode_paged(const sas_shape* shape, int K, const void* q, const void* kpages,
                             const void* vpages, int num_pages, const int32_t* block_table,

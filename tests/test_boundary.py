@@ -220,10 +220,16 @@ def test_paged_decode_checks():
     assert call(bt_ld=15) == L.SAS_ERR_INVALID_ARG          # table narrower than seqlen
     assert call(K=65) == L.SAS_ERR_UNSUPPORTED
     assert call(n=ws - 1) == L.SAS_ERR_WORKSPACE
-    # the fused paged step needs the fused shapes (here block 32)
-    sh32 = shape(seqlen=1000, hq=8, hkv=2, block=32)
-    n = lib.sas_decode_step_workspace_size(C.byref(sh32), 8)
-    st = lib.sas_decode_step_paged(C.byref(sh32), 8, FAKE, FAKE, L.SAS_DTYPE_BF16, 64, FAKE,
-                                   FAKE, 40, FAKE, 32, FAKE, 1, FAKE, FAKE, None, None, None,
-                                   FAKE, n, None)
-    assert st == L.SAS_ERR_UNSUPPORTED
+    # the paged step: the same host-side checks (all fail before any launch)
+    n = lib.sas_decode_step_workspace_size(C.byref(sh), 8)
+
+    def step(K=8, table=FAKE, bt_ld=16, kbar_ld=64, n_=n):
+        return lib.sas_decode_step_paged(C.byref(sh), K, FAKE, FAKE, L.SAS_DTYPE_BF16, kbar_ld,
+                                         FAKE, FAKE, 40, table, bt_ld, FAKE, 1, FAKE, FAKE, None,
+                                         None, None, FAKE, n_, None)
+
+    assert step(K=65) == L.SAS_ERR_UNSUPPORTED
+    assert step(table=None) == L.SAS_ERR_INVALID_ARG
+    assert step(bt_ld=15) == L.SAS_ERR_INVALID_ARG
+    assert step(kbar_ld=14) == L.SAS_ERR_INVALID_ARG         # C = 15 pooled rows needed
+    assert step(n_=n - 1) == L.SAS_ERR_WORKSPACE
