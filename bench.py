@@ -231,7 +231,61 @@ def bench_train(args):
     return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
                 ms_with_kernel_events=ms_events,
                 kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb),
-                gate_variants=None if args.no_variants else bench_gate_variants(args, w, x))
+                gate_variants=None if args.no_variants else bench_gate_variants(args, w, x),
+                ragged=None if args.no_variants else bench_ragged_train(args))
+
+
+def bench_ragged_train(args):
+    """A ragged training batch in the padded layout: 4 sequences of 8192, 6177,
+    3077 and 1024 tokens (padded to 8192), 32/8 heads, d 128, block 64, Top-31,
+    stand-in selector; one step = the same path as the 8K workload with
+    per-sequence lengths.  FLOPs count the selected pairs of each sequence."""
+    import numpy as np
+    import torch
+    import synth
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    lens = [8192, 6177, 3077, 1024]
+    w = synth.workload(2, batch=len(lens))
+    x = synth.train_inputs(w, seed=77, device="cuda")
+    for bb, nb in enumerate(lens):
+        for key in ("q", "k", "v", "dout"):
+            x[key][bb, :, nb:] = 0
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    T, bs = w.nblocks, w.block
+    sh = ops.shape_of(x["q"], x["k"], bs)
+    ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, w.topk), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        qb = ops.block_pool(x["q"], bs, w.group, seq_lens=sl)
+        kb = ops.block_pool(x["k"], bs, 1, seq_lens=sl)
+        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, w.topk, qbar=qb, kbar=kb,
+                                              seq_lens=sl, seqlen=w.seqlen, block=bs)
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, bs, seq_lens=sl)
+        ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s, bs,
+                     workspace=ws, seq_lens=sl)
+        return idx
+
+    idx = step().cpu().numpy()
+    pairs = 0
+    for bb, nb in enumerate(lens):
+        for t in range(-(-nb // bs)):
+            rows = min(bs, nb - t * bs)
+            pairs += (int((idx[bb, :, t] >= 0).sum()) * bs * rows
+                      + w.hkv * rows * (rows + 1) // 2) * w.group
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"seq_lens": lens, "padded_len": w.seqlen, "selected_pairs": pairs,
+            "ms_per_step": round(ms, 4),
+            "TFLOPs": round(12 * w.head_dim * pairs / (ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(sum(lens) / (ms * 1e-3), 1)}
 
 
 def bench_selector_bwd(args, w, gr, qb, kb):
@@ -542,7 +596,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged ragged decode")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the gate-variant and dense-scope training steps")
+                    help="skip the gate-variant, dense-scope and ragged-batch training steps")
     ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
     ap.add_argument("--decode-workloads", default="4,5")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -584,6 +638,7 @@ def main():
             "ms_per_step_with_kernel_events": round(res["ms_with_kernel_events"], 4),
             "selector_bwd": res["selector_bwd"],
             "gate_variants": res["gate_variants"],
+            "ragged_batch": res["ragged"],
         })
     if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")

@@ -88,9 +88,22 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
   const int g = lane >> 5, c = lane & 31;
   const int kt = wave & 1, qh = wave >> 1;  // qh also selects the head-dim half
   const int key = kt * 32 + c;  // key within the block (this lane's column)
+  const size_t kvrow = (bk * dm.n + (size_t)m * BS + key) * D;
+  // ragged batch: a key block past the sequence's end is selected by no row and
+  // its diagonal rows are padding, so dK = dV = 0 (uniform over the workgroup)
+  if (dm.seq_lens && m * BS >= min(max(dm.seq_lens[b], 0), dm.n)) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dd = qh * 64 + dt * 32 + r4 * 8 + g * 4;
+        *reinterpret_cast<uint2*>(dk + kvrow + dd) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(dv + kvrow + dd) = make_uint2(0u, 0u);
+      }
+    return;
+  }
 
   // K, V of the wave's 32 keys as B operands (column = key, k = dims).
-  const size_t kvrow = (bk * dm.n + (size_t)m * BS + key) * D;
   bf16x8 kf[8], vf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
@@ -277,6 +290,18 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   const int h = kv * dm.g + chunk * HPW + (wave >> 1);
   const int qt = wave & 1;
   const int qi = qt * 32 + c;
+  // ragged batch: a query tile past the sequence's end has P = 0 everywhere,
+  // so dQ = 0 and D = 0 (uniform over the workgroup)
+  if (dm.seq_lens && t * BS >= min(max(dm.seq_lens[b], 0), dm.n)) {
+    const size_t prow = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
+    if (g == 0) Dv[prow] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<uint2*>(dq + prow * D + dt * 32 + r4 * 8 + g * 4) = make_uint2(0u, 0u);
+    return;
+  }
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
   if (threadIdx.x == 0) {
