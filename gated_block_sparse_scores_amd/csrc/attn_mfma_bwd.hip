@@ -294,7 +294,7 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   // so dQ = 0 and D = 0 (uniform over the workgroup)
   if (dm.seq_lens && t * BS >= min(max(dm.seq_lens[b], 0), dm.n)) {
     const size_t prow = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
-    if (g == 0) Dv[prow] = 0.0f;
+    if (g == 0 && Dv) Dv[prow] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -331,15 +331,20 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   const float l2 = lse[row] * LOG2E;
   // D = dO . o for this lane's row: 64 dims per lane half, then the halves;
   // also stored for the dK / dV kernel, which runs after this one.
-  float dval = 0.0f;
+  // D as a fixed tree over the 16 chunk partials p(kc, g) (8 dims each):
+  // pairs in kc, then quads, then the two halves (bwd_dval_kernel sums alike)
+  float pd[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
     const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * D + kc * 16 + g * 8);
+    float a = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dval = fmaf((float)of[kc][e], (float)ov[e], dval);
+    for (int e = 0; e < 8; ++e) a = fmaf((float)of[kc][e], (float)ov[e], a);
+    pd[kc] = a;
   }
+  float dval = ((pd[0] + pd[1]) + (pd[2] + pd[3])) + ((pd[4] + pd[5]) + (pd[6] + pd[7]));
   dval += __shfl_xor(dval, 32);
-  if (g == 0) Dv[row] = dval;
+  if (g == 0 && Dv) Dv[row] = dval;  // (null when a separate kernel formed D)
   f32x16 dqa[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -416,8 +421,80 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     }
 }
 
+// D = dO . o per query row, summed exactly as the dQ kernel's prologue sums it,
+// so both kernels see the same D: 16 lanes per row, lane 2 kc + g forms the
+// partial of dims kc * 16 + g * 8 .. +8, then the tree over kc (lane xor 2, 4,
+// 8) and the two halves (xor 1).
+__global__ void __launch_bounds__(256) bwd_dval_kernel(const bf16_t* __restrict__ o,
+                                                     const bf16_t* __restrict__ dout,
+                                                     float* __restrict__ Dv, size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int kc = sub >> 1, g = sub & 1;
+  float a = 0.0f;
+  if (row < rows) {
+    const bf16x8 of = *reinterpret_cast<const bf16x8*>(dout + row * D + kc * 16 + g * 8);
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * D + kc * 16 + g * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaf((float)of[e], (float)ov[e], a);
+  }
+  a += __shfl_xor(a, 2);
+  a += __shfl_xor(a, 4);
+  a += __shfl_xor(a, 8);
+  a += __shfl_xor(a, 1);
+  if (row < rows && sub == 0) Dv[row] = a;
+}
+
+// The dQ kernel's second stream and its fork / join events, per host thread and
+// device (created once, default priority).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int cus = 0;
+};
+
+SideStream* side_stream() {
+  constexpr int kMaxDev = 64;
+  thread_local SideStream per_dev[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    if (hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return nullptr;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+  }
+  return &ss;
+}
+
+void launch_dq(const Dims& dm, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, float* Dv, const int32_t* idx,
+               const float* logg, void* dq, hipStream_t st) {
+  const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
+  ProfScope ps("bwd_dq_mfma", st);
+  auto kern = dm.outer ? bwd_dq_mfma_kernel<true> : bwd_dq_mfma_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm, (const bf16_t*)q,
+                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
+                     lse, Dv, idx, logg, (bf16_t*)dq);
+}
+
+void launch_dkdv(const Dims& dm, const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse, const float* logg, const BwdWorkspace& ws, void* dk,
+                 void* dv, hipStream_t st) {
+  const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
+  ProfScope ps("bwd_dkdv_mfma", st);
+  auto kern = dm.outer ? bwd_dkdv_mfma_kernel<true> : bwd_dkdv_mfma_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm, (const bf16_t*)q,
+                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout, lse, ws.D, logg,
+                     ws.slotmap, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part);
+}
+
 }  // namespace
 
+// Inner and outer gating (templated kernels).
 bool mfma_bwd_supported(const Dims& dm) {
   return dm.bf16 && dm.d == D && dm.bs == BS && dm.n % BS == 0 && dm.g % HPW == 0 &&
          dm.T <= DKV_MAXT;
@@ -429,26 +506,38 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
                            const BwdWorkspace& ws, int* nchunk_out, hipStream_t st) {
   // dlogg is written whole by the dK/dV kernel (one partial per row).
   *nchunk_out = 1;
-  {
-    // dQ first: it also forms D = rowsum(dO o), which dK / dV reads.
-    const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
-    ProfScope ps("bwd_dq_mfma", st);
-    auto kern = dm.outer ? bwd_dq_mfma_kernel<true> : bwd_dq_mfma_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
-                       (const bf16_t*)dout, lse, ws.D, idx, logg, (bf16_t*)dq);
+  // When the dK/dV grid is at most two rounds of its two-per-CU occupancy, its
+  // last workgroups (the longest inverse lists) leave CUs idle: D is then
+  // formed by a small kernel and dQ runs beside dK/dV on a second stream.
+  // Larger grids have no such tail and run dQ (which forms D) first.
+  SideStream* ss = nullptr;
+  const size_t dkdv_wgs = (size_t)dm.b * dm.hkv * dm.T;
+  if (!dm.seq_lens) {
+    ss = side_stream();
+    if (ss && dkdv_wgs > (size_t)4 * ss->cus) ss = nullptr;
+  }
+  if (!ss) {
+    launch_dq(dm, q, k, v, o, dout, lse, ws.D, idx, logg, dq, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
+    return hipGetLastError();
   }
+  const size_t rows = (size_t)dm.b * dm.hq * dm.n;
   {
-    const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
-    ProfScope ps("bwd_dkdv_mfma", st);
-    auto kern = dm.outer ? bwd_dkdv_mfma_kernel<true> : bwd_dkdv_mfma_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout, lse, ws.D, logg,
-                       ws.slotmap, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part);
+    ProfScope ps("bwd_dot", st);
+    hipLaunchKernelGGL(bwd_dval_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
+                       (const bf16_t*)o, (const bf16_t*)dout, ws.D, rows);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+  launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
+  launch_dq(dm, q, k, v, o, dout, lse, nullptr, idx, logg, dq, ss->s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+  return hipStreamWaitEvent(st, ss->join, 0);
 }
 
 }  // namespace sas

@@ -764,7 +764,10 @@ hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, i
                               bool gated, int32_t* idx_out, float* logg_out, float* lse_s_out,
                               void* o, float* lse, void* ws, hipStream_t st) {
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
-  const int bps = decode_blocks_per_split(dm);
+  // Four waves per workgroup whatever the grid: every workgroup merges the
+  // row's chunk candidates first, which 256 threads do four times faster than
+  // 64 (the partial buffer of decode_workspace_bytes covers this split count).
+  const int bps = 4;
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;

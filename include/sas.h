@@ -46,7 +46,10 @@
  *     up to 255 blocks; 1 <= K <= 64 for sas_select_topk with C > 512 and the
  *     decode calls.  Anything else returns SAS_ERR_UNSUPPORTED.
  *   - Calls are thread-safe.  Calls that share output buffers must not
- *     overlap.
+ *     overlap.  Every call is ordered on the caller's stream; sas_attn_bwd may
+ *     fork part of its work onto a second stream of the library's own (one per
+ *     host thread and device, default priority, created on first use) and
+ *     joins it back to the caller's stream with events before returning.
  */
 #ifndef SAS_H
 #define SAS_H

@@ -153,3 +153,29 @@ def test_ragged_decode_dense_cache(case):
     assert max_abs(flogg.cpu(), rlogg) <= GATE_ATOL
     say(f"  decode o {max_abs(o.cpu(), oo):.2e}; step o {max_abs(fo.cpu(), oo):.2e}")
     assert max_abs(fo.cpu(), oo) <= atol and max_abs(flse.cpu(), ol) <= atol
+
+
+def test_full_lengths_equal_dense_bitwise():
+    """A ragged batch whose lengths are all full gives bitwise the results of
+    the plain batch (the ragged backward runs dQ and dK/dV one after the other,
+    the plain one at this size concurrently; both use the same D)."""
+    from gated_block_sparse_scores_amd import ops
+    w = synth.workload(2, seqlen=2048)
+    x = {k_: v_.to(DEV) for k_, v_ in synth.train_inputs(w, seed=5).items() if v_ is not None}
+    T = w.nblocks
+    sl = torch.full((w.batch,), w.seqlen, dtype=torch.int32, device=DEV)
+    outs = []
+    for lens in (None, sl):
+        kw = {} if lens is None else {"seq_lens": lens, "seqlen": w.seqlen, "block": w.block}
+        qb = ops.block_pool(x["q"], w.block, w.group, seq_lens=lens)
+        kb = ops.block_pool(x["k"], w.block, 1, seq_lens=lens)
+        idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, w.topk, qbar=qb, kbar=kb, **kw)
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block, seq_lens=lens)
+        gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s, w.block,
+                          seq_lens=lens)
+        outs.append((o, lse, gr))
+    torch.cuda.synchronize()
+    (o1, l1, g1), (o2, l2, g2) = outs
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for key in ("dq", "dk", "dv", "dlogg", "ds"):
+        assert torch.equal(g1[key], g2[key]), key
