@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     int qgroup, const Tk* __restrict__ kbar, int kbar_ld, int d, double scale, int T, int C,
     int row_offset, int K, int nchunk, float* __restrict__ s_out, uint64_t* __restrict__ cand,
     float2* __restrict__ stats, RowLens rl) {
-  __shared__ uint64_t keys[kChunk];
+  __shared__ uint64_t srt[kChunk / 64][64];  // each wave's keys, sorted descending
   __shared__ float sval[kChunk];
   __shared__ float fscr[16];
   __shared__ double dscr[16];
@@ -393,14 +393,42 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   // Invalid entries get keys below every valid one (high word 0), still distinct.
   const uint64_t mykey = ((valid ? (uint64_t)order_key(f) : 0ull) << 32) |
                          (uint64_t)(0xFFFFFFFFu - (uint32_t)m);
-  keys[tid] = mykey;
-  const float mx = block_max(valid ? f : -INFINITY, fscr);  // barriers: keys[] complete
+  // Rank of every key in the chunk (keys are distinct): each wave sorts its 64
+  // keys descending with a bitonic network in registers; a key's rank is its
+  // position in its wave plus, for each other wave, how many of that wave's
+  // sorted keys exceed it (binary search in LDS).
+  const int lane = tid & 63, wave = tid >> 6;
+  uint64_t v = mykey;
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, j);
+      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j);
+      const uint64_t o = ((uint64_t)ohi << 32) | olo;
+      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
+      v = keep_max ? (v > o ? v : o) : (v > o ? o : v);
+    }
+  }
+  srt[wave][lane] = v;
+  const float mx = block_max(valid ? f : -INFINITY, fscr);  // barriers: srt[] complete
   const double se = block_sum_d(valid ? (double)expf(f - mx) : 0.0, dscr);
-  int rank = 0;
-#pragma unroll 8
-  for (int j = 0; j < kChunk; ++j) rank += keys[j] > mykey;
+  int rank = lane;
+#pragma unroll
+  for (int w2 = 0; w2 < kChunk / 64; ++w2) {
+    if (w2 == wave) continue;
+    int lo = 0, hi = 64;  // first position of wave w2's list not above v
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (srt[w2][mid] > v)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    rank += lo;
+  }
   const size_t cbase = (row * nchunk + chunk) * (size_t)K;
-  if (rank < K) cand[cbase + rank] = mykey;
+  if (rank < K) cand[cbase + rank] = v;
   if (tid == 0) stats[row * nchunk + chunk] = make_float2(mx, (float)se);
 }
 
