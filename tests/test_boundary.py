@@ -233,3 +233,28 @@ def test_paged_decode_checks():
     assert step(bt_ld=15) == L.SAS_ERR_INVALID_ARG
     assert step(kbar_ld=14) == L.SAS_ERR_INVALID_ARG         # C = 15 pooled rows needed
     assert step(n_=n - 1) == L.SAS_ERR_WORKSPACE
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of sas_shape and sas_kernel_time have the C header's
+    size and field offsets (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in L.sas_shape._fields_]
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "sas.h"\nint main(void) {\n'
+        '  printf("%zu %zu\\n", sizeof(sas_shape), sizeof(sas_kernel_time));\n'
+        + "".join(f'  printf("%zu\\n", offsetof(sas_shape, {f}));\n' for f in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert int(out[0]) == C.sizeof(L.sas_shape)
+    assert int(out[1]) == C.sizeof(L.sas_kernel_time)
+    for f, off in zip(fields, out[2:]):
+        assert int(off) == getattr(L.sas_shape, f).offset, f
