@@ -460,12 +460,21 @@ SideStream* side_stream() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
   SideStream& ss = per_dev[dev];
   if (!ss.s) {
-    if (hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    // published only when every part exists (else the caller runs serially)
+    SideStream n;
+    if (hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return nullptr;
-    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      hipEventDestroy(n.fork);
       return nullptr;
+    }
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) {
+      hipEventDestroy(n.fork);
+      hipEventDestroy(n.join);
+      return nullptr;
+    }
+    ss = n;
   }
   return &ss;
 }

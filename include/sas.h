@@ -161,8 +161,14 @@ sas_status sas_block_pool(const sas_shape* shape, const void* x, int heads, int 
  *   idx[r, :] = the min(K, C_t) blocks of largest s, equal scores resolved
  *               to the lower block index (-0.0 equals +0.0), ascending,
  *               -1 padded
- *   logg[r,:] = s_idx - lse_s (fp32; 0 on padded slots)
- * Uses shape->batch, hkv, head_dim, scale.  C <= 16384.
+ *   logg[r,:] = log g of those blocks under the gate activation
+ *               (shape->gate: s_idx - lse_s for softmax; fp32; 0 on padded
+ *               slots)
+ * Uses shape->batch, hkv, head_dim, scale, gate.  C <= 16384.
+ * Ragged batch (shape->seq_lens): shape->seqlen and ->block then give the
+ * tokens and block size; training rows (row_offset 0) at or past a sequence's
+ * last block have no history (C_t = 0), decode rows rank the sequence's own
+ * (seq_lens[b] - 1) / block blocks.
  *
  * Rows with more than 512 history blocks are served by two kernels (chunked
  * candidates, then a per-row merge) whose candidates live in the workspace:
