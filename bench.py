@@ -237,7 +237,47 @@ def bench_train(args):
                 ms_with_kernel_events=ms_events,
                 kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb),
                 gate_variants=None if args.no_variants else bench_gate_variants(args, w, x),
-                ragged=None if args.no_variants else bench_ragged_train(args))
+                ragged=None if args.no_variants else bench_ragged_train(args),
+                train_32k=None if args.no_variants else bench_train_32k(args))
+
+
+def bench_train_32k(args):
+    """The 32K-token training workload (32/8 heads, d 128, block 64, Top-15,
+    given scores): selection, forward and backward per step, timed like the
+    8K step."""
+    import torch
+    import synth
+    from gated_block_sparse_scores_amd import _lib as L
+    from gated_block_sparse_scores_amd import ops
+    w = synth.workload(3)
+    x = synth.train_inputs(w, device="cuda")
+    T = w.nblocks
+    sh = ops.shape_of(x["q"], x["k"], w.block)
+    ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, w.topk), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        idx, logg, lse_s, _ = ops.select_topk(w.batch, w.hkv, T, T, w.topk, s=x["s"])
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block)
+        ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, x["s"], lse_s,
+                     w.block, workspace=ws)
+        return idx
+
+    idx = step()
+    pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(5, args.steps // 2)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 12 * w.head_dim * pairs
+    return {"workload": w.name, "selected_pairs": int(pairs), "steps": steps,
+            "ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_ragged_train(args):
@@ -601,7 +641,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged ragged decode")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the gate-variant, dense-scope and ragged-batch training steps")
+                    help="skip the gate-variant, dense-scope, ragged-batch and 32K training steps")
     ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
     ap.add_argument("--decode-workloads", default="4,5")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -644,6 +684,7 @@ def main():
             "selector_bwd": res["selector_bwd"],
             "gate_variants": res["gate_variants"],
             "ragged_batch": res["ragged"],
+            "train_32k": res["train_32k"],
         })
     if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")
