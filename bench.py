@@ -94,7 +94,10 @@ def bench_gate_variants(args, w, x):
         idx, _, _, _ = step()
         torch.cuda.synchronize()
         pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
-        steps = 3
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        steps = 5
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
@@ -187,11 +190,17 @@ def bench_train(args):
     sh = ops.shape_of(x["q"], x["k"], w.block)
     ws = torch.empty(L.sas_attn_bwd_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
     step = train_step_fn(w, x, ws)
-    for _ in range(args.warmup):
-        idx, gr, qb, kb = step()
-    torch.cuda.synchronize()
+    # The outputs kept for counting and for the selector backward come from a
+    # step before the warm-up, so the warm-up steps leave the allocator's cache
+    # holding one step's buffers and the timed steps allocate nothing new.
+    idx, gr, qb, kb = step()
+    # counted before the warm-up: the first steps after a host-side reduction
+    # like this one run measurably slower
     pairs = selected_pairs_device(idx, w.seqlen, w.block, w.group)
     flops = 12 * w.head_dim * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
 
     # Step time with nothing but the step on the stream.
     torch.cuda.synchronize()
