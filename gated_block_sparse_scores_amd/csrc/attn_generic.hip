@@ -481,7 +481,7 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
   const float ls = lse_s ? lse_s[row] : 0.0f;
-  if (threadIdx.x < K) {
+  if ((int)threadIdx.x < K) {
     float a = 0.0f;
     for (int c = 0; c < nchunk; ++c) a += dlogg_part[(row * nchunk + c) * K + threadIdx.x];
     const int m = idx[row * K + threadIdx.x];

@@ -466,12 +466,12 @@ SideStream* side_stream() {
       return nullptr;
     if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
-      hipEventDestroy(n.fork);
+      (void)hipEventDestroy(n.fork);  // clean-up on the failure path; its own status is moot
       return nullptr;
     }
     if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) {
-      hipEventDestroy(n.fork);
-      hipEventDestroy(n.join);
+      (void)hipEventDestroy(n.fork);
+      (void)hipEventDestroy(n.join);
       return nullptr;
     }
     ss = n;

@@ -5,7 +5,6 @@ device and calls the matching libsas entry point; nothing is computed here.
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import torch

@@ -59,7 +59,7 @@ precision the scores are stored in, exactly as the device library takes it.
 from __future__ import annotations
 
 import math
-from typing import Iterable, Optional
+from typing import Optional
 
 import numpy as np
 import torch

@@ -5,7 +5,7 @@ import torch
 
 import synth
 from oracle import sas_oracle as O
-from tests._gpu_helpers import max_abs, np64, say, tols
+from tests._gpu_helpers import max_abs, say, tols
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"

@@ -7,7 +7,7 @@ import torch
 
 import synth
 from oracle import sas_oracle as O
-from tests._gpu_helpers import GATE_ATOL, gpu_select_given, max_abs, np64, say
+from tests._gpu_helpers import GATE_ATOL, gpu_select_given, max_abs, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"

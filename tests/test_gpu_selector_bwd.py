@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import sas_oracle as O
-from tests._gpu_helpers import max_abs, rel_l2, say
+from tests._gpu_helpers import rel_l2, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
