@@ -477,6 +477,7 @@ def bench_decode(wl, steps, layers=12):
         "wall_us_per_call": round(step_wall_us, 2),
         "kernels": {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)}
                     for k, v in kt2.items()},
+        "graph": graph_replays(one_step, qs[calls:], layers, calls),
     }
     del caches
     torch.cuda.empty_cache()
@@ -499,6 +500,38 @@ def bench_decode(wl, steps, layers=12):
                      "avg_launch_us": round(split_us, 2)},
         "kernels": kernels,
     }
+
+
+def graph_replays(one_step, qs, layers, calls):
+    """The fused step of each layer captured once in a HIP graph (its query in a
+    static buffer), then the graphs replayed round-robin over the layers, as a
+    serving loop that launches one graph per layer would: wall time per replay.
+    The layers' caches rotate, so the selected blocks still come from HBM."""
+    import torch
+    qstat = [q.clone() for q in qs[:layers]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):              # warm-up outside the captures
+        for layer in range(layers):
+            one_step(qstat[layer], layer)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for layer in range(layers):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_step(qstat[layer], layer)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in range(calls):
+        graphs[c % layers].replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / calls
+    del graphs
+    return {"wall_us_per_call": round(us, 2), "replays": calls}
 
 
 def bench_decode_paged(steps=10, layers=12):
