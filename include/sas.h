@@ -50,6 +50,10 @@
  *     fork part of its work onto a second stream of the library's own (one per
  *     host thread and device, default priority, created on first use) and
  *     joins it back to the caller's stream with events before returning.
+ *   - No call allocates device memory, records a memset or synchronises, so
+ *     every call can be captured in a HIP graph on a capturing stream (make
+ *     one eager sas_attn_bwd call first, so that its second stream exists
+ *     before the capture begins).
  */
 #ifndef SAS_H
 #define SAS_H
