@@ -49,6 +49,36 @@ constexpr int HPW = 2;   // heads per workgroup
 constexpr int NW = 4;    // waves per workgroup (two 32-row halves per head)
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
+// oacc[dt] += V^T(rows 16 ch .. +16, dims 32 dt .. +32) P^T[ch] over the four
+// 16-key chunks ch of a gathered V tile (V^T read with ds_read_b64_tr_b16).
+// The fragments of chunk ch + 1 are read while chunk ch's four MFMAs run: the
+// issue order is pinned (one MFMA, then two of the next chunk's reads), so a
+// chunk waits once for its reads instead of once per MFMA.
+__device__ __forceinline__ void pv_chunks(const bf16_t* Vc, const bf16x8 (&pf)[4],
+                                          f32x16 (&oacc)[4]) {
+  bf16x8 fr[2][4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) fr[0][dt] = tr_frag(Vc, 0, dt * 32);
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    if (ch < 3) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) fr[(ch + 1) & 1][dt] = tr_frag(Vc, (ch + 1) * 16, dt * 32);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma32(fr[ch & 1][dt], pf[ch], oacc[dt]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // chunk 0's reads
+#pragma unroll
+  for (int ch = 0; ch < 3; ++ch)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of chunk ch
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two reads of chunk ch + 1
+    }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
 template <bool OUTER>
 __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -193,12 +223,11 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
       }
 
     // O^T += V^T P^T over four 16-key chunks.
+    {
+      bf16x8 pf[4];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const bf16x8 pf = pack8(sacc[ch >> 1], (ch & 1) * 8);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = mfma32(tr_frag(Vc, ch * 16, dt * 32), pf, oacc[dt]);
+      for (int ch = 0; ch < 4; ++ch) pf[ch] = pack8(sacc[ch >> 1], (ch & 1) * 8);
+      pv_chunks(Vc, pf, oacc);
     }
     wait_all_loads();   // this wave's copies of the next block
     __syncthreads();    // everyone's copies landed; everyone is done with (Kc, Vc)
