@@ -65,8 +65,11 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dv,
     const float* __restrict__ logg, const uint8_t* __restrict__ slotmap,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg) {
-  __shared__ __align__(16) bf16_t Qs[BS * TILE_LD];
-  __shared__ __align__(16) bf16_t Os[BS * TILE_LD];
+  // q and dout tiles in one array: they are only read after every copy into
+  // them has landed, and one base register with constant offsets addresses both
+  __shared__ __align__(16) bf16_t QO[2 * BS * TILE_LD];
+  bf16_t* const Qs = QO;
+  bf16_t* const Os = QO + BS * TILE_LD;
   __shared__ __align__(16) bf16x8 xch[4][4][64];  // [wave][P0, P1, dS0, dS1][lane]
   __shared__ float Ls[BS], Dl[BS];
   __shared__ float cur_bias;
