@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
       __syncthreads();
       float sc[KC];
       float cmax = -INFINITY;
-#pragma unroll
+#pragma unroll 2
       for (int j = 0; j < KC; ++j) {
         const float z = reduce_p<D>(dot_slice<D>(qv, Ks[j], p)) * dm.scale + bias;
         const bool valid = j < nk && (m != t || lo + j <= i);
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(512) fwd_generic_kernel(
       lrun *= alpha;
 #pragma unroll
       for (int e = 0; e < 32; ++e) acc[e] *= alpha;
-#pragma unroll
+#pragma unroll 2
       for (int j = 0; j < KC; ++j) {
         const float pj = sc[j] == -INFINITY ? 0.0f : expf(sc[j] - mnew);
         lrun += pj;
@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(512) bwd_dq_generic_kernel(
       stage_rows<T, D, KC>(Ks, kbase + (size_t)lo * D, nk);
       stage_rows<T, D, KC>(Vs, vbase + (size_t)lo * D, nk);
       __syncthreads();
-#pragma unroll
+#pragma unroll 2
       for (int j = 0; j < KC; ++j) {
         const float z = reduce_p<D>(dot_slice<D>(qv, Ks[j], p)) * dm.scale + bias;
         const float dp = reduce_p<D>(dot_slice<D>(dov, Vs[j], p)) * gain;
