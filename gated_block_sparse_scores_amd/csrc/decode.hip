@@ -399,7 +399,7 @@ struct SelectChunks {
   float* lse_out;    // optional [b*hkv]
 };
 
-template <int G, int kDecWaves, bool SEL>
+template <int G, int kDecWaves, bool SEL, int kBpw>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     Dims dm, int Lmax, KvView kvv, int nsplit, const bf16_t* __restrict__ q,
     const int32_t* __restrict__ idx, const float* __restrict__ logg,
@@ -407,8 +407,10 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
   __shared__ __align__(16) uint32_t Pb[kDecWaves][BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
-  __shared__ __align__(16) float wacc[kDecWaves][G][D];
-  __shared__ float wml[kDecWaves][G][2];
+  __shared__ __align__(16) float wacc[kDecWaves * kBpw][G][D];  // one partial per block
+  __shared__ float wml[kDecWaves * kBpw][G][2];
+  __shared__ int sidx[64];
+  __shared__ float slg[64];
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int kv = bk % dm.hkv, b = bk / dm.hkv;
@@ -418,16 +420,16 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   const size_t prow = (size_t)b * dm.hq + (size_t)kv * G;
   const int hbase = (lane >> 4) * 4;
 
-  // This wave's block: entry j of [valid selected blocks (slot order)..., current block].
-  const int j = split * kDecWaves + wave;
-  int m = -1;
-  float bias = 0.0f;
+  // Entries: [valid selected blocks (slot order)..., current block].  The
+  // workgroup takes kDecWaves * kBpw consecutive entries, wave w the kBpw
+  // entries from (split * kDecWaves + w) * kBpw, one after the other.
+  int nvalid = 0;  // valid selected blocks of the row (the current block follows)
+  int mm = -1;     // given idx: the row's entry `lane`
+  unsigned long long bal = 0;
   if constexpr (SEL) {
     extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
     __shared__ int widx[64];
     __shared__ float wval[64];
-    __shared__ int sidx[64];
-    __shared__ float slg[64];
     __shared__ float fscr[16];
     __shared__ double dscr[16];
     const int K = dm.K, nc = sel.nchunk * K;
@@ -489,26 +491,31 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       if (tid == 0) sel.lse_out[bk] = lse_s;
     }
     __syncthreads();
-    if (j < kk) {
+    nvalid = kk;
+  } else {
+    mm = lane < dm.K ? idx[(size_t)bk * dm.K + lane] : -1;
+    bal = __ballot(mm >= 0 && mm < c);
+    nvalid = __popcll(bal);
+  }
+#pragma unroll 1
+  for (int e = 0; e < kBpw; ++e) {
+  const int j = (split * kDecWaves + wave) * kBpw + e;
+  int m = -1;
+  float bias = 0.0f;
+  if (j < nvalid) {
+    if constexpr (SEL) {
       m = sidx[j];
       bias = sel.gated ? slg[j] : 0.0f;
-    } else if (j == kk) {
-      m = c;
-    }
-  } else {
-    const int mm = lane < dm.K ? idx[(size_t)bk * dm.K + lane] : -1;
-    const bool ok = mm >= 0 && mm < c;
-    const unsigned long long bal = __ballot(ok);
-    const int nvalid = __popcll(bal);
-    if (j < nvalid) {
+    } else {
+      const bool ok = mm >= 0 && mm < c;
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
       const unsigned long long hit = __ballot(ok && before == j);
       const int src = __ffsll((long long)hit) - 1;
       m = __shfl(mm, src);
       bias = logg ? logg[(size_t)bk * dm.K + src] : 0.0f;
-    } else if (j == nvalid) {
-      m = c;
     }
+  } else if (j == nvalid) {
+    m = c;
   }
   // The block's rows (a block on an out-of-range page is skipped).
   const bf16_t* kblk = nullptr;
@@ -633,32 +640,35 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       }
     }
   }
-  // The wave's partial into LDS (an empty wave contributes max -inf, sum 0).
+  // The block's partial into LDS (an empty entry contributes max -inf, sum 0).
+  const int slot = wave * kBpw + e;
 #pragma unroll
   for (int h = 0; h < G; ++h)
-    *reinterpret_cast<float2*>(&wacc[wave][h][2 * lane]) =
+    *reinterpret_cast<float2*>(&wacc[slot][h][2 * lane]) =
         make_float2(acc[h][0] * gain, acc[h][1] * gain);
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = hbase + r;
       if (h < G) {
-        wml[wave][h][0] = mh[r];
-        wml[wave][h][1] = lh[r];
+        wml[slot][h][0] = mh[r];
+        wml[slot][h][1] = lh[r];
       }
     }
   }
+  }  // entries of this wave
   __syncthreads();
+  constexpr int nslot = kDecWaves * kBpw;
 
-  // Fold the four blocks: wave w takes heads w, w + 4, ...; weights e^{m - M},
-  // 0 for empty blocks.
+  // Fold the workgroup's blocks: wave w takes heads w, w + kDecWaves, ...;
+  // weights e^{m - M}, 0 for empty blocks.
   for (int h = wave; h < G; h += kDecWaves) {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wml[w][h][0]);
+    for (int w = 0; w < nslot; ++w) M = fmaxf(M, wml[w][h][0]);
     float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < nslot; ++w) {
       const float l = wml[w][h][1];
       const float wt = l > 0.0f ? expf(wml[w][h][0] - M) : 0.0f;
       Ls += wt * l;
@@ -672,18 +682,26 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 }
 
+// bps entries per workgroup: 8 (four waves of two blocks), 4 (four waves of
+// one) or 1 (one wave).
 template <int G, bool SEL>
-void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, int waves,
+void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, int bps,
                           const void* q, const int32_t* idx, const float* logg, float* part_ml,
                           float* part_acc, const SelectChunks& sel, hipStream_t st) {
   const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
   const size_t lds = SEL ? (size_t)2 * sel.nchunk * dm.K * sizeof(uint64_t) : 0;
-  if (waves == 4)
-    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL>), dim3((unsigned)wgs), dim3(256), lds, st,
-                       dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc, sel);
+  if (bps == 8)
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 2>), dim3((unsigned)wgs), dim3(256), lds,
+                       st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
+                       sel);
+  else if (bps == 4)
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 1>), dim3((unsigned)wgs), dim3(256), lds,
+                       st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
+                       sel);
   else
-    hipLaunchKernelGGL((decode_block4_kernel<G, 1, SEL>), dim3((unsigned)wgs), dim3(64), lds, st,
-                       dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc, sel);
+    hipLaunchKernelGGL((decode_block4_kernel<G, 1, SEL, 1>), dim3((unsigned)wgs), dim3(64), lds,
+                       st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
+                       sel);
 }
 
 // Workspace: [partials (max, sum) per (b, h, split)][partial outputs per
@@ -692,7 +710,7 @@ template <typename T, int D, int BS>
 hipError_t decode_typed(const Dims& dm, int L, const KvView& kvv, const void* q,
                         const int32_t* idx, const float* logg, void* o, float* lse, void* ws,
                         hipStream_t st) {
-  const int bps = decode_blocks_per_split(dm);
+  const int bps = kvv.table && decode_two_per_wave(dm) ? 8 : decode_blocks_per_split(dm);
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
@@ -728,9 +746,20 @@ hipError_t decode_typed(const Dims& dm, int L, const KvView& kvv, const void* q,
 
 bool decode_mfma_path(const Dims& dm) { return dm.bf16 && dm.d == 128 && dm.bs == 64; }
 
+// Four waves of two blocks each per workgroup (MFMA path): when that still
+// fills every CU with two workgroups, the grid runs in one round, each wave's
+// second block loading after its first is folded.  Measured faster for the
+// paged decode and the fused steps (half as many workgroups merge the chunk
+// candidates), slower for the dense separate decode, which keeps one block
+// per wave.
+bool decode_two_per_wave(const Dims& dm) {
+  return decode_mfma_path(dm) && (long)dm.b * dm.hkv * ((dm.K + 8) / 8) >= 512;
+}
+
 int decode_blocks_per_split(const Dims& dm) {
   // MFMA path: four blocks (waves) per workgroup when that still leaves at
-  // least two workgroups per CU, else one.
+  // least two workgroups per CU, else one.  The workspace is sized for this
+  // split count, which is at least that of two blocks per wave.
   if (decode_mfma_path(dm))
     return (long)dm.b * dm.hkv * ((dm.K + 4) / 4) >= 512 ? 4 : 1;
   const long total = (long)dm.b * dm.hkv * (dm.K + 1);
@@ -766,8 +795,9 @@ hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, i
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
   // Four waves per workgroup whatever the grid: every workgroup merges the
   // row's chunk candidates first, which 256 threads do four times faster than
-  // 64 (the partial buffer of decode_workspace_bytes covers this split count).
-  const int bps = 4;
+  // 64; two blocks per wave when the separate decode takes them too (the
+  // partial buffer of decode_workspace_bytes covers this split count).
+  const int bps = decode_two_per_wave(dm) ? 8 : 4;
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;

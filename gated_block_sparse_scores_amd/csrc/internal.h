@@ -99,6 +99,7 @@ int bwd_dlogg_chunks(const Dims& dm);
 
 // ---- decode (decode.hip)
 int decode_blocks_per_split(const Dims& dm);
+bool decode_two_per_wave(const Dims& dm);
 size_t decode_workspace_bytes(const Dims& dm);
 // Fused decode step (bf16, d 128, block 64): chunk selection over the pooled-key
 // cache with the query pooled in-kernel, then the decode kernel merging the

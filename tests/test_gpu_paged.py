@@ -65,6 +65,8 @@ PAGED = [
     ([1000, 64, 3000, 4097], 8, 2, 128, 64, 8, torch.bfloat16),
     ([300, 17, 129], 4, 4, 64, 16, 4, torch.float32),
     ([4096 * 4 + 7, 130, 65], 40, 8, 128, 64, 31, torch.bfloat16),
+    # batch 8 x 8 KV heads, K 63: the grid that takes four waves of two blocks
+    ([4500, 8000, 6100, 4200, 5000, 7777, 4160, 4500], 32, 8, 128, 64, 63, torch.bfloat16),
 ]
 
 
@@ -128,6 +130,8 @@ STEP = [
     # lens,                                  hq, hkv, K
     ([1000, 64, 3000, 4097], 8, 2, 8),
     ([64 * 700 + 5, 64 * 40 + 1, 65, 64 * 1023 + 1], 32, 8, 63),
+    # batch 8 x 8 KV heads, K 63: four waves of two blocks per workgroup
+    ([4500, 8000, 6100, 4200, 5000, 7777, 4160, 64 * 63 + 1], 32, 8, 63),
 ]
 
 
