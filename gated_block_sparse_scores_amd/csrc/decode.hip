@@ -541,31 +541,68 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
 
     // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
+    // The separate decode with four waves of one block issues its V loads
+    // after the score products instead, into the registers K held: 30 fewer
+    // registers, and V's latency overlaps the softmax (measured 6% faster;
+    // the other shapes are slower that way).
+    constexpr bool kLateV = kDecWaves == 4 && kBpw == 1 && !SEL;
     bf16x8_t kf[4][4];
     uint32_t vr[BS];
-    if (pos0 + BS <= L) {  // full block (every history block): plain offsets
-      const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
-      const bf16_t* vrow = vblk + 2 * lane;
+    auto load_v = [&]() {
+      if (pos0 + BS <= L) {
+        const bf16_t* vrow = vblk + 2 * lane;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+      } else {  // rows past L - 1 are read clamped, then masked
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
-#pragma unroll
-      for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
-    } else {  // the current block: rows past L - 1 are read clamped, then masked
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int rr = min(kt * 16 + (lane & 15), last - pos0);
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-          kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kblk + (size_t)rr * D + ch * 32 +
-                                                          (lane >> 4) * 8);
+        for (int r = 0; r < BS; ++r)
+          vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
+                                                     2 * lane);
       }
+    };
+    if constexpr (kLateV) {
+      if (pos0 + BS <= L) {
+        const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
 #pragma unroll
-      for (int r = 0; r < BS; ++r)
-        vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
-                                                   2 * lane);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int rr = min(kt * 16 + (lane & 15), last - pos0);
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kblk + (size_t)rr * D + ch * 32 +
+                                                            (lane >> 4) * 8);
+        }
+      }
+    } else {
+      if (pos0 + BS <= L) {  // full block (every history block): plain offsets
+        const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
+        const bf16_t* vrow = vblk + 2 * lane;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
+#pragma unroll
+        for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+      } else {  // the current block: rows past L - 1 are read clamped, then masked
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int rr = min(kt * 16 + (lane & 15), last - pos0);
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(kblk + (size_t)rr * D + ch * 32 +
+                                                            (lane >> 4) * 8);
+        }
+#pragma unroll
+        for (int r = 0; r < BS; ++r)
+          vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
+                                                     2 * lane);
+      }
     }
     bf16x8_t qf[4];
     {
@@ -585,6 +622,10 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ch], kf[kt][ch], sacc[kt], 0, 0, 0);
+    }
+    if constexpr (kLateV) {
+      __builtin_amdgcn_sched_barrier(0);  // the V loads stay after the score products
+      load_v();
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
