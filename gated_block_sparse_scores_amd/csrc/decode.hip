@@ -11,8 +11,8 @@
 // (max, sum, unnormalised output) of every split goes to the workspace and the
 // splits of each (b, h) are merged with log-sum-exp weights.
 //  * bf16, head_dim 128, block 64 (decode_block4_kernel): four waves per
-//    workgroup, one selected block per wave, MFMA scores; the workgroup folds
-//    its four blocks in LDS into one partial.
+//    workgroup (one on small grids), one or two selected blocks per wave,
+//    MFMA scores; the workgroup folds its blocks in LDS into one partial.
 //  * every other shape (decode_split_kernel): each key row is read by 16 lanes
 //    with one vector load per lane, dot products reduced with DPP row
 //    operations.
@@ -378,9 +378,11 @@ __device__ __forceinline__ float row16_max(float x) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // kDecWaves waves per workgroup (4 when there are enough workgroups to fill
-// the chip, else 1), one selected block per wave; the workgroup folds its
-// blocks into one partial in LDS, so the merge kernel reads a quarter of the
-// partials it would read at one block per workgroup.  (Merging in the last
+// the chip, else 1), kBpw selected blocks per wave taken one after the other
+// (2 for the paged decode and the fused steps on grids that then still fill
+// every CU twice); the workgroup folds its blocks into one partial in LDS, so
+// the merge kernel reads a fraction of the partials it would read at one block
+// per workgroup.  (Merging in the last
 // workgroup to finish would need a device-scope fence per workgroup, which on
 // this multi-die part writes back the L2 and costs far more than the second
 // launch.)
