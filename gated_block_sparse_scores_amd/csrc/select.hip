@@ -345,21 +345,39 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     // 16 groups of 16 lanes; group grp scores blocks m0 + grp + 16 i.
     const int sub = tid & 15, grp = tid >> 4;
     const int nsl = d / 8;  // lanes carrying 8 dims each (16 for d = 128, 8 for d = 64)
+    // The summary rows' loads go out first: nothing in their addresses waits on
+    // the query, so their latency overlaps the query's.
+    Slice8<Tk> sl[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mm = m0 + grp + 16 * i;
+      if (sub < nsl && mm < ct) sl[i].load(kbar + (bk * kbar_ld + mm) * (size_t)d + sub * 8);
+    }
     double qd[8];
     if (qraw) {
       // decode (T = 1): the pooled query is the mean of the qgroup heads of this
       // KV head, formed here exactly as the pooling kernel forms it (the sum of
-      // bf16 values in fp64 is exact), rounded once to fp32
+      // bf16 values in fp64 is exact), rounded once to fp32.  Heads are read
+      // eight at a time, every load of a batch issued before the first add (a
+      // head index past the group re-reads the last head).
       const bf16_t* qh = qraw + row * (size_t)qgroup * d + (sub < nsl ? sub * 8 : 0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qd[e] = 0.0;
-      for (int h = 0; h < qgroup; ++h) {
-        const uint4 u = *reinterpret_cast<const uint4*>(qh + (size_t)h * d);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      for (int h0 = 0; h0 < qgroup; h0 += 8) {
+        uint4 u[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          qd[2 * k] += (double)__uint_as_float(w[k] << 16);
-          qd[2 * k + 1] += (double)__uint_as_float(w[k] & 0xFFFF0000u);
+        for (int h = 0; h < 8; ++h)
+          u[h] = *reinterpret_cast<const uint4*>(qh + (size_t)min(h0 + h, qgroup - 1) * d);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          // a head past the group adds +0.0, which leaves every sum unchanged
+          const bool in = h0 + h < qgroup;
+          const uint32_t w[4] = {u[h].x, u[h].y, u[h].z, u[h].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            qd[2 * k] += in ? (double)__uint_as_float(w[k] << 16) : 0.0;
+            qd[2 * k + 1] += in ? (double)__uint_as_float(w[k] & 0xFFFF0000u) : 0.0;
+          }
         }
       }
 #pragma unroll
@@ -368,12 +386,6 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
       const float* qr = qbar + row * (size_t)d;
 #pragma unroll
       for (int e = 0; e < 8; ++e) qd[e] = sub < nsl ? (double)qr[sub * 8 + e] : 0.0;
-    }
-    Slice8<Tk> sl[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mm = m0 + grp + 16 * i;
-      if (sub < nsl && mm < ct) sl[i].load(kbar + (bk * kbar_ld + mm) * (size_t)d + sub * 8);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -413,20 +425,27 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   srt[wave][lane] = v;
   const float mx = block_max(valid ? f : -INFINITY, fscr);  // barriers: srt[] complete
   const double se = block_sum_d(valid ? (double)expf(f - mx) : 0.0, dscr);
-  int rank = lane;
+  // The count of keys above v in a descending list of 64 is found in six fixed
+  // halving steps (exact for counts up to 63), with the last entry checked
+  // apart for a count of 64.  The waves' searches are independent, so their LDS
+  // reads interleave.  A wave's own list counts its lane index instead.
+  int cnt[kChunk / 64];
+  bool all_above[kChunk / 64];
 #pragma unroll
   for (int w2 = 0; w2 < kChunk / 64; ++w2) {
-    if (w2 == wave) continue;
-    int lo = 0, hi = 64;  // first position of wave w2's list not above v
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (srt[w2][mid] > v)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    rank += lo;
+    cnt[w2] = 0;
+    all_above[w2] = srt[w2][63] > v;
   }
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+    for (int w2 = 0; w2 < kChunk / 64; ++w2)
+      if (srt[w2][cnt[w2] + step - 1] > v) cnt[w2] += step;
+  }
+  int rank = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kChunk / 64; ++w2)
+    rank += w2 == wave ? lane : all_above[w2] ? 64 : cnt[w2];
   const size_t cbase = (row * nchunk + chunk) * (size_t)K;
   if (rank < K) cand[cbase + rank] = v;
   if (tid == 0) stats[row * nchunk + chunk] = make_float2(mx, (float)se);
