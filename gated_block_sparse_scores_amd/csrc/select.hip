@@ -423,8 +423,21 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     }
   }
   srt[wave][lane] = v;
-  const float mx = block_max(valid ? f : -INFINITY, fscr);  // barriers: srt[] complete
-  const double se = block_sum_d(valid ? (double)expf(f - mx) : 0.0, dscr);
+  // Chunk statistics: one barrier publishes the sorted lists and the wave
+  // maxima together; the waves' fp64 sums of exp are combined, in wave order,
+  // after the last barrier below.
+  {
+    const float wmx = wave_max(valid ? f : -INFINITY);
+    if (lane == 0) fscr[wave] = wmx;
+  }
+  __syncthreads();
+  float mx = fscr[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kChunk / 64; ++w2) mx = fmaxf(mx, fscr[w2]);
+  {
+    const double wse = wave_sum_d(valid ? (double)expf(f - mx) : 0.0);
+    if (lane == 0) dscr[wave] = wse;
+  }
   // The count of keys above v in a descending list of 64 is found in six fixed
   // halving steps (exact for counts up to 63), with the last entry checked
   // apart for a count of 64.  The waves' searches are independent, so their LDS
@@ -448,7 +461,13 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     rank += w2 == wave ? lane : all_above[w2] ? 64 : cnt[w2];
   const size_t cbase = (row * nchunk + chunk) * (size_t)K;
   if (rank < K) cand[cbase + rank] = v;
-  if (tid == 0) stats[row * nchunk + chunk] = make_float2(mx, (float)se);
+  __syncthreads();
+  if (tid == 0) {
+    double se = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kChunk / 64; ++w2) se += dscr[w2];
+    stats[row * nchunk + chunk] = make_float2(mx, (float)se);
+  }
 }
 
 __global__ void __launch_bounds__(256) select_merge_kernel(
