@@ -76,6 +76,80 @@ __device__ __forceinline__ float from_order_key(uint32_t k) {
   return __uint_as_float(b);
 }
 
+// Lane exchange x <- x of lane (lane ^ J) within a wave of 64, on cross-lane
+// paths that bypass the LDS unit: DPP quad permutes for J = 1, 2; a half-row
+// mirror followed by a quad reversal for J = 4 (7 - (i ^ 3) = i ^ 4 within
+// eight lanes); a row rotation by 8 for J = 8; gfx950's row-pair swaps for
+// J = 16 and 32, whose first result holds the lower row (half) of each pair in
+// both, the second the upper, so a lane takes the other side's.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (J == 4) {
+    const int m = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    return __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);               // quad_perm 3,2,1,0
+  } else if constexpr (J == 8) {
+    return __builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
+// Sorts a bitonic sequence of 64 keys, one per lane, into descending lane
+// order: half-cleaners at distances 32, 16, ..., 1, the larger key kept by the
+// lower lane of each pair.
+template <int J = 32>
+__device__ __forceinline__ uint64_t bitonic_desc64(uint64_t v, int lane) {
+  const uint64_t o = ((uint64_t)xor_lane<J>((uint32_t)(v >> 32)) << 32) |
+                     xor_lane<J>((uint32_t)v);
+  v = ((lane & J) == 0) == (v > o) ? v : o;
+  if constexpr (J > 1) return bitonic_desc64<J / 2>(v, lane);
+  else return v;
+}
+
+// Top K (K <= 64) of nl descending lists of K distinct nonzero keys held in
+// LDS, descending.  Two descending lists of 64 (zero-padded) meet by taking
+// the larger of a[i] and b[63 - i] lane by lane, which keeps the top 64 of the
+// pair as a bitonic sequence, sorted again by bitonic_desc64.  Wave w folds
+// lists w, w + NW, ... into its running top list (the next list's LDS read in
+// flight during the current fold); wave 0 then folds the other waves' lists
+// from `wl` (NW * 64 keys of LDS; one barrier when NW > 1, which every thread
+// of the workgroup reaches).  Lane i of wave 0 returns the key of rank i (0
+// past the end).
+template <int NW>
+__device__ __forceinline__ uint64_t merge_top64(const uint64_t* lists, int nl, int K,
+                                                uint64_t* wl) {
+  const int lane = threadIdx.x & 63, wave = (int)(threadIdx.x >> 6);
+  const int rev = 63 - lane;
+  uint64_t acc = 0;
+  uint64_t nb = wave < nl && rev < K ? lists[wave * K + rev] : 0ull;
+  for (int l = wave; l < nl; l += NW) {
+    const uint64_t b = nb;
+    nb = l + NW < nl && rev < K ? lists[(l + NW) * K + rev] : 0ull;
+    acc = bitonic_desc64(acc > b ? acc : b, lane);
+  }
+  if constexpr (NW > 1) {
+    wl[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const uint64_t b = wl[w * 64 + rev];
+        acc = bitonic_desc64(acc > b ? acc : b, lane);
+      }
+    }
+  }
+  return acc;
+}
+
 // Top K of two descending lists of exactly K distinct keys, by merge path:
 // output j is found by binary search for how many of the first j + 1 come from A.
 __device__ __forceinline__ uint64_t merge_path_kth(const uint64_t* A, const uint64_t* B, int K,

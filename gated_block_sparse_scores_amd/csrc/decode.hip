@@ -449,9 +449,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     S = block_sum_d(S, dscr);
     const int Crow = kvv.seq_lens ? min(sel.C, c) : sel.C;  // this sequence's history
     const float lse_s = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
+    // K <= 64: wave-level folds in registers; larger K: pairwise merge-path rounds
+    __shared__ uint64_t wl[kDecWaves * 64];
+    const uint64_t top = K <= 64 ? merge_top64<kDecWaves>(lists, sel.nchunk, K, wl) : 0ull;
     uint64_t* src = lists;
     uint64_t* dst = lists + nc;
-    int nl = sel.nchunk;
+    int nl = K <= 64 ? 1 : sel.nchunk;
     while (nl > 1) {
       const int np = nl >> 1;
       for (int job = tid; job < np * K; job += nth) {
@@ -468,7 +471,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     }
     const int kk = min(K, Crow);
     if (tid < kk) {
-      const uint64_t key = src[tid];
+      const uint64_t key = K <= 64 ? top : src[tid];
       widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
       wval[tid] = from_order_key((uint32_t)(key >> 32));
     }

@@ -495,10 +495,14 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
                                  dscr);
     if (threadIdx.x == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
   }
-  // Pairwise merges, keeping the top K of each pair, until one list remains.
+  // K <= 64: each wave folds a share of the lists into its top list in
+  // registers, then wave 0 folds the waves' lists.  Larger K: pairwise merges,
+  // keeping the top K of each pair, until one list remains.
+  __shared__ uint64_t wl[4 * 64];
+  const uint64_t top = K <= 64 ? merge_top64<4>(lists, nchunk, K, wl) : 0ull;
   uint64_t* src = lists;
   uint64_t* dst = lists + nc;
-  int nl = nchunk;
+  int nl = K <= 64 ? 1 : nchunk;
   while (nl > 1) {
     const int np = nl >> 1;
     for (int job = threadIdx.x; job < np * K; job += blockDim.x) {
@@ -515,7 +519,7 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
   }
   const int kk = min(K, ct);
   if ((int)threadIdx.x < kk) {
-    const uint64_t key = src[threadIdx.x];
+    const uint64_t key = K <= 64 ? top : src[threadIdx.x];
     widx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
     wval[threadIdx.x] = from_order_key((uint32_t)(key >> 32));
   }
