@@ -150,28 +150,6 @@ __device__ __forceinline__ uint64_t merge_top64(const uint64_t* lists, int nl, i
   return acc;
 }
 
-// Top K of two descending lists of exactly K distinct keys, by merge path:
-// output j is found by binary search for how many of the first j + 1 come from A.
-__device__ __forceinline__ uint64_t merge_path_kth(const uint64_t* A, const uint64_t* B, int K,
-                                                  int j) {
-  const int d = j + 1;
-  int lo = d > K ? d - K : 0, hi = d < K ? d : K;
-  // smallest a in [lo, hi] such that taking a from A is not too few:
-  // too few <=> a < K and d - a > 0 and A[a] > B[d - a - 1]
-  while (lo < hi) {
-    const int a = (lo + hi) >> 1;
-    if (A[a] > B[d - a - 1])
-      lo = a + 1;
-    else
-      hi = a;
-  }
-  const int a = lo, b = d - lo;
-  if (a == 0) return B[b - 1];
-  if (b == 0) return A[a - 1];
-  const uint64_t x = A[a - 1], y = B[b - 1];
-  return x < y ? x : y;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -388,8 +388,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // launch.)
 // With SEL the block list is not read from idx / logg but formed here from the
 // long-history selection's chunk candidates (SelectChunks): every workgroup of
-// a (b, kv) merges the sorted candidate lists of its row pairwise by merge path
-// (the rule the selection merge kernel uses), orders the K winners by block
+// a (b, kv) folds the sorted candidate lists of its row into the top K (the
+// wave-level merges the selection merge kernel uses), orders the winners by block
 // index and takes the entries it serves; workgroup 0 of each (b, kv) also
 // stores idx, logg and lse_s for the caller.
 struct SelectChunks {
@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   int mm = -1;     // given idx: the row's entry `lane`
   unsigned long long bal = 0;
   if constexpr (SEL) {
-    extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
+    extern __shared__ uint64_t lists[];  // nchunk * K keys
     __shared__ int widx[64];
     __shared__ float wval[64];
     __shared__ float fscr[16];
@@ -449,29 +449,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     S = block_sum_d(S, dscr);
     const int Crow = kvv.seq_lens ? min(sel.C, c) : sel.C;  // this sequence's history
     const float lse_s = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
-    // K <= 64: wave-level folds in registers; larger K: pairwise merge-path rounds
+    // wave-level folds of the chunk lists in registers (K <= 64)
     __shared__ uint64_t wl[kDecWaves * 64];
-    const uint64_t top = K <= 64 ? merge_top64<kDecWaves>(lists, sel.nchunk, K, wl) : 0ull;
-    uint64_t* src = lists;
-    uint64_t* dst = lists + nc;
-    int nl = K <= 64 ? 1 : sel.nchunk;
-    while (nl > 1) {
-      const int np = nl >> 1;
-      for (int job = tid; job < np * K; job += nth) {
-        const int pr = job / K, jj = job % K;
-        dst[pr * K + jj] = merge_path_kth(src + (2 * pr) * K, src + (2 * pr + 1) * K, K, jj);
-      }
-      if (nl & 1)
-        for (int jj = tid; jj < K; jj += nth) dst[np * K + jj] = src[(nl - 1) * K + jj];
-      __syncthreads();
-      uint64_t* tmp = src;
-      src = dst;
-      dst = tmp;
-      nl = np + (nl & 1);
-    }
+    const uint64_t top = merge_top64<kDecWaves>(lists, sel.nchunk, K, wl);
     const int kk = min(K, Crow);
     if (tid < kk) {
-      const uint64_t key = K <= 64 ? top : src[tid];
+      const uint64_t key = top;
       widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
       wval[tid] = from_order_key((uint32_t)(key >> 32));
     }
@@ -735,7 +718,7 @@ void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, 
                           const void* q, const int32_t* idx, const float* logg, float* part_ml,
                           float* part_acc, const SelectChunks& sel, hipStream_t st) {
   const size_t wgs = (size_t)dm.b * dm.hkv * nsplit;
-  const size_t lds = SEL ? (size_t)2 * sel.nchunk * dm.K * sizeof(uint64_t) : 0;
+  const size_t lds = SEL ? (size_t)sel.nchunk * dm.K * sizeof(uint64_t) : 0;
   if (bps == 8)
     hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 2>), dim3((unsigned)wgs), dim3(256), lds,
                        st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,

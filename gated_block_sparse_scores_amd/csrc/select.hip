@@ -309,12 +309,13 @@ __global__ void __launch_bounds__(256) topk_kernel(
 // or the stand-in score with fp64 dot products read by 16 lanes per summary row
 // and reduced with DPP), records the chunk's max and sum of exp, and ranks its
 // 256 composite keys (order-preserving score bits, then the complemented block
-// index, so equal scores rank the lower block first; all keys are distinct) by
-// counting, against LDS broadcasts, the keys above each one; keys of rank < K
+// index, so equal scores rank the lower block first; all keys are distinct):
+// each wave sorts its 64 keys in registers, and a key's rank adds, for every
+// other wave, the count of that wave's sorted keys above it; keys of rank < K
 // are written in rank order as the chunk's candidates.  Every block of the
-// row's Top-K is among its chunk's first K.  Stage 2 merges the sorted chunk
-// lists pairwise (log2(chunks) rounds; each output of a pair is located by a
-// merge-path binary search), combines the chunk statistics into lse_s, and
+// row's Top-K is among its chunk's first K.  Stage 2 (K <= 64) folds the sorted
+// chunk lists into one top-K list with wave-level bitonic merges, combines the
+// chunk statistics into lse_s, and
 // emits the K winners in ascending block order.
 constexpr int kChunk = 256;
 
@@ -474,7 +475,7 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
     const uint64_t* __restrict__ cand, const float2* __restrict__ stats, int T, int C,
     int row_offset, int K, int nchunk, int act, int32_t* __restrict__ idx,
     float* __restrict__ logg, float* __restrict__ lse_s, RowLens rl) {
-  extern __shared__ uint64_t lists[];  // two buffers of nchunk * K keys
+  extern __shared__ uint64_t lists[];  // nchunk * K keys
   __shared__ int widx[64];
   __shared__ float wval[64];
   __shared__ float lse_sh;
@@ -495,31 +496,13 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
                                  dscr);
     if (threadIdx.x == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
   }
-  // K <= 64: each wave folds a share of the lists into its top list in
-  // registers, then wave 0 folds the waves' lists.  Larger K: pairwise merges,
-  // keeping the top K of each pair, until one list remains.
+  // Each wave folds a share of the lists into its top list in registers, then
+  // wave 0 folds the waves' lists (the two-stage path runs with K <= 64 only).
   __shared__ uint64_t wl[4 * 64];
-  const uint64_t top = K <= 64 ? merge_top64<4>(lists, nchunk, K, wl) : 0ull;
-  uint64_t* src = lists;
-  uint64_t* dst = lists + nc;
-  int nl = K <= 64 ? 1 : nchunk;
-  while (nl > 1) {
-    const int np = nl >> 1;
-    for (int job = threadIdx.x; job < np * K; job += blockDim.x) {
-      const int pr = job / K, j = job % K;
-      dst[pr * K + j] = merge_path_kth(src + (2 * pr) * K, src + (2 * pr + 1) * K, K, j);
-    }
-    if (nl & 1)
-      for (int j = threadIdx.x; j < K; j += blockDim.x) dst[np * K + j] = src[(nl - 1) * K + j];
-    __syncthreads();
-    uint64_t* tmp = src;
-    src = dst;
-    dst = tmp;
-    nl = np + (nl & 1);
-  }
+  const uint64_t top = merge_top64<4>(lists, nchunk, K, wl);
   const int kk = min(K, ct);
   if ((int)threadIdx.x < kk) {
-    const uint64_t key = K <= 64 ? top : src[threadIdx.x];
+    const uint64_t key = top;
     widx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
     wval[threadIdx.x] = from_order_key((uint32_t)(key >> 32));
   }
@@ -576,7 +559,7 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
   {
     ProfScope ps("select_merge", st);
     hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256),
-                       (size_t)2 * nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
+                       (size_t)nchunk * K * sizeof(uint64_t), st, cand, stats, T, C, row_offset,
                        K, nchunk, act, idx, logg, lse_s, rl);
   }
   return hipGetLastError();
