@@ -432,21 +432,20 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     extern __shared__ uint64_t lists[];  // nchunk * K keys
     __shared__ int widx[64];
     __shared__ float wval[64];
-    __shared__ float fscr[16];
-    __shared__ double dscr[16];
     const int K = dm.K, nc = sel.nchunk * K;
     const int tid = threadIdx.x, nth = 64 * kDecWaves;
     const uint64_t* crow = sel.cand + (size_t)bk * nc;
     for (int i = tid; i < nc; i += nth) lists[i] = crow[i];
-    float M = -INFINITY;
-    double S = 0.0;
-    for (int i = tid; i < sel.nchunk; i += nth) M = fmaxf(M, sel.stats[(size_t)bk * sel.nchunk + i].x);
-    M = block_max(M, fscr);  // barriers: lists[] complete afterwards
-    for (int i = tid; i < sel.nchunk; i += nth) {
-      const float2 st = sel.stats[(size_t)bk * sel.nchunk + i];
-      S += st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0;
-    }
-    S = block_sum_d(S, dscr);
+    // lse_s from the chunk statistics (nchunk <= 64: lane i holds chunk i's max
+    // and sum of exp), reduced by every wave on its own, so no barrier waits on
+    // it; the selection merge kernel's arithmetic (fp32 max, fp64 sum of the
+    // chunk sums rescaled to it, one fp32 rounding of max + log(sum))
+    const float2 cst = lane < sel.nchunk ? sel.stats[(size_t)bk * sel.nchunk + lane]
+                                         : make_float2(-INFINITY, 0.0f);
+    __syncthreads();  // lists[] complete
+    const float M = wave_max(cst.x);
+    const double S =
+        wave_sum_d(cst.y > 0.0f ? (double)cst.y * exp((double)cst.x - (double)M) : 0.0);
     const int Crow = kvv.seq_lens ? min(sel.C, c) : sel.C;  // this sequence's history
     const float lse_s = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
     // wave-level folds of the chunk lists in registers (K <= 64)
