@@ -478,35 +478,37 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
   extern __shared__ uint64_t lists[];  // nchunk * K keys
   __shared__ int widx[64];
   __shared__ float wval[64];
-  __shared__ float lse_sh;
-  __shared__ float fscr[16];
-  __shared__ double dscr[16];
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
   const int ct = row_history(t, row_offset, C, rl, row / T);
   const int nc = nchunk * K;
   const uint64_t* crow = cand + row * (size_t)nc;
   for (int i = threadIdx.x; i < nc; i += blockDim.x) lists[i] = crow[i];
-  {
-    // combine the chunks' (max, sum of exp) in parallel (nchunk <= 64)
-    const float2 st = (int)threadIdx.x < nchunk ? stats[row * nchunk + threadIdx.x]
-                                                : make_float2(-INFINITY, 0.0f);
-    const float M = block_max(st.x, fscr);  // barriers: lists[] complete afterwards
-    const double S = block_sum_d(st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0,
-                                 dscr);
-    if (threadIdx.x == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
-  }
+  // The chunks' (max, sum of exp) are combined by the last wave (nchunk <= 64,
+  // lane i holds chunk i) while wave 0 folds the waves' lists: fp32 max, fp64
+  // sum of the chunk sums rescaled to it, one fp32 rounding of max + log(sum).
+  const int lane = threadIdx.x & 63, wave = (int)(threadIdx.x >> 6);
+  __shared__ float lse_sh;
+  float2 st = make_float2(-INFINITY, 0.0f);
+  if (wave == 3 && lane < nchunk) st = stats[row * nchunk + lane];
+  __syncthreads();  // lists[] complete
   // Each wave folds a share of the lists into its top list in registers, then
   // wave 0 folds the waves' lists (the two-stage path runs with K <= 64 only).
   __shared__ uint64_t wl[4 * 64];
   const uint64_t top = merge_top64<4>(lists, nchunk, K, wl);
+  if (wave == 3) {
+    const float M = wave_max(st.x);
+    const double S =
+        wave_sum_d(st.y > 0.0f ? (double)st.y * exp((double)st.x - (double)M) : 0.0);
+    if (lane == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
+  }
   const int kk = min(K, ct);
   if ((int)threadIdx.x < kk) {
     const uint64_t key = top;
     widx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
     wval[threadIdx.x] = from_order_key((uint32_t)(key >> 32));
   }
-  __syncthreads();
+  __syncthreads();  // winners and lse_sh in LDS
   const float lse = lse_sh;
   int32_t* irow = idx + row * (size_t)K;
   float* lrow = logg + row * (size_t)K;
