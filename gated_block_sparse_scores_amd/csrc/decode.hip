@@ -437,27 +437,33 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     const uint64_t* crow = sel.cand + (size_t)bk * nc;
     for (int i = tid; i < nc; i += nth) lists[i] = crow[i];
     // lse_s from the chunk statistics (nchunk <= 64: lane i holds chunk i's max
-    // and sum of exp), reduced by every wave on its own, so no barrier waits on
-    // it; the selection merge kernel's arithmetic (fp32 max, fp64 sum of the
-    // chunk sums rescaled to it, one fp32 rounding of max + log(sum))
-    const float2 cst = lane < sel.nchunk ? sel.stats[(size_t)bk * sel.nchunk + lane]
-                                         : make_float2(-INFINITY, 0.0f);
+    // and sum of exp), combined by the last wave once its folds are done, while
+    // wave 0 folds the waves' lists; the selection merge kernel's arithmetic
+    // (fp32 max, fp64 sum of the chunk sums rescaled to it, one fp32 rounding
+    // of max + log(sum)).  It reaches wave 0 through LDS at the next barrier.
+    __shared__ float lse_sh;
+    float2 cst = make_float2(-INFINITY, 0.0f);
+    if (wave == kDecWaves - 1 && lane < sel.nchunk)
+      cst = sel.stats[(size_t)bk * sel.nchunk + lane];
     __syncthreads();  // lists[] complete
-    const float M = wave_max(cst.x);
-    const double S =
-        wave_sum_d(cst.y > 0.0f ? (double)cst.y * exp((double)cst.x - (double)M) : 0.0);
     const int Crow = kvv.seq_lens ? min(sel.C, c) : sel.C;  // this sequence's history
-    const float lse_s = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
     // wave-level folds of the chunk lists in registers (K <= 64)
     __shared__ uint64_t wl[kDecWaves * 64];
     const uint64_t top = merge_top64<kDecWaves>(lists, sel.nchunk, K, wl);
+    if (wave == kDecWaves - 1) {
+      const float M = wave_max(cst.x);
+      const double S =
+          wave_sum_d(cst.y > 0.0f ? (double)cst.y * exp((double)cst.x - (double)M) : 0.0);
+      if (lane == 0) lse_sh = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
+    }
     const int kk = min(K, Crow);
     if (tid < kk) {
       const uint64_t key = top;
       widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
       wval[tid] = from_order_key((uint32_t)(key >> 32));
     }
-    __syncthreads();
+    __syncthreads();  // winners and lse_sh in LDS
+    const float lse_s = lse_sh;
     if (tid < kk) {
       const int mine = widx[tid];
       int rank = 0;
