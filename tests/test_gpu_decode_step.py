@@ -85,6 +85,7 @@ STEP_CASES = [
     (3, 5, 1, 4097, 128, 64, 64, torch.bfloat16),       # C = K = 64
     (2, 16, 2, 64 * 700 + 5, 128, 64, 31, torch.bfloat16),   # 3 chunks (odd), ragged tail
     (1, 40, 8, 64 * 2300 + 1, 128, 64, 31, torch.bfloat16),  # 9 chunks, G = 5
+    (2, 8, 2, 64 * 1300 + 7, 128, 64, 64, torch.bfloat16),   # 6 chunks, K = 64: full-width folds
     (1, 4, 4, 17, 64, 16, 2, torch.float32),            # separate-call path, short history
     (2, 8, 2, 3000, 64, 16, 8, torch.float32),          # separate-call path, two-stage select
     (1, 16, 2, 3000, 128, 32, 64, torch.bfloat16),      # separate-call path (block 32)
