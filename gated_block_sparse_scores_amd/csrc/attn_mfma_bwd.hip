@@ -267,7 +267,7 @@ template <bool OUTER>
 __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     Dims dm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-    const float* __restrict__ lse, float* __restrict__ Dv,
+    const float* __restrict__ lse, float* __restrict__ Dv, const float* __restrict__ Dsrc,
     const int32_t* __restrict__ idx, const float* __restrict__ logg, bf16_t* __restrict__ dq) {
   // Two K/V tile buffers as four separate arrays (see the forward kernel: the
   // loop is unrolled by two so that copies and transposed reads of different
@@ -332,22 +332,27 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     of[kc] = *reinterpret_cast<const bf16x8*>(dout + row * D + kc * 16 + g * 8);
   }
   const float l2 = lse[row] * LOG2E;
-  // D = dO . o for this lane's row: 64 dims per lane half, then the halves;
-  // also stored for the dK / dV kernel, which runs after this one.
-  // D as a fixed tree over the 16 chunk partials p(kc, g) (8 dims each):
-  // pairs in kc, then quads, then the two halves (bwd_dval_kernel sums alike)
-  float pd[8];
+  float dval;
+  if (Dsrc) {
+    dval = Dsrc[row];  // formed by bwd_dval_kernel with the same sums as below
+  } else {
+    // D = dO . o for this lane's row: 64 dims per lane half, then the halves;
+    // also stored for the dK / dV kernel, which runs after this one.
+    // D as a fixed tree over the 16 chunk partials p(kc, g) (8 dims each):
+    // pairs in kc, then quads, then the two halves (bwd_dval_kernel sums alike)
+    float pd[8];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * D + kc * 16 + g * 8);
-    float a = 0.0f;
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * D + kc * 16 + g * 8);
+      float a = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a = fmaf((float)of[kc][e], (float)ov[e], a);
-    pd[kc] = a;
+      for (int e = 0; e < 8; ++e) a = fmaf((float)of[kc][e], (float)ov[e], a);
+      pd[kc] = a;
+    }
+    dval = ((pd[0] + pd[1]) + (pd[2] + pd[3])) + ((pd[4] + pd[5]) + (pd[6] + pd[7]));
+    dval += __shfl_xor(dval, 32);
+    if (g == 0 && Dv) Dv[row] = dval;
   }
-  float dval = ((pd[0] + pd[1]) + (pd[2] + pd[3])) + ((pd[4] + pd[5]) + (pd[6] + pd[7]));
-  dval += __shfl_xor(dval, 32);
-  if (g == 0 && Dv) Dv[row] = dval;  // (null when a separate kernel formed D)
   f32x16 dqa[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -482,15 +487,16 @@ SideStream* side_stream() {
   return &ss;
 }
 
+// Dv: where dQ stores the D it forms; Dsrc: D formed beforehand (then o is not read).
 void launch_dq(const Dims& dm, const void* q, const void* k, const void* v, const void* o,
-               const void* dout, const float* lse, float* Dv, const int32_t* idx,
-               const float* logg, void* dq, hipStream_t st) {
+               const void* dout, const float* lse, float* Dv, const float* Dsrc,
+               const int32_t* idx, const float* logg, void* dq, hipStream_t st) {
   const size_t tiles = (size_t)dm.b * dm.hkv * dm.T * (dm.g / HPW);
   ProfScope ps("bwd_dq_mfma", st);
   auto kern = dm.outer ? bwd_dq_mfma_kernel<true> : bwd_dq_mfma_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DQ_NT), 0, st, dm, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, (const bf16_t*)dout,
-                     lse, Dv, idx, logg, (bf16_t*)dq);
+                     lse, Dv, Dsrc, idx, logg, (bf16_t*)dq);
 }
 
 void launch_dkdv(const Dims& dm, const void* q, const void* k, const void* v, const void* dout,
@@ -529,7 +535,7 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
     if (ss && dkdv_wgs > (size_t)4 * ss->cus) ss = nullptr;
   }
   if (!ss) {
-    launch_dq(dm, q, k, v, o, dout, lse, ws.D, idx, logg, dq, st);
+    launch_dq(dm, q, k, v, o, dout, lse, ws.D, nullptr, idx, logg, dq, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
@@ -546,7 +552,7 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
   if ((e = hipEventRecord(ss->fork, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
-  launch_dq(dm, q, k, v, o, dout, lse, nullptr, idx, logg, dq, ss->s);
+  launch_dq(dm, q, k, v, o, dout, lse, nullptr, ws.D, idx, logg, dq, ss->s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
   return hipStreamWaitEvent(st, ss->join, 0);
