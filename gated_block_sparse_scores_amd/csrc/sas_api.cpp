@@ -83,7 +83,11 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.on) return;
   ProfRecord r{name, p.take(), p.take()};
-  if (!r.start || !r.stop) return;
+  if (!r.start || !r.stop) {  // event creation failed: this launch goes untimed
+    if (r.start) p.pool.push_back(r.start);
+    if (r.stop) p.pool.push_back(r.stop);
+    return;
+  }
   (void)hipEventRecord(r.start, s);
   open_records.push_back(r);
   slot = (int)open_records.size() - 1;
