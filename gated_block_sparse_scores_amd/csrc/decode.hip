@@ -534,12 +534,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
 
     // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
-    // With four waves of one block (separate decode and fused step) the V
-    // loads are issued after the score products instead, into the registers K
-    // held: 30 fewer registers, and V's latency overlaps the softmax (measured
-    // 6% faster for the separate decode, 2% for the fused step at 512K; the
-    // other shapes are slower that way).
-    constexpr bool kLateV = kDecWaves == 4 && kBpw == 1;
+    // With one block per wave the V loads are issued after the score products
+    // instead, into the registers K held: 30 fewer registers, and V's latency
+    // overlaps the softmax (measured: separate decode 6% faster with four waves
+    // per workgroup at 8x64K and 8% with one wave at 512K, fused step 2% at
+    // 512K).  With two blocks per wave it was slower.
+    constexpr bool kLateV = kBpw == 1;
     bf16x8_t kf[4][4];
     uint32_t vr[BS];
     auto load_v = [&]() {
