@@ -784,9 +784,9 @@ bool decode_mfma_path(const Dims& dm) { return dm.bf16 && dm.d == 128 && dm.bs =
 // Four waves of two blocks each per workgroup (MFMA path): when that still
 // fills every CU with two workgroups, the grid runs in one round, each wave's
 // second block loading after its first is folded.  Measured faster for the
-// paged decode and the fused steps (half as many workgroups merge the chunk
-// candidates), slower for the dense separate decode, which keeps one block
-// per wave.
+// paged decode and the paged fused step; the dense separate decode and the
+// dense fused step keep one block per wave, whose V loads wait until after
+// the score products (faster for them).
 bool decode_two_per_wave(const Dims& dm) {
   return decode_mfma_path(dm) && (long)dm.b * dm.hkv * ((dm.K + 8) / 8) >= 512;
 }
@@ -829,10 +829,10 @@ hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, i
                               void* o, float* lse, void* ws, hipStream_t st) {
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
   // Four waves per workgroup whatever the grid: every workgroup merges the
-  // row's chunk candidates first, which 256 threads do four times faster than
-  // 64; two blocks per wave when the separate decode takes them too (the
-  // partial buffer of decode_workspace_bytes covers this split count).
-  const int bps = decode_two_per_wave(dm) ? 8 : 4;
+  // row's chunk candidates first, which four waves share; two blocks per wave
+  // when the paged decode takes them too (the partial buffer of
+  // decode_workspace_bytes covers either split count).
+  const int bps = kvv.table && decode_two_per_wave(dm) ? 8 : 4;
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
