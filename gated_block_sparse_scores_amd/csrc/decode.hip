@@ -341,14 +341,21 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(int nsplit, int D,
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;  // no key at all: o = 0, lse = -inf
   const float* acc = part_acc + row * nsplit * D;
   for (int dd = lane; dd < D; dd += 64) {
-    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // the splits' loads go out sixteen (then eight) at a time: one memory round
+    // trip per batch, the batch's terms spread over independent partial sums
+    float a[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     int s = 0;
+    for (; s + 16 <= nsplit; s += 16) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a[u] += w[s + u] * acc[(size_t)(s + u) * D + dd];
+    }
     for (; s + 8 <= nsplit; s += 8) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) a[u] += w[s + u] * acc[(size_t)(s + u) * D + dd];
     }
     for (; s < nsplit; ++s) a[0] += w[s] * acc[(size_t)s * D + dd];
-    const float tot = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    const float tot = (((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]))) +
+                      (((a[8] + a[9]) + (a[10] + a[11])) + ((a[12] + a[13]) + (a[14] + a[15])));
     Elem<T>::store(o, row * D + dd, tot * inv);
   }
   if (lane == 0) lse[row] = Ls > 0.0f ? M + logf(Ls) : -INFINITY;
