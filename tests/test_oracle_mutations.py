@@ -106,6 +106,37 @@ def _gate_log_sigmoid_as_softmax(s_vals, lse, act="softmax"):
     return _orig_gate_log(s_vals, lse, "softmax" if act == "sigmoid" else act)
 
 
+_orig_decode = O.decode
+_orig_key_block = O.bwd_key_block
+
+
+def _decode_qbar_transposed_groups(q, hkv):
+    q = O._np64(q)
+    b, hq, d = q.shape
+    return q.reshape(b, hq // hkv, hkv, d).mean(axis=1)[:, :, None, :]
+
+
+def _decode_outer_ignored(q, kcache, vcache, L, idx, logg, bs, scale=None, outer=False):
+    return _orig_decode(q, kcache, vcache, L, idx, logg, bs, scale, False)
+
+
+def _key_block_without_diagonal(q, k, v, dout, idx, logg, bs, scale, bb, kv, m, outer=False):
+    n = q.shape[2]
+    lo, hi = O.block_span(m, bs, n)
+    dk = np.zeros((hi - lo, q.shape[3]))
+    dv = np.zeros_like(dk)
+    idx_np = O._npint(idx[bb, kv])
+    for t in range(m + 1, O.n_blocks(n, bs)):
+        if m not in idx_np[t].tolist():
+            continue
+        _, _, (J, dkj, dvj) = O.bwd_row_block(q, k, v, dout, idx, logg, bs, scale, bb, kv, t,
+                                              outer)
+        sel = (J >= lo) & (J < hi)
+        dk[J[sel] - lo] += dkj[sel]
+        dv[J[sel] - lo] += dvj[sel]
+    return dk, dv
+
+
 MUTATIONS = [
     ("ds_row", _ds_row_no_softmax_term),
     ("topk_history", _topk_ties_high_index),
@@ -122,6 +153,9 @@ MUTATIONS = [
     ("ds_row", _ds_row_ste_without_gate),
     ("fwd_row_block", _fwd_row_outer_ignored),
     ("gate_log", _gate_log_sigmoid_as_softmax),
+    ("decode_qbar", _decode_qbar_transposed_groups),
+    ("decode", _decode_outer_ignored),
+    ("bwd_key_block", _key_block_without_diagonal),
 ]
 
 PINS = [
@@ -142,6 +176,9 @@ PINS = [
     lambda: pins.test_p16_variant_finite_differences("sigmoid", False),
     lambda: pins.test_p16_variant_finite_differences("softmax", True),
     lambda: pins.test_p17_straight_through("softmax"),
+    pins.test_p20_decode_qbar_groups_the_heads_of_each_kv_head,
+    lambda: pins.test_p21_outer_decode_equals_last_outer_forward_row(61),
+    pins.test_p22_key_block_gradients_equal_the_full_backward,
 ]
 
 

@@ -597,26 +597,28 @@ def test_p14_gate_activations_closed_forms():
 
 def _outer_reference(q, k, v, idx, logg, bs):
     """o = softmax(q K_J^T / sqrt(d), causal on the current block) @ (g * V_J),
-    written with torch ops per query block (outer gating)."""
+    written with torch ops per query block and head (outer gating; query head h
+    reads KV head h // G and that KV head's selection)."""
     b, hq, n, d = q.shape
     g_ = hq // k.shape[1]
     out = torch.zeros(b, hq, n, d, dtype=F64)
     for t in range(O.n_blocks(n, bs)):
         lo, hi = O.block_span(t, bs, n)
-        keys, gains = [], []
-        for sl, m in enumerate(idx[0, 0, t].tolist()):
-            if m >= 0:
-                mlo, mhi = O.block_span(m, bs, n)
-                keys += list(range(mlo, mhi))
-                gains += [math.exp(logg[0, 0, t, sl])] * (mhi - mlo)
-        keys += list(range(lo, hi))
-        gains += [1.0] * (hi - lo)
-        J = torch.tensor(keys)
         for h in range(hq):
-            z = q[0, h, lo:hi] @ k[0, h // g_, J].T / math.sqrt(d)
+            kv = h // g_
+            keys, gains = [], []
+            for sl, m in enumerate(idx[0, kv, t].tolist()):
+                if m >= 0:
+                    mlo, mhi = O.block_span(m, bs, n)
+                    keys += list(range(mlo, mhi))
+                    gains += [math.exp(logg[0, kv, t, sl])] * (mhi - mlo)
+            keys += list(range(lo, hi))
+            gains += [1.0] * (hi - lo)
+            J = torch.tensor(keys)
+            z = q[0, h, lo:hi] @ k[0, kv, J].T / math.sqrt(d)
             future = (J[None, :] > torch.arange(lo, hi)[:, None]) & (J[None, :] >= lo)
             z = z.masked_fill(future, -math.inf)
-            out[0, h, lo:hi] = torch.softmax(z, 1) @ (v[0, h // g_, J] *
+            out[0, h, lo:hi] = torch.softmax(z, 1) @ (v[0, kv, J] *
                                                      torch.tensor(gains, dtype=F64)[:, None])
     return out
 
@@ -834,3 +836,97 @@ def test_p19_ragged_batch():
     # and the short sequence alone is the dense method on its 21 tokens
     alone = O.ragged_train(q[1:], k[1:], v[1:], dout[1:], [21], K, bs, standin=True)
     np.testing.assert_array_equal(alone["o"][0], r1["o"][1])
+
+
+# ---------------------------------------------------------------- P20: decode query pooling per KV head
+
+def test_p20_decode_qbar_groups_the_heads_of_each_kv_head():
+    """picx 'Efficiency Benefits' (GQA with per-group selection): in decode the
+    selector's query summary of KV head kv is the mean of the one new token's
+    G query heads that read kv, i.e. heads h with h // G == kv.  Checked with
+    hkv = 3, G = 4 (a transposed grouping gives other heads) against an
+    accumulation keyed by h // G, against torch's mean over each head slice,
+    and against the training pool (pinned above) of a one-token sequence with
+    block 1; the decode scores it gives equal the group mean of the per-head
+    scores q_h . kbar (linearity)."""
+    b, hkv, G, d, C = 2, 3, 4, 5, 6
+    gen = torch.Generator().manual_seed(53)
+    q = torch.randn(b, hkv * G, d, generator=gen, dtype=F64)
+    kbar = torch.randn(b, hkv, C, d, generator=gen, dtype=F64)
+    qb = O.decode_qbar(q, hkv)
+    assert qb.shape == (b, hkv, 1, d)
+    acc = np.zeros((b, hkv, d))
+    cnt = np.zeros(hkv)
+    for h in range(hkv * G):
+        acc[:, h // G] += q[:, h].numpy()
+        cnt[h // G] += 1
+    np.testing.assert_allclose(qb[:, :, 0], acc / cnt[None, :, None], atol=1e-15)
+    for kv in range(hkv):
+        np.testing.assert_allclose(qb[:, kv, 0], q[:, kv * G:(kv + 1) * G].mean(dim=1).numpy(),
+                                   atol=1e-15)
+    np.testing.assert_allclose(qb, O.pool_queries(q[:, :, None, :], hkv, 1), atol=1e-15)
+    per_head = torch.stack([(q[:, h][:, None, :] * kbar[:, h // G]).sum(-1)
+                            for h in range(hkv * G)], dim=1)            # [b, hq, C]
+    group_mean = per_head.reshape(b, hkv, G, C).mean(2) / math.sqrt(d)
+    s = O.standin_scores(qb, kbar.numpy(), 1.0 / math.sqrt(d), C, row_offset=C)
+    np.testing.assert_allclose(s[:, :, 0], group_mean.numpy(), rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------- P21: outer-gated decode
+
+@pytest.mark.parametrize("L", [64, 61])
+def test_p21_outer_decode_equals_last_outer_forward_row(L):
+    """Outer gating ([picx] 'Gradient Analysis' Eq. 5, right: the gate scales a
+    block's values after an ungated softmax) in decode: the token at position
+    L - 1 under its block's selection equals row L - 1 of the outer-gated
+    forward (pinned by P15) and of the torch-written outer reference, for
+    every head of two KV heads; its LSE is the ungated softmax's."""
+    bs, K = 8, 3
+    w, x = small(seed=59, hq=4, hkv=2, n=L, d=8, bs=bs, K=K)
+    idx, logg, _ = select(x, K)
+    t = (L - 1) // bs
+    assert np.any(logg[:, :, t] < -1e-3)          # the gates really differ from 1
+    o, lse = O.attn_fwd(x["q"], x["k"], x["v"], idx, logg, bs, outer=True)
+    od, lsed = O.decode(x["q"][:, :, L - 1], x["k"], x["v"], L, idx[:, :, t], logg[:, :, t], bs,
+                        outer=True)
+    np.testing.assert_allclose(od, o[:, :, L - 1], atol=1e-13)
+    np.testing.assert_allclose(lsed, lse[:, :, L - 1], atol=1e-13)
+    q, k, v = (x[n_].to(F64) for n_ in ("q", "k", "v"))
+    ref = _outer_reference(q, k, v, idx, logg, bs)
+    np.testing.assert_allclose(od, ref[:, :, L - 1].numpy(), atol=1e-13)
+    # the ungated LSE: torch.logsumexp over the row's selected and causal keys
+    for h in range(4):
+        keys = [j for m in idx[0, h // 2, t] if m >= 0 for j in range(m * bs, (m + 1) * bs)]
+        keys += list(range(t * bs, L))
+        z = q[0, h, L - 1] @ k[0, h // 2, keys].T / math.sqrt(8)
+        assert abs(lsed[0, h] - float(torch.logsumexp(z, 0))) <= 1e-13
+
+
+# ---------------------------------------------------------------- P22: per-key-block dk / dv
+
+def test_p22_key_block_gradients_equal_the_full_backward():
+    """dk, dv of one key block B_m are the sums over the row blocks whose key
+    set holds B_m: the blocks that selected m and m itself on the diagonal
+    ([picx] 'Gradient Analysis' Eq. 5, left; 'Kernel Design': key-side
+    gradients gathered from the selecting rows).  For every key block of both
+    KV heads they equal the full backward's dk, dv on that block's rows (the
+    full backward is pinned by P1, P4 and P6), under inner and outer gating;
+    block 1 is selected by every later row block and the last block is partial."""
+    bs, K, n = 8, 2, 60
+    w, x = small(seed=61, hq=4, hkv=2, n=n, d=8, bs=bs, K=K)
+    T = O.n_blocks(n, bs)
+    s = x["s"].clone()
+    s[..., 1] += 6.0                               # block 1 wins every row that sees it
+    idx, logg, lse_s = O.select_topk(s, K)
+    for kv in range(2):
+        assert all(1 in idx[0, kv, t].tolist() for t in range(2, T))
+    scale = O.default_scale(8)
+    for outer in (False, True):
+        gr = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], idx, logg, s, lse_s, bs, outer=outer)
+        for kv in range(2):
+            for m in range(T):
+                dk, dv = O.bwd_key_block(x["q"], x["k"], x["v"], x["dout"], idx, logg, bs, scale,
+                                         0, kv, m, outer)
+                lo, hi = O.block_span(m, bs, n)
+                np.testing.assert_allclose(dk, gr["dk"][0, kv, lo:hi], atol=1e-12, rtol=0)
+                np.testing.assert_allclose(dv, gr["dv"][0, kv, lo:hi], atol=1e-12, rtol=0)
