@@ -55,20 +55,27 @@ def selected_pairs_device(idx, n, bs, g):
     return (hist + cur) * g
 
 
-def train_step_fn(w, x, ws, gate=0, K=None):
+def train_step_fn(w, x, ws, gate=0, K=None, seq_lens=None):
+    """One training step of the stand-in workload.  With seq_lens (every
+    sequence at full length, so the results are bitwise those of the dense
+    call) the library runs the backward's dQ and dK/dV kernels one after the
+    other on one stream, which times each kernel alone."""
     import torch
     from gated_block_sparse_scores_amd import ops
     T = w.nblocks
     K = w.topk if K is None else K
+    rl = {} if seq_lens is None else {"seq_lens": seq_lens}
+    sel_rl = {} if seq_lens is None else {"seq_lens": seq_lens, "seqlen": w.seqlen,
+                                          "block": w.block}
 
     def step():
-        qb = ops.block_pool(x["q"], w.block, w.group)
-        kb = ops.block_pool(x["k"], w.block, 1)
+        qb = ops.block_pool(x["q"], w.block, w.group, **rl)
+        kb = ops.block_pool(x["k"], w.block, 1, **rl)
         idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, K, qbar=qb, kbar=kb,
-                                              gate=gate)
-        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block, gate=gate)
+                                              gate=gate, **sel_rl)
+        o, lse = ops.attn_fwd(x["q"], x["k"], x["v"], idx, logg, w.block, gate=gate, **rl)
         gr = ops.attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, s, lse_s,
-                          w.block, workspace=ws, gate=gate)
+                          w.block, workspace=ws, gate=gate, **rl)
         return idx, gr, qb, kb
     return step
 
@@ -106,6 +113,25 @@ def bench_gate_variants(args, w, x):
                      "TFLOPs": round(12 * w.head_dim * pairs / (ms * 1e-3) / 1e12, 2),
                      "selected_pairs": int(pairs)}
         del ws
+    return out
+
+
+def kernel_rooflines(kt, pairs, d, workload):
+    """Roofline of every MFMA kernel from its average launch time (ms) in kt:
+    algorithmic FLOPs (selected pairs only: forward 4d; backward 8d split as
+    dK/dV 6d for dP, dV, dK and dQ 2d) over the kernel's own duration."""
+    out = {}
+    for name, (n, tot) in kt.items():
+        kf = kernel_flops(name, pairs, d)
+        if kf is None:
+            continue
+        avg_ms = tot / n
+        ach = kf / (avg_ms * 1e-3) / 1e12
+        out[name] = {"bound": "mfma", "kernel": name, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(name, workload),
+                     "avg_launch_ms": round(avg_ms, 4), "gflop_per_launch": round(kf / 1e9, 2)}
     return out
 
 
@@ -212,7 +238,8 @@ def bench_train(args):
     tflops = flops / (ms * 1e-3) / 1e12
     # Kernel durations: the same steps again with a HIP event pair recorded
     # around every launch on its stream (the events add a little time between
-    # kernels, so this pass is not the step time).
+    # kernels, so this pass is not the step time).  At this size dQ runs on a
+    # second stream beside dK/dV, so their event spans overlap.
     L.sas_profiler_reset()
     L.sas_profiler_enable(True)
     t2 = time.perf_counter()
@@ -223,25 +250,29 @@ def bench_train(args):
     L.sas_profiler_enable(False)
     kt = L.sas_profiler_read()
     ms_events = (t3 - t2) * 1e3 / args.steps
-    # dominant kernel: dK/dV (the largest when the kernels run one after another;
-    # at this size dQ runs beside it, so dQ's event span includes the time the
-    # two share the GPU and is no measure of dQ alone)
-    if "bwd_dkdv_mfma" in kt:
-        name, (n, tot) = "bwd_dkdv_mfma", kt["bwd_dkdv_mfma"]
-    else:
-        name, (n, tot) = max(kt.items(), key=lambda kv: kv[1][1])
-    avg_ms = tot / n
-    kf = kernel_flops(name, pairs, w.head_dim)
-    mfma = "mfma" in name
-    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
-    roof = None
-    if kf is not None:
-        ach = kf / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma" if mfma else "alu", "kernel": name, "achieved": round(ach, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": recorded_traffic(name, w.name), "avg_launch_ms": round(avg_ms, 4)}
+    # Each kernel alone: the same steps through the ragged-batch entry with
+    # every sequence at full length (bitwise the same results), where the
+    # backward runs dQ, then dK/dV, on one stream.  The rooflines use these
+    # durations; the dominant kernel is the longest one.
+    full = torch.full((w.batch,), w.seqlen, dtype=torch.int32, device=dev)
+    step_serial = train_step_fn(w, x, ws, seq_lens=full)
+    for _ in range(3):
+        step_serial()
+    torch.cuda.synchronize()
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    for _ in range(args.steps):
+        step_serial()
+    torch.cuda.synchronize()
+    L.sas_profiler_enable(False)
+    kt_alone = L.sas_profiler_read()
+    roofs = kernel_rooflines(kt_alone, pairs, w.head_dim, w.name)
+    roof = max(roofs.values(), key=lambda r: r["avg_launch_ms"]) if roofs else None
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
+    kernels_alone = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)}
+                     for k, v in kt_alone.items()}
     return dict(w=w, pairs=pairs, flops=flops, ms=ms, tflops=tflops, roofline=roof,
+                kernel_rooflines=roofs, kernels_alone=kernels_alone,
                 ms_with_kernel_events=ms_events,
                 kernels=kernels, x=x, idx=idx, selector_bwd=bench_selector_bwd(args, w, gr, qb, kb),
                 gate_variants=None if args.no_variants else bench_gate_variants(args, w, x),
@@ -283,9 +314,22 @@ def bench_train_32k(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     flops = 12 * w.head_dim * pairs
+    # kernel durations (at this size the backward already runs dQ, then dK/dV)
+    L.sas_profiler_reset()
+    L.sas_profiler_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    L.sas_profiler_enable(False)
+    kt = L.sas_profiler_read()
+    roofs = kernel_rooflines(kt, pairs, w.head_dim, w.name)
     return {"workload": w.name, "selected_pairs": int(pairs), "steps": steps,
             "ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": max(roofs.values(), key=lambda r: r["avg_launch_ms"]) if roofs else None,
+            "kernel_rooflines": roofs,
+            "kernels": {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)}
+                        for k, v in kt.items()}}
 
 
 def bench_ragged_train(args):
@@ -376,11 +420,39 @@ def bench_selector_bwd(args, w, gr, qb, kb):
             "pool_spread_frac_of_hbm_peak": None if gbs is None else round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def bench_decode(wl, steps, layers=12):
+def oracle_decode_baseline(w, kc, vc, kb, q, Lc):
+    """The fp64 oracle, as it stands, on one call of a decode workload: its
+    selection from the pooled query and the (device-pooled, bf16) pooled-key
+    cache, then its decode over the selected blocks; host cores only."""
+    from oracle import sas_oracle as O
+    kc, vc, q = kc.cpu(), vc.cpu(), q.cpu()
+    kb32 = kb.float().cpu().numpy()
+    C = (Lc - 1) // w.block
+    t0 = time.perf_counter()
+    qb = O.to_f32(O.decode_qbar(q, w.hkv))
+    s = O.standin_scores(qb, kb32, O.default_scale(w.head_dim), C, row_offset=C)
+    idx, logg, _ = O.select_topk(s, w.topk, row_offset=C, C=C)
+    t1 = time.perf_counter()
+    O.decode(q, kc, vc, Lc, idx[:, :, 0], logg[:, :, 0], w.block)
+    t2 = time.perf_counter()
+    sel_bytes = w.batch * w.hkv * (w.topk + 1) * w.block * w.head_dim * 2 * 2
+    kbar_bytes = w.batch * w.hkv * C * w.head_dim * 2
+    return {"workload": w.name, "selection_s": round(t1 - t0, 3),
+            "selection_GBps": round(kbar_bytes / (t1 - t0) / 1e9, 3),
+            "decode_s": round(t2 - t1, 3),
+            "decode_GBps": round(sel_bytes / (t2 - t1) / 1e9, 3),
+            "sample": "one call (batch of one new token per sequence), the same shapes"}
+
+
+def bench_decode(wl, steps, layers=12, kbar_layers=64, cpu=False):
     """Decode of one new token per sequence.  Each call takes a fresh random
     query (so a new selection) and the calls rotate over `layers` distinct K/V
-    caches with their own pooled-key caches, as consecutive layers of a model
-    would: 2 GiB of K/V per layer, far more than the last-level cache holds.
+    caches (K and V 1 GiB each per layer at both workloads) and, independently,
+    over `kbar_layers` distinct pooled-key caches (16.8 MB each, 1.07 GB in all,
+    four times the 256 MB last-level cache), as consecutive layers of a model
+    would, so both the selection's pooled-key stream and the selected blocks
+    come from HBM.  Pooled-key cache i is the pool of K/V layer i % layers for
+    i < layers, and a perturbed copy of it (bf16, + N(0, 0.01^2)) beyond.
     One call = pool the query over its head group, stand-in scores over the
     pooled-key cache + gate normalisation + Top-K, split-K decode + LSE merge,
     through the separate calls; the same calls are then timed as fused steps
@@ -394,23 +466,29 @@ def bench_decode(wl, steps, layers=12):
     dev = "cuda"
     Lc = w.seqlen
     C = (Lc - 1) // w.block
-    caches = []
+    caches, kbars = [], []
     for layer in range(layers):
         x = synth.decode_inputs(w, seed=w.number * 1000 + layer, device=dev)
-        kb = ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16)
-        caches.append((x["kcache"], x["vcache"], kb))
+        kbars.append(ops.block_pool(x["kcache"], w.block, 1, torch.bfloat16))
+        caches.append((x["kcache"], x["vcache"]))
         del x
-    torch.cuda.synchronize()
     gen = torch.Generator(device=dev).manual_seed(1000 + wl)
+    for i in range(layers, kbar_layers):
+        kb = kbars[i % layers].float()
+        kb += 0.01 * torch.randn(kb.shape, generator=gen, device=dev)
+        kbars.append(kb.to(torch.bfloat16))
+        del kb
+    torch.cuda.synchronize()
     qshape = (w.batch, w.hq, w.head_dim)
-    calls = steps * layers
+    calls = max(steps * layers, 2 * kbar_layers)
     qs = [torch.randn(qshape, generator=gen, device=dev).to(torch.bfloat16)
           for _ in range(calls + layers)]
     sh = ops.shape_of(qs[0], caches[0][0], w.block, seqlen=Lc)
     ws = torch.empty(L.sas_decode_workspace_size(sh, w.topk), dtype=torch.uint8, device=dev)
 
-    def one(q, layer):
-        kc, vc, kb = caches[layer]
+    def one(q, c):
+        kc, vc = caches[c % layers]
+        kb = kbars[c % kbar_layers]
         qb = ops.block_pool(q.unsqueeze(2), w.block, w.group)
         idx, logg, _, _ = ops.select_topk(w.batch, w.hkv, 1, C, w.topk, row_offset=C, qbar=qb,
                                           kbar=kb)
@@ -424,7 +502,7 @@ def bench_decode(wl, steps, layers=12):
             L.sas_profiler_enable(True)
         t0 = time.perf_counter()
         for c in range(calls):
-            fn(qs[c], c % layers)
+            fn(qs[c], c)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         kt_ = None
@@ -460,8 +538,9 @@ def bench_decode(wl, steps, layers=12):
     ws_step = torch.empty(L.sas_decode_step_workspace_size(sh, w.topk), dtype=torch.uint8,
                           device=dev)
 
-    def one_step(q, layer):
-        kc, vc, kb = caches[layer]
+    def one_step(q, c):
+        kc, vc = caches[c % layers]
+        kb = kbars[c % kbar_layers]
         return ops.decode_step(q, kb, kc, vc, Lc, w.topk, w.block, with_selection=False,
                                workspace=ws_step)
 
@@ -477,13 +556,17 @@ def bench_decode(wl, steps, layers=12):
         "wall_us_per_call": round(step_wall_us, 2),
         "kernels": {k: {"launches": v[0], "avg_us": round(v[1] / v[0] * 1e3, 2)}
                     for k, v in kt2.items()},
-        "graph": graph_replays(one_step, qs[calls:], layers, calls),
+        "graph": graph_replays(one_step, qs, kbar_layers, calls),
     }
-    del caches
+    oracle_cpu = (oracle_decode_baseline(w, caches[0][0], caches[0][1], kbars[0], qs[0], Lc)
+                  if cpu else None)
+    del caches, kbars
     torch.cuda.empty_cache()
     return {
+        "cpu_oracle": oracle_cpu,
         "workload": w.name, "batch": w.batch, "context": Lc, "hq": w.hq, "hkv": w.hkv,
-        "topk": w.topk, "layers_rotated": layers, "calls": calls,
+        "topk": w.topk, "layers_rotated": layers, "pooled_key_caches_rotated": kbar_layers,
+        "calls": calls,
         "selected_kv_bytes": sel_bytes, "pooled_key_bytes": kbar_bytes,
         "decode_GBps": round(dec_gbs, 1),
         "decode_frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
@@ -502,32 +585,33 @@ def bench_decode(wl, steps, layers=12):
     }
 
 
-def graph_replays(one_step, qs, layers, calls):
-    """The fused step of each layer captured once in a HIP graph (its query in a
-    static buffer), then the graphs replayed round-robin over the layers, as a
-    serving loop that launches one graph per layer would: wall time per replay.
-    The layers' caches rotate, so the selected blocks still come from HBM."""
+def graph_replays(one_step, qs, ngraphs, calls):
+    """The fused step of call i (i < ngraphs: its K/V layer and pooled-key cache)
+    captured once in a HIP graph (its query in a static buffer), then the graphs
+    replayed round-robin, as a serving loop that launches one graph per layer
+    would: wall time per replay.  The caches rotate, so the pooled keys and the
+    selected blocks still come from HBM."""
     import torch
-    qstat = [q.clone() for q in qs[:layers]]
+    qstat = [q.clone() for q in qs[:ngraphs]]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):              # warm-up outside the captures
-        for layer in range(layers):
-            one_step(qstat[layer], layer)
+        for i in range(ngraphs):
+            one_step(qstat[i], i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
-    for layer in range(layers):
+    for i in range(ngraphs):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            one_step(qstat[layer], layer)
+            one_step(qstat[i], i)
         graphs.append(g)
     for g in graphs:
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for c in range(calls):
-        graphs[c % layers].replay()
+        graphs[c % ngraphs].replay()
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) * 1e6 / calls
     del graphs
@@ -663,8 +747,18 @@ def cpu_baseline(res, budget_s=15.0):
         pairs = (nsel * w.block * w.block + w.block * (w.block + 1) // 2) * w.group
         flops += 12 * w.head_dim * pairs
         done += 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(flops / t_rows / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
+            "selection_s": round(t_sel, 3),
             "sample": f"fp64 numpy oracle: selection over all {w.hkv * T} rows "
                       f"({t_sel:.1f} s), then forward+backward of {done} of the "
                       f"{w.hkv * T} (KV head, query block) rows ({t_rows:.1f} s); value = "
@@ -720,7 +814,9 @@ def main():
             "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
             "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
             "roofline": res["roofline"],
+            "kernel_rooflines": res["kernel_rooflines"],
             "kernels": res["kernels"],
+            "kernels_alone": res["kernels_alone"],
             "ms_per_step_with_kernel_events": round(res["ms_with_kernel_events"], 4),
             "selector_bwd": res["selector_bwd"],
             "gate_variants": res["gate_variants"],
@@ -730,7 +826,8 @@ def main():
     if args.part in ("all", "decode") and not args.no_decode:
         log("decode workloads ...")
         steps = {4: 10, 5: 25}
-        out["decode"] = [bench_decode(int(wl), steps=steps.get(int(wl), 10))
+        out["decode"] = [bench_decode(int(wl), steps=steps.get(int(wl), 10),
+                                      cpu=int(wl) == 4 and not args.no_cpu_baseline)
                          for wl in args.decode_workloads.split(",") if wl]
         if not args.no_paged:
             log("paged ragged decode ...")
@@ -738,6 +835,9 @@ def main():
     if res is not None and not args.no_cpu_baseline:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(res)
+        for dec in out.get("decode", []):
+            if dec.get("cpu_oracle"):
+                out["cpu_baseline"]["decode"] = dec["cpu_oracle"]
     print(json.dumps(out), flush=True)
 
 

@@ -1,5 +1,5 @@
 // Fused gated block-sparse backward with bf16 MFMA (gfx950): head_dim 128,
-// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv a multiple of 4.
+// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv even.
 //
 // picx.dev summary of SAS, 'Gradient Analysis' Eq. 5 (inner gating): the
 // gradient of a block's log gate is the sum of dS over that block's keys
@@ -8,29 +8,35 @@
 //
 // Two kernels, no floating-point atomics (results are bitwise reproducible):
 //  * dK/dV (key-major): one workgroup of four waves per (batch, KV head, key
-//    block m).  Wave w owns keys 32*(w%2)..+32 of the block (K, V fragments in
-//    registers) and query rows 32*(w/2)..+32 of every visited query tile; its
-//    partial dK^T, dV^T stay in registers and the two query halves are summed
-//    through LDS at the end.  The workgroup visits the diagonal query block
-//    t = m and every later query block whose selection holds m (read from the
-//    slot map, compacted 256 at a time), for each of the G heads, staging that
-//    head's 64 rows of q and dout in LDS row-major: rows are the A operand of
-//    S = Q K^T and dP = dO V^T, and the transposing LDS read
-//    (ds_read_b64_tr_b16) gives the A operand of dK^T = Q^T dS, dV^T = dO^T P.
-//    Block m is the only owner of the (t, slot) pairs that selected it, so it
-//    also writes dlogg[t][slot] (sum over G heads, 64 rows, 64 keys) directly.
-//  All tiles are copied global -> LDS with the direct-to-LDS load into double
-//  buffers (the next tile streams in while the current one is computed) and
-//  laid out swizzled so that row fragments and transposed reads are both free
-//  of bank conflicts.
+//    block m), two workgroups per CU.  Wave w computes S and dP for keys
+//    32*(w%2)..+32 of the block (K, V fragments in registers) and query rows
+//    32*(w/2)..+32 of every visited query tile, and accumulates dK^T, dV^T for
+//    those keys and head dims 64*(w/2)..+64 over all 64 rows, taking the P / dS
+//    fragments of the other 32 rows from its partner wave (w ^ 2) through LDS;
+//    each wave owns its part of dK and dV, with no reduction at the end.  The
+//    workgroup visits the diagonal query block t = m and every later query
+//    block whose selection holds m (read from the slot map, compacted 256 at a
+//    time), for each of the G heads, staging that head's 64 rows of q and dout
+//    in LDS row-major: rows are the A operand of S = Q K^T and dP = dO V^T, and
+//    the transposing LDS read (ds_read_b64_tr_b16) gives the A operand of
+//    dK^T = Q^T dS, dV^T = dO^T P.  Block m is the only owner of the (t, slot)
+//    pairs that selected it, so it also writes dlogg[t][slot] (sum over G
+//    heads, 64 rows, 64 keys) directly.  The q / dout tiles are single-buffered:
+//    the next item is copied (direct-to-LDS loads) after every wave is done
+//    with the current one, and the second workgroup on the CU computes
+//    meanwhile.
 //  * dQ (query-major): the forward's tiling (2 heads x 64 rows per workgroup,
 //    four waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
 //    selected block and accumulating dQ^T += K^T dS^T, with K and V staged
-//    row-major in LDS (K^T read with ds_read_b64_tr_b16).
+//    row-major in LDS (K^T read with ds_read_b64_tr_b16), double-buffered.
+//  All tiles are laid out swizzled so that row fragments and transposed reads
+//  are both free of bank conflicts.
 // With OUTER (gates applied after the softmax, the right-hand gradient of
 // Eq. 5) the logits carry no bias, dP = g dO . v, dV takes g P, and the gate
 // gradient of a block is the sum of P dP instead of dS.
 #include <math.h>
+
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -453,36 +459,50 @@ __global__ void __launch_bounds__(256) bwd_dval_kernel(const bf16_t* __restrict_
   if (row < rows && sub == 0) Dv[row] = a;
 }
 
-// The dQ kernel's second stream and its fork / join events, per host thread and
-// device (created once, default priority).
+// The dQ kernel's second stream and its fork / join events, one set per
+// device for the whole process (created on first use, default priority, never
+// destroyed).  Callers on different threads share it: a backward holds `mu`
+// while it enqueues its fork, its two kernels and its join, so the events
+// always order the right pair of streams; the dQ kernels of concurrent
+// backwards then run one after another on the side stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   int cus = 0;
+  bool ready = false;
+  std::mutex mu;
 };
 
 SideStream* side_stream() {
   constexpr int kMaxDev = 64;
-  thread_local SideStream per_dev[kMaxDev];
+  static SideStream per_dev[kMaxDev];
+  static std::mutex create_mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
   SideStream& ss = per_dev[dev];
-  if (!ss.s) {
+  std::lock_guard<std::mutex> lk(create_mu);
+  if (!ss.ready) {
     // published only when every part exists (else the caller runs serially)
-    SideStream n;
-    if (hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int cus = 0;
+    hipEvent_t fork = nullptr, join = nullptr;
+    hipStream_t s = nullptr;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return nullptr;
-    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
-      (void)hipEventDestroy(n.fork);  // clean-up on the failure path; its own status is moot
-      return nullptr;
-    }
-    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) {
-      (void)hipEventDestroy(n.fork);
-      (void)hipEventDestroy(n.join);
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipEventDestroy(fork);  // clean-up on the failure path; its own status is moot
       return nullptr;
     }
-    ss = n;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+      (void)hipEventDestroy(fork);
+      (void)hipEventDestroy(join);
+      return nullptr;
+    }
+    ss.s = s;
+    ss.fork = fork;
+    ss.join = join;
+    ss.cus = cus;
+    ss.ready = true;
   }
   return &ss;
 }
@@ -549,6 +569,7 @@ hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const v
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(ss->mu);
   if ((e = hipEventRecord(ss->fork, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);

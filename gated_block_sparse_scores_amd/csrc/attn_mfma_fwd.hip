@@ -1,5 +1,5 @@
 // Fused gated block-sparse forward with bf16 MFMA (gfx950): head_dim 128,
-// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv a multiple of 4.
+// block 64, bf16 tensors, N a multiple of 64, G = hq / hkv even.
 //
 // picx.dev summary of SAS, 'Key Idea' Eq. 9 and 'Kernel Design': logits of
 // the selected blocks get their normalised log gate, the current block gets 0

@@ -1,7 +1,7 @@
 // gfx950 bf16 MFMA helpers (wave64).
 //
-// v_mfma_f32_32x32x16_bf16, as used here (checked by tests/test_gpu_mfma_layout
-// through the attention parity tests):
+// v_mfma_f32_32x32x16_bf16, as used here (the attention parity tests depend on
+// every part of this layout):
 //   A (32 x 16): lane l supplies row l % 32, eight k-values of k-group l / 32;
 //   B (16 x 32): lane l supplies column l % 32, the same eight k-values;
 //   D (32 x 32): lane l holds column l % 32, rows

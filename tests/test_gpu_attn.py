@@ -1,5 +1,6 @@
 """GPU parity of the fused gated block-sparse forward and backward (C ABI)."""
 import math
+import time
 
 import numpy as np
 import pytest
@@ -74,8 +75,10 @@ CASES = [
     (1, 5, 1, 257, 128, 64, 2),
     (1, 4, 4, 64, 128, 64, 1),
     (1, 2, 1, 1000, 64, 64, 64),
-    # shapes served by the bf16 MFMA kernels (G % 4 == 0, d 128, block 64, N % 64 == 0)
+    # shapes served by the bf16 MFMA kernels (G even, d 128, block 64, N % 64 == 0)
     (1, 4, 1, 64, 128, 64, 2),
+    (1, 4, 2, 384, 128, 64, 3),
+    (1, 6, 1, 256, 128, 64, 2),
     (1, 8, 2, 512, 128, 64, 3),
     (2, 8, 1, 640, 128, 64, 5),
     (1, 16, 4, 1024, 128, 64, 16),
@@ -149,13 +152,18 @@ def run_workload(wl):
     return w, x, dict(idx=idx, logg=logg, lse_s=lse_s, s=s, o=o, lse=lse, **gr)
 
 
+@pytest.mark.timeout(400)
 @pytest.mark.parametrize("wl", [2, 3])
 def test_training_workload_sampled(wl):
     """Full-size training workloads (8K tokens / 32K tokens, 32/8 heads, d 128,
-    block 64).  The oracle recomputes sampled query blocks (o, LSE, dq, dlogg,
-    ds) and sampled key blocks (dk, dv) on the device's selection, which is
-    itself checked against the oracle's Top-K of the same fp32 scores."""
+    block 64).  For every KV head the oracle recomputes sampled query blocks
+    (o, LSE, dq, dlogg, ds) and sampled key blocks (dk, dv; always including
+    the key block with that head's longest inverse list) on the device's
+    selection, which is itself checked against the oracle's Top-K of the same
+    fp32 scores.  Each sampled block is held to the tolerance on its own, and
+    the pooled errors too."""
     say(f"training workload {wl}")
+    t_start = time.perf_counter()
     w, x, r = run_workload(wl)
     T = w.nblocks
     xc = {k_: x[k_].cpu() for k_ in ("q", "k", "v", "dout")}
@@ -174,13 +182,19 @@ def test_training_workload_sampled(wl):
     assert max_abs(r["logg"].cpu().numpy(), ol) <= GATE_ATOL
     scale = O.default_scale(w.head_dim)
     rng = np.random.default_rng(wl)
-    tsamp = sorted({0, 1, T // 2, T - 1, *rng.integers(0, T, 3).tolist()})
     g = w.group
     o_gpu, lse_gpu, dq_gpu = r["o"].cpu(), r["lse"].cpu(), r["dq"].cpu()
     ds_gpu, dl_gpu = r["ds"].cpu().numpy(), r["dlogg"].cpu().numpy()
+    dk_gpu, dv_gpu = r["dk"].cpu(), r["dv"].cpu()
     errs = {"o": 0.0, "lse": 0.0}
-    dq_num = dq_den = dl_num = dl_den = ds_num = ds_den = 0.0
-    for kv in (0, w.hkv - 1):
+    blocks = {k_: [] for k_ in ("dq", "dlogg", "ds", "dk", "dv")}
+
+    def acc(name, got, ref, where):
+        blocks[name].append((float(np.sum((got - ref) ** 2)), float(np.sum(ref ** 2)), where))
+
+    nblk = nkey = 0
+    for kv in range(w.hkv):
+        tsamp = sorted({0, 1, T // 2, T - 1, *rng.integers(0, T, 2).tolist()})
         for t in tsamp:
             lo, hi = O.block_span(t, w.block, w.seqlen)
             ob, lb, _, _ = O.fwd_row_block(xc["q"], xc["k"], xc["v"], oi, ol, w.block, scale, 0,
@@ -190,30 +204,44 @@ def test_training_workload_sampled(wl):
             errs["lse"] = max(errs["lse"], max_abs(lse_gpu[0, hs, lo:hi], lb))
             dqb, dlb, _ = O.bwd_row_block(xc["q"], xc["k"], xc["v"], xc["dout"], oi, ol, w.block,
                                           scale, 0, kv, t)
-            dq_num += np.sum((np64(dq_gpu[0, hs, lo:hi]) - dqb) ** 2)
-            dq_den += np.sum(dqb ** 2)
-            dl_num += np.sum((dl_gpu[0, kv, t] - dlb) ** 2)
-            dl_den += np.sum(dlb ** 2)
+            acc("dq", np64(dq_gpu[0, hs, lo:hi]), dqb, (kv, t))
             if t > 0:
+                acc("dlogg", dl_gpu[0, kv, t], dlb, (kv, t))
                 dsr = O.ds_row(s_np[0, kv, t, :t], ols[0, kv, t], oi[0, kv, t], dlb)
-                ds_num += np.sum((ds_gpu[0, kv, t, :t] - dsr) ** 2)
-                ds_den += np.sum(dsr ** 2)
-    dk_num = dk_den = dv_num = dv_den = 0.0
-    dk_gpu, dv_gpu = r["dk"].cpu(), r["dv"].cpu()
-    for kv in (0, w.hkv - 1):
-        for m in sorted({0, T // 3, T - 2}):
+                acc("ds", ds_gpu[0, kv, t, :t], dsr, (kv, t))
+            nblk += 1
+        # key blocks: the longest inverse list of this head (the most query
+        # blocks folded into one dK / dV), the second to last block, and for
+        # the first and last head a middle block
+        counts = np.bincount(oi[0, kv][oi[0, kv] >= 0], minlength=T)
+        msamp = {int(np.argmax(counts)), T - 2}
+        if kv in (0, w.hkv - 1):
+            msamp.add(int(rng.integers(T // 3, T - 2)))
+        msamp = sorted(msamp)
+        nkey += len(msamp)
+        for m in msamp:
             dkb, dvb = O.bwd_key_block(xc["q"], xc["k"], xc["v"], xc["dout"], oi, ol, w.block,
                                        scale, 0, kv, m)
             lo, hi = O.block_span(m, w.block, w.seqlen)
-            dk_num += np.sum((np64(dk_gpu[0, kv, lo:hi]) - dkb) ** 2)
-            dk_den += np.sum(dkb ** 2)
-            dv_num += np.sum((np64(dv_gpu[0, kv, lo:hi]) - dvb) ** 2)
-            dv_den += np.sum(dvb ** 2)
-    for name, num, den in (("dq", dq_num, dq_den), ("dlogg", dl_num, dl_den),
-                           ("ds", ds_num, ds_den), ("dk", dk_num, dk_den),
-                           ("dv", dv_num, dv_den)):
-        errs[name] = math.sqrt(num / den)
-    say("  sampled errors: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+            acc("dk", np64(dk_gpu[0, kv, lo:hi]), dkb, (kv, m, int(counts[m])))
+            acc("dv", np64(dv_gpu[0, kv, lo:hi]), dvb, (kv, m, int(counts[m])))
+    # Every sampled block on its own: its error over its own norm, or over the
+    # RMS block norm of that quantity when larger (a dlogg row of one history
+    # block, or a ds row, can be a near-zero sum of cancelling terms), and the
+    # pooled relative L2 over all sampled blocks.
+    worst = {}
+    for name, rows in blocks.items():
+        rms = math.sqrt(sum(d_ for _, d_, _ in rows) / len(rows))
+        for num, den, where in rows:
+            e = math.sqrt(num) / max(math.sqrt(den), rms)
+            if e > worst.get(name, (0.0, None))[0]:
+                worst[name] = (e, where)
+            assert e <= 3e-2, f"{name} error {e:.3e} at {where}"
+        errs[name] = math.sqrt(sum(n_ for n_, _, _ in rows) / sum(d_ for _, d_, _ in rows))
+    say(f"  {nblk} query blocks and {nkey} key blocks over all {w.hkv} KV heads; "
+        "pooled errors: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+    say("  worst block: " + ", ".join(f"{k_}={e:.2e} at {wh}" for k_, (e, wh) in worst.items()))
+    say(f"  host time {time.perf_counter() - t_start:.1f} s")
     assert errs["o"] <= 2e-2 and errs["lse"] <= 2e-2
     for name in ("dq", "dlogg", "ds", "dk", "dv"):
         assert errs[name] <= 3e-2, name
