@@ -33,7 +33,8 @@ EXPORTED = [
     "sas_select_topk",
     "sas_attn_fwd_workspace_size", "sas_attn_fwd", "sas_attn_bwd_workspace_size",
     "sas_attn_bwd", "sas_decode_workspace_size", "sas_decode", "sas_decode_step_workspace_size",
-    "sas_decode_step", "sas_decode_paged", "sas_decode_step_paged", "sas_selector_bwd",
+    "sas_decode_step", "sas_decode_step_noalloc", "sas_decode_paged", "sas_decode_step_paged",
+    "sas_selector_bwd",
     "sas_profiler_enable",
     "sas_profiler_reset", "sas_profiler_read",
 ]
@@ -113,12 +114,15 @@ def lib():
     L.sas_decode_step_workspace_size.restype = C.c_size_t
     L.sas_decode_step.argtypes = [sp, C.c_int, C.c_int, P, P, C.c_int, C.c_int, P, P, C.c_int,
                                   P, P, P, P, P, P, C.c_size_t, P]
+    L.sas_decode_step_noalloc.argtypes = [sp, C.c_int, C.c_int, P, P, C.c_int, C.c_int, P, P,
+                                          C.c_int, P, P, P, P, P, P]
     L.sas_profiler_enable.argtypes = [C.c_int]
     L.sas_profiler_reset.argtypes = []
     L.sas_profiler_read.argtypes = [C.POINTER(sas_kernel_time), C.c_int]
     L.sas_profiler_read.restype = C.c_int
     for name in ("sas_block_pool", "sas_select_topk", "sas_attn_fwd", "sas_attn_bwd",
-                 "sas_decode", "sas_decode_step", "sas_decode_paged", "sas_decode_step_paged",
+                 "sas_decode", "sas_decode_step", "sas_decode_step_noalloc", "sas_decode_paged",
+                 "sas_decode_step_paged",
                  "sas_selector_bwd"):
         getattr(L, name).restype = C.c_int
     _lib = L
@@ -231,6 +235,19 @@ def sas_decode_step(shape: Shape, cache_len: int, K: int, q, kbar, kbar_dtype: i
         C.byref(shape.c()), cache_len, K, _ptr(q), _ptr(kbar), kbar_dtype, kbar_ld, _ptr(kcache),
         _ptr(vcache), 1 if gated else 0, _ptr(o), _ptr(lse), _ptr(idx), _ptr(logg), _ptr(lse_s),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# Size of the static device scratch of sas_decode_step_noalloc (include/sas.h).
+SAS_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def sas_decode_step_noalloc(shape: Shape, cache_len: int, K: int, q, kbar, kbar_dtype: int,
+                            kbar_ld: int, kcache, vcache, gated: bool, o, lse, idx, logg, lse_s,
+                            stream=None):
+    _check("sas_decode_step_noalloc", lib().sas_decode_step_noalloc(
+        C.byref(shape.c()), cache_len, K, _ptr(q), _ptr(kbar), kbar_dtype, kbar_ld, _ptr(kcache),
+        _ptr(vcache), 1 if gated else 0, _ptr(o), _ptr(lse), _ptr(idx), _ptr(logg), _ptr(lse_s),
+        _stream(stream)))
 
 
 def sas_decode_paged(shape: Shape, K: int, q, kpages, vpages, num_pages: int, block_table,

@@ -475,6 +475,61 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                           lse_s, workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of sas_decode_step_noalloc: one copy per GPU, held until the process
+// ends.  Host code never passes `scratch` itself (on the host it names a stand-in,
+// not device memory): each device's address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept in scratch_table.
+static __device__ __align__(256) unsigned char scratch[SAS_STATIC_SCRATCH_BYTES];
+
+struct ScratchTable {
+  std::mutex mu;
+  void* ptr[64] = {};
+};
+
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+
+// The current device's copy of `scratch`, or nullptr when it cannot be found.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  ScratchTable& t = scratch_table();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    t.ptr[dev] = p;
+  }
+  return t.ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+sas_status sas_decode_step_noalloc(const sas_shape* shape, int cache_len, int K, const void* q,
+                                   const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                                   const void* kcache, const void* vcache, int gated, void* o,
+                                   float* lse, int32_t* idx, float* logg, float* lse_s,
+                                   void* stream) {
+  SAS_TRY(check_shape(shape));
+  if (K <= 0 || cache_len < 0) return SAS_ERR_INVALID_ARG;
+  if (K > 64) return SAS_ERR_UNSUPPORTED;
+  // the size check is host arithmetic only: no device call before it
+  if (step_layout(shape, K).bytes > (size_t)SAS_STATIC_SCRATCH_BYTES) return SAS_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return SAS_ERR_LAUNCH;
+  return sas_decode_step(shape, cache_len, K, q, kbar, kbar_dtype, kbar_ld, kcache, vcache,
+                         gated, o, lse, idx, logg, lse_s, ws, (size_t)SAS_STATIC_SCRATCH_BYTES,
+                         stream);
+}
+
 sas_status sas_decode_paged(const sas_shape* shape, int K, const void* q, const void* kpages,
                             const void* vpages, int num_pages, const int32_t* block_table,
                             int bt_ld, const int32_t* seq_lens, const int32_t* idx,

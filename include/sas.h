@@ -272,6 +272,27 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * sas_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks and results as
+ * sas_decode_step; the candidates and decode partials live in a static
+ * SAS_STATIC_SCRATCH_BYTES device array that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up once per device).
+ * Nothing is allocated and nothing needs clearing: the step writes every
+ * scratch byte it reads.  Returns SAS_ERR_WORKSPACE, before any device call,
+ * when the step needs more scratch than that (sas_decode_step_workspace_size
+ * gives the need; e.g. batch 8 x 64K tokens, 32/8 heads, K 63: 2.3 MB).  All
+ * calls on one GPU share its array: calls that overlap on one GPU (two streams,
+ * two threads) race and must be serialised by the caller.
+ * ---------------------------------------------------------------------- */
+#define SAS_STATIC_SCRATCH_BYTES (16u << 20)
+sas_status sas_decode_step_noalloc(const sas_shape* shape, int cache_len, int K, const void* q,
+                                   const void* kbar, sas_dtype kbar_dtype, int kbar_ld,
+                                   const void* kcache, const void* vcache, int gated, void* o,
+                                   float* lse, int32_t* idx, float* logg, float* lse_s,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * Paged cache, ragged batch: the serving setting of the pages' decode
  * measurements (picx 'Decode Efficiency (Figure 7)': batch 8 at 64K, batch 1
  * up to 512K).  Sequence b has its own valid length L_b = seq_lens[b] (its new

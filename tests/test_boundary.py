@@ -178,6 +178,26 @@ def test_decode_step_checks():
     assert call(big, kbar_ld=16385, n=1 << 40) == L.SAS_ERR_UNSUPPORTED
 
 
+def test_decode_step_noalloc_rejects_more_than_its_scratch():
+    """The entry point without a workspace argument refuses, from host
+    arithmetic alone, a step needing more than its static scratch, and its
+    scratch size is the header's."""
+    text = open(os.path.join(ROOT, "include", "sas.h")).read()
+    m = re.search(r"#define SAS_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SAS_STATIC_SCRATCH_BYTES
+    lib = L.lib()
+    big = shape(batch=64, hq=32, hkv=8, seqlen=65536)     # 18 MB of candidates + partials
+    assert lib.sas_decode_step_workspace_size(C.byref(big), 63) > L.SAS_STATIC_SCRATCH_BYTES
+    args = [C.byref(big), 0, 63, FAKE, FAKE, L.SAS_DTYPE_BF16, 1023, FAKE, FAKE, 1, FAKE, FAKE,
+            None, None, None, None]
+    assert lib.sas_decode_step_noalloc(*args) == L.SAS_ERR_WORKSPACE
+    args[2] = 65                                            # K past the supported range
+    assert lib.sas_decode_step_noalloc(*args) == L.SAS_ERR_UNSUPPORTED
+    bad = shape(batch=0)
+    args[0], args[2] = C.byref(bad), 8
+    assert lib.sas_decode_step_noalloc(*args) == L.SAS_ERR_INVALID_ARG
+
+
 def test_selector_bwd_checks():
     sh = shape(seqlen=1000, hq=8, hkv=2)
     lib = L.lib()
