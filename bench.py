@@ -1,7 +1,7 @@
 """Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part all|train|decode] [--decode-workloads 4,5]
+                    [--part all|train|train32k|decode] [--decode-workloads 4,5]
     python bench.py --calibrate-copy      # plain 256 MiB device copy (counter scale)
 
 One step is one pass of the training hot path over the Qwen3-4B-shaped 8K
@@ -777,7 +777,8 @@ def main():
     ap.add_argument("--no-paged", action="store_true", help="skip the paged ragged decode")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the gate-variant, dense-scope, ragged-batch and 32K training steps")
-    ap.add_argument("--part", choices=("all", "train", "decode"), default="all")
+    ap.add_argument("--part", choices=("all", "train", "train32k", "decode"), default="all",
+                    help="train32k: only the 32K-token training workload (profiling)")
     ap.add_argument("--decode-workloads", default="4,5")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -800,6 +801,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
     }
     res = None
+    if args.part == "train32k":
+        log("32K training workload ...")
+        out["train_32k"] = bench_train_32k(args)
     if args.part in ("all", "train"):
         log("training workload ...")
         res = bench_train(args)
