@@ -115,6 +115,21 @@ __device__ __forceinline__ uint64_t bitonic_desc64(uint64_t v, int lane) {
   else return v;
 }
 
+// Sorts 64 keys, one per lane, into ascending lane order with the full
+// bitonic network: merge stages of width 2, 4, ..., 64, each a run of
+// exchanges at distances KK / 2, ..., 1 across lane pairs (the lower lane
+// keeps the smaller key when lane & KK is clear, the larger when it is set).
+template <int KK = 2, int J = 1>
+__device__ __forceinline__ uint64_t bitonic_sort_asc64(uint64_t v, int lane) {
+  const uint64_t o = ((uint64_t)xor_lane<J>((uint32_t)(v >> 32)) << 32) |
+                     xor_lane<J>((uint32_t)v);
+  const bool lower = (lane & J) == 0, up = (lane & KK) == 0 || KK == 64;
+  v = (lower == up) ? (v < o ? v : o) : (v < o ? o : v);
+  if constexpr (J > 1) return bitonic_sort_asc64<KK, J / 2>(v, lane);
+  else if constexpr (KK < 64) return bitonic_sort_asc64<KK * 2, KK>(v, lane);
+  else return v;
+}
+
 // Top K (K <= 64) of nl descending lists of K distinct nonzero keys held in
 // LDS, descending.  Two descending lists of 64 (zero-padded) meet by taking
 // the larger of a[i] and b[63 - i] lane by lane, which keeps the top 64 of the

@@ -437,8 +437,6 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   unsigned long long bal = 0;
   if constexpr (SEL) {
     extern __shared__ uint64_t lists[];  // nchunk * K keys
-    __shared__ int widx[64];
-    __shared__ float wval[64];
     const int K = dm.K, nc = sel.nchunk * K;
     const int tid = threadIdx.x, nth = 64 * kDecWaves;
     const uint64_t* crow = sel.cand + (size_t)bk * nc;
@@ -464,23 +462,24 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       if (lane == 0) lse_sh = Crow > 0 ? (float)((double)M + log(S)) : -INFINITY;
     }
     const int kk = min(K, Crow);
-    if (tid < kk) {
-      const uint64_t key = top;
-      widx[tid] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
-      wval[tid] = from_order_key((uint32_t)(key >> 32));
+    // wave 0 holds the winners by rank and re-sorts them by block index in
+    // registers (key: block index, then the score's order key)
+    uint64_t byidx = ~0ull;
+    if (wave == 0) {
+      if (lane < kk)
+        byidx = ((uint64_t)(0xFFFFFFFFu - (uint32_t)(top & 0xFFFFFFFFull)) << 32) | (top >> 32);
+      byidx = bitonic_sort_asc64(byidx, lane);
     }
-    __syncthreads();  // winners and lse_sh in LDS
+    __syncthreads();  // lse_sh in LDS
     const float lse_s = lse_sh;
-    if (tid < kk) {
-      const int mine = widx[tid];
-      int rank = 0;
-      for (int q2 = 0; q2 < kk; ++q2) rank += widx[q2] < mine;
-      sidx[rank] = mine;
-      const float lg = gate_log(wval[tid], lse_s, sel.act);
-      slg[rank] = lg;
+    if (wave == 0 && lane < kk) {
+      const int mine = (int)(byidx >> 32);
+      const float lg = gate_log(from_order_key((uint32_t)byidx), lse_s, sel.act);
+      sidx[lane] = mine;
+      slg[lane] = lg;
       if (split == 0 && sel.idx_out) {
-        sel.idx_out[(size_t)bk * K + rank] = mine;
-        sel.logg_out[(size_t)bk * K + rank] = lg;
+        sel.idx_out[(size_t)bk * K + lane] = mine;
+        sel.logg_out[(size_t)bk * K + lane] = lg;
       }
     }
     if (split == 0 && sel.idx_out) {

@@ -476,8 +476,6 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
     int row_offset, int K, int nchunk, int act, int32_t* __restrict__ idx,
     float* __restrict__ logg, float* __restrict__ lse_s, RowLens rl) {
   extern __shared__ uint64_t lists[];  // nchunk * K keys
-  __shared__ int widx[64];
-  __shared__ float wval[64];
   const size_t row = blockIdx.x;
   const int t = (int)(row % T);
   const int ct = row_history(t, row_offset, C, rl, row / T);
@@ -503,21 +501,22 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
     if (lane == 0) lse_sh = ct > 0 ? (float)((double)M + log(S)) : -INFINITY;
   }
   const int kk = min(K, ct);
-  if ((int)threadIdx.x < kk) {
-    const uint64_t key = top;
-    widx[threadIdx.x] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
-    wval[threadIdx.x] = from_order_key((uint32_t)(key >> 32));
+  // Wave 0 holds the winners by rank; it re-sorts them by block index in
+  // registers (key: block index, then the score's order key) while the last
+  // wave combines the statistics.
+  uint64_t byidx = ~0ull;
+  if (wave == 0) {
+    if (lane < kk)
+      byidx = ((uint64_t)(0xFFFFFFFFu - (uint32_t)(top & 0xFFFFFFFFull)) << 32) | (top >> 32);
+    byidx = bitonic_sort_asc64(byidx, lane);
   }
-  __syncthreads();  // winners and lse_sh in LDS
+  __syncthreads();  // lse_sh in LDS
   const float lse = lse_sh;
   int32_t* irow = idx + row * (size_t)K;
   float* lrow = logg + row * (size_t)K;
-  if ((int)threadIdx.x < kk) {
-    const int mine = widx[threadIdx.x];
-    int rank = 0;
-    for (int j = 0; j < kk; ++j) rank += widx[j] < mine;
-    irow[rank] = mine;
-    lrow[rank] = gate_log(wval[threadIdx.x], lse, act);
+  if (wave == 0 && lane < kk) {
+    irow[lane] = (int)(byidx >> 32);
+    lrow[lane] = gate_log(from_order_key((uint32_t)byidx), lse, act);
   }
   for (int p = kk + threadIdx.x; p < K; p += blockDim.x) {
     irow[p] = -1;
