@@ -11,8 +11,9 @@
 // (max, sum, unnormalised output) of every split goes to the workspace and the
 // splits of each (b, h) are merged with log-sum-exp weights.
 //  * bf16, head_dim 128, block 64 (decode_block4_kernel): four waves per
-//    workgroup (one on small grids), one or two selected blocks per wave,
-//    MFMA scores; the workgroup folds its blocks in LDS into one partial.
+//    workgroup, one or two selected blocks per wave or, on small grids, one
+//    block shared by the four waves (sixteen keys each); MFMA scores; the
+//    workgroup folds its waves' partials in LDS into one.
 //  * every other shape (decode_split_kernel): each key row is read by 16 lanes
 //    with one vector load per lane, dot products reduced with DPP row
 //    operations.
@@ -384,12 +385,11 @@ __device__ __forceinline__ float row16_max(float x) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// kDecWaves waves per workgroup (4 when there are enough workgroups to fill
-// the chip, else 1), kBpw selected blocks per wave taken one after the other
-// (2 for the paged decode and the fused steps on grids that then still fill
-// every CU twice); the workgroup folds its blocks into one partial in LDS, so
-// the merge kernel reads a fraction of the partials it would read at one block
-// per workgroup.  (Merging in the last
+// kDecWaves waves per workgroup, kBpw selected blocks per wave taken one
+// after the other (2 for the paged decode and the fused steps on grids that
+// then still fill every CU twice); the workgroup folds its blocks into one
+// partial in LDS, so the merge kernel reads a fraction of the partials it would
+// read at one block per workgroup.  (Merging in the last
 // workgroup to finish would need a device-scope fence per workgroup, which on
 // this multi-die part writes back the L2 and costs far more than the second
 // launch.)
@@ -408,14 +408,21 @@ struct SelectChunks {
   float* lse_out;    // optional [b*hkv]
 };
 
-template <int G, int kDecWaves, bool SEL, int kBpw>
+// kKW keys per wave: 64 (a whole block per wave), or 16 with the four waves
+// of a workgroup sharing one block (keys 16 w .. 16 w + 15 for wave w), which
+// puts four times as many waves on a small grid (their partials are folded in
+// LDS like those of separate blocks).
+template <int G, int kDecWaves, bool SEL, int kBpw, int kKW = 64>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     Dims dm, int Lmax, KvView kvv, int nsplit, const bf16_t* __restrict__ q,
     const int32_t* __restrict__ idx, const float* __restrict__ logg,
     float* __restrict__ part_ml, float* __restrict__ part_acc, SelectChunks sel) {
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
-  __shared__ __align__(16) uint32_t Pb[kDecWaves][BS / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
+  constexpr bool kShared = kKW < BS;          // the workgroup's waves share one block
+  static_assert(kKW == BS || (kKW * kDecWaves == BS && kBpw == 1), "block split over waves");
+  constexpr int NKT = kKW / 16;               // 16-key tiles per wave
+  __shared__ __align__(16) uint32_t Pb[kDecWaves][kKW / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
   __shared__ __align__(16) float wacc[kDecWaves * kBpw][G][D];  // one partial per block
   __shared__ float wml[kDecWaves * kBpw][G][2];
   __shared__ int sidx[64];
@@ -431,7 +438,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
 
   // Entries: [valid selected blocks (slot order)..., current block].  The
   // workgroup takes kDecWaves * kBpw consecutive entries, wave w the kBpw
-  // entries from (split * kDecWaves + w) * kBpw, one after the other.
+  // entries from (split * kDecWaves + w) * kBpw, one after the other; with
+  // kShared it takes entry `split` alone.
   int nvalid = 0;  // valid selected blocks of the row (the current block follows)
   int mm = -1;     // given idx: the row's entry `lane`
   unsigned long long bal = 0;
@@ -498,7 +506,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 #pragma unroll 1
   for (int e = 0; e < kBpw; ++e) {
-  const int j = (split * kDecWaves + wave) * kBpw + e;
+  const int j = kShared ? split : (split * kDecWaves + wave) * kBpw + e;
   int m = -1;
   float bias = 0.0f;
   if (j < nvalid) {
@@ -524,6 +532,17 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     vblk = view_block<bf16_t>(kvv, kvv.v, b, kv, dm.hkv, m, BS, D);
     if (!kblk || !vblk) m = -1;
   }
+  // kShared: this wave's keys of the block; all of them past the sequence's end
+  // (current block only) leave the wave's entry empty.
+  const int koff = kShared ? wave * kKW : 0;
+  if (kShared && m >= 0) {
+    if (m * BS + koff > L - 1) {
+      m = -1;
+    } else {
+      kblk += (size_t)koff * D;
+      vblk += (size_t)koff * D;
+    }
+  }
   // Outer gating: the logits carry no bias and the block's P V is scaled by g.
   float gain = 1.0f;
   if (dm.outer) {
@@ -536,41 +555,41 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
   if (m >= 0) {
-    const int pos0 = m * BS;
+    const int pos0 = m * BS + koff;  // position of the wave's first key
     const int last = L - 1;  // rows past it (current block only) are read clamped, then masked
 
     // Loads: K in MFMA B layout, V one row per wave instruction, q as A operand.
     // With one block per wave the V loads are issued after the score products
     // instead, into the registers K held: 30 fewer registers, and V's latency
-    // overlaps the softmax (measured: separate decode 6% faster with four waves
-    // per workgroup at 8x64K and 8% with one wave at 512K, fused step 2% at
-    // 512K).  With two blocks per wave it was slower.
+    // overlaps the softmax (measured with whole blocks per wave: separate
+    // decode 6% faster at 8x64K and 8% at 512K, fused step 2% at 512K).  With
+    // two blocks per wave it was slower.
     constexpr bool kLateV = kBpw == 1;
-    bf16x8_t kf[4][4];
-    uint32_t vr[BS];
+    bf16x8_t kf[NKT][4];
+    uint32_t vr[kKW];
     auto load_v = [&]() {
-      if (pos0 + BS <= L) {
+      if (pos0 + kKW <= L) {
         const bf16_t* vrow = vblk + 2 * lane;
 #pragma unroll
-        for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+        for (int r = 0; r < kKW; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
       } else {  // rows past L - 1 are read clamped, then masked
 #pragma unroll
-        for (int r = 0; r < BS; ++r)
+        for (int r = 0; r < kKW; ++r)
           vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
                                                      2 * lane);
       }
     };
     if constexpr (kLateV) {
-      if (pos0 + BS <= L) {
+      if (pos0 + kKW <= L) {
         const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch)
             kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
       } else {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
           const int rr = min(kt * 16 + (lane & 15), last - pos0);
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch)
@@ -579,19 +598,19 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
         }
       }
     } else {
-      if (pos0 + BS <= L) {  // full block (every history block): plain offsets
+      if (pos0 + kKW <= L) {  // full block (every history block): plain offsets
         const bf16_t* krow = kblk + (size_t)(lane & 15) * D + (lane >> 4) * 8;
         const bf16_t* vrow = vblk + 2 * lane;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch)
             kf[kt][ch] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 16 * D + ch * 32);
 #pragma unroll
-        for (int r = 0; r < BS; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
+        for (int r = 0; r < kKW; ++r) vr[r] = *reinterpret_cast<const uint32_t*>(vrow + r * D);
       } else {  // the current block: rows past L - 1 are read clamped, then masked
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
           const int rr = min(kt * 16 + (lane & 15), last - pos0);
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch)
@@ -599,7 +618,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
                                                             (lane >> 4) * 8);
         }
 #pragma unroll
-        for (int r = 0; r < BS; ++r)
+        for (int r = 0; r < kKW; ++r)
           vr[r] = *reinterpret_cast<const uint32_t*>(vblk + (size_t)min(r, last - pos0) * D +
                                                      2 * lane);
       }
@@ -615,9 +634,9 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     }
 
     // S[h][key]: lane holds key kt*16 + lane%16, heads 4*(lane/16) + r.
-    f32x4_t sacc[4];
+    f32x4_t sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
       sacc[kt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
@@ -631,7 +650,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     for (int r = 0; r < 4; ++r) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         const int pos = pos0 + kt * 16 + (lane & 15);
         const float z = pos < L ? sacc[kt][r] * dm.scale + bias : -INFINITY;
         sacc[kt][r] = z;
@@ -640,7 +659,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
       mx = row16_max(mx);
       float sm = 0.0f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         const float pz = expf(sacc[kt][r] - mx);  // exp(-inf) = 0 for masked keys
         sacc[kt][r] = pz;
         sm += pz;
@@ -653,7 +672,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     for (int r = 0; r < 4; ++r) {
       const int h = hbase + r;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         const float mine = sacc[kt][r];
         const float nb = __int_as_float(
             __builtin_amdgcn_update_dpp(0, __float_as_int(mine), 0xB1, 0xF, 0xF, true));
@@ -663,7 +682,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own P is in LDS
 #pragma unroll
-    for (int kp = 0; kp < BS / 2; ++kp) {
+    for (int kp = 0; kp < kKW / 2; ++kp) {
       const uint32_t v0 = vr[2 * kp], v1 = vr[2 * kp + 1];
       const bf16x2_t vlo =
           __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(v1, v0, 0x05040100u));
@@ -723,8 +742,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 }
 
-// bps entries per workgroup: 8 (four waves of two blocks), 4 (four waves of
-// one) or 1 (one wave).
+// bps entries per workgroup of four waves: 8 (two blocks per wave), 4 (one
+// block per wave) or 1 (one block, sixteen keys per wave).
 template <int G, bool SEL>
 void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, int bps,
                           const void* q, const int32_t* idx, const float* logg, float* part_ml,
@@ -740,9 +759,9 @@ void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, 
                        st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
                        sel);
   else
-    hipLaunchKernelGGL((decode_block4_kernel<G, 1, SEL, 1>), dim3((unsigned)wgs), dim3(64), lds,
-                       st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
-                       sel);
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 1, 16>), dim3((unsigned)wgs), dim3(256),
+                       lds, st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml,
+                       part_acc, sel);
 }
 
 // Workspace: [partials (max, sum) per (b, h, split)][partial outputs per
@@ -799,8 +818,10 @@ bool decode_two_per_wave(const Dims& dm) {
 
 int decode_blocks_per_split(const Dims& dm) {
   // MFMA path: four blocks (waves) per workgroup when that still leaves at
-  // least two workgroups per CU, else one.  The workspace is sized for this
-  // split count, which is at least that of two blocks per wave.
+  // least two workgroups per CU, else one block shared by the four waves,
+  // sixteen keys each (measured at 512K against one wave per block: split
+  // kernel 10.6 -> 8.8 us).  The workspace is sized for this split count, which
+  // is at least that of two blocks per wave.
   if (decode_mfma_path(dm))
     return (long)dm.b * dm.hkv * ((dm.K + 4) / 4) >= 512 ? 4 : 1;
   const long total = (long)dm.b * dm.hkv * (dm.K + 1);
@@ -834,11 +855,11 @@ hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, i
                               bool gated, int32_t* idx_out, float* logg_out, float* lse_s_out,
                               void* o, float* lse, void* ws, hipStream_t st) {
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
-  // Four waves per workgroup whatever the grid: every workgroup merges the
-  // row's chunk candidates first, which four waves share; two blocks per wave
-  // when the paged decode takes them too (the partial buffer of
-  // decode_workspace_bytes covers either split count).
-  const int bps = kvv.table && decode_two_per_wave(dm) ? 8 : 4;
+  // Entries split as in the separate decode: every workgroup (four waves)
+  // merges the row's chunk candidates first, then serves its entries.  One
+  // block per workgroup on small grids puts four times as many workgroups on
+  // the chip as four blocks would (measured at 512K: 16.5 -> 12.8 us).
+  const int bps = kvv.table && decode_two_per_wave(dm) ? 8 : decode_blocks_per_split(dm);
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + (size_t)dm.b * dm.hq * nsplit * 2;
