@@ -11,9 +11,10 @@
 // (max, sum, unnormalised output) of every split goes to the workspace and the
 // splits of each (b, h) are merged with log-sum-exp weights.
 //  * bf16, head_dim 128, block 64 (decode_block4_kernel): four waves per
-//    workgroup, one or two selected blocks per wave or, on small grids, one
-//    block shared by the four waves (sixteen keys each); MFMA scores; the
-//    workgroup folds its waves' partials in LDS into one.
+//    workgroup, each block shared by two waves (32 keys each) or, on small
+//    grids, by four (sixteen keys each); two whole blocks per wave in the paged
+//    decode on large grids; MFMA scores; the workgroup folds its waves'
+//    partials in LDS into one.
 //  * every other shape (decode_split_kernel): each key row is read by 16 lanes
 //    with one vector load per lane, dot products reduced with DPP row
 //    operations.
@@ -408,10 +409,10 @@ struct SelectChunks {
   float* lse_out;    // optional [b*hkv]
 };
 
-// kKW keys per wave: 64 (a whole block per wave), or 16 with the four waves
-// of a workgroup sharing one block (keys 16 w .. 16 w + 15 for wave w), which
-// puts four times as many waves on a small grid (their partials are folded in
-// LDS like those of separate blocks).
+// kKW keys per wave: 64 (a whole block per wave), or fewer with 64 / kKW
+// waves of a workgroup sharing one block (wave w takes keys
+// (w % (64 / kKW)) kKW .. + kKW - 1), which puts more waves on a small grid
+// (their partials are folded in LDS like those of separate blocks).
 template <int G, int kDecWaves, bool SEL, int kBpw, int kKW = 64>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     Dims dm, int Lmax, KvView kvv, int nsplit, const bf16_t* __restrict__ q,
@@ -419,8 +420,9 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
     float* __restrict__ part_ml, float* __restrict__ part_acc, SelectChunks sel) {
   constexpr int D = 128, BS = 64;
   constexpr int GP = G <= 4 ? 4 : 8;          // heads per LDS row (padded)
-  constexpr bool kShared = kKW < BS;          // the workgroup's waves share one block
-  static_assert(kKW == BS || (kKW * kDecWaves == BS && kBpw == 1), "block split over waves");
+  constexpr bool kShared = kKW < BS;          // waves share blocks
+  constexpr int WPB = BS / kKW;                // waves per block
+  static_assert(kKW == BS || (kDecWaves % WPB == 0 && kBpw == 1), "block split over waves");
   constexpr int NKT = kKW / 16;               // 16-key tiles per wave
   __shared__ __align__(16) uint32_t Pb[kDecWaves][kKW / 2][GP];  // bf16 pairs (keys 2i, 2i+1)
   __shared__ __align__(16) float wacc[kDecWaves * kBpw][G][D];  // one partial per block
@@ -439,7 +441,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   // Entries: [valid selected blocks (slot order)..., current block].  The
   // workgroup takes kDecWaves * kBpw consecutive entries, wave w the kBpw
   // entries from (split * kDecWaves + w) * kBpw, one after the other; with
-  // kShared it takes entry `split` alone.
+  // kShared wave w takes entry split * kDecWaves / WPB + w / WPB.
   int nvalid = 0;  // valid selected blocks of the row (the current block follows)
   int mm = -1;     // given idx: the row's entry `lane`
   unsigned long long bal = 0;
@@ -506,7 +508,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 #pragma unroll 1
   for (int e = 0; e < kBpw; ++e) {
-  const int j = kShared ? split : (split * kDecWaves + wave) * kBpw + e;
+  const int j =
+      kShared ? (split * kDecWaves + wave) / WPB : (split * kDecWaves + wave) * kBpw + e;
   int m = -1;
   float bias = 0.0f;
   if (j < nvalid) {
@@ -534,7 +537,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
   // kShared: this wave's keys of the block; all of them past the sequence's end
   // (current block only) leave the wave's entry empty.
-  const int koff = kShared ? wave * kKW : 0;
+  const int koff = kShared ? (wave % WPB) * kKW : 0;
   if (kShared && m >= 0) {
     if (m * BS + koff > L - 1) {
       m = -1;
@@ -742,8 +745,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_block4_kernel(
   }
 }
 
-// bps entries per workgroup of four waves: 8 (two blocks per wave), 4 (one
-// block per wave) or 1 (one block, sixteen keys per wave).
+// bps entries per workgroup of four waves: 8 (two blocks per wave), 2 (two
+// blocks, 32 keys per wave) or 1 (one block, sixteen keys per wave).
 template <int G, bool SEL>
 void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, int bps,
                           const void* q, const int32_t* idx, const float* logg, float* part_ml,
@@ -754,10 +757,10 @@ void launch_decode_block4(const Dims& dm, int L, const KvView& kvv, int nsplit, 
     hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 2>), dim3((unsigned)wgs), dim3(256), lds,
                        st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
                        sel);
-  else if (bps == 4)
-    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 1>), dim3((unsigned)wgs), dim3(256), lds,
-                       st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml, part_acc,
-                       sel);
+  else if (bps == 2)
+    hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 1, 32>), dim3((unsigned)wgs), dim3(256),
+                       lds, st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml,
+                       part_acc, sel);
   else
     hipLaunchKernelGGL((decode_block4_kernel<G, 4, SEL, 1, 16>), dim3((unsigned)wgs), dim3(256),
                        lds, st, dm, L, kvv, nsplit, (const bf16_t*)q, idx, logg, part_ml,
@@ -809,21 +812,23 @@ bool decode_mfma_path(const Dims& dm) { return dm.bf16 && dm.d == 128 && dm.bs =
 // Four waves of two blocks each per workgroup (MFMA path): when that still
 // fills every CU with two workgroups, the grid runs in one round, each wave's
 // second block loading after its first is folded.  Measured faster for the
-// paged decode and the paged fused step; the dense separate decode and the
-// dense fused step keep one block per wave, whose V loads wait until after
-// the score products (faster for them).
+// paged decode and the paged fused step (measured against one block per wave);
+// the dense separate decode and the dense fused step share each block between
+// two waves, whose V loads wait until after the score products.
 bool decode_two_per_wave(const Dims& dm) {
   return decode_mfma_path(dm) && (long)dm.b * dm.hkv * ((dm.K + 8) / 8) >= 512;
 }
 
 int decode_blocks_per_split(const Dims& dm) {
-  // MFMA path: four blocks (waves) per workgroup when that still leaves at
-  // least two workgroups per CU, else one block shared by the four waves,
-  // sixteen keys each (measured at 512K against one wave per block: split
-  // kernel 10.6 -> 8.8 us).  The workspace is sized for this split count, which
-  // is at least that of two blocks per wave.
+  // MFMA path, four waves per workgroup: two blocks, 32 keys per wave, when
+  // four blocks per workgroup would still leave two workgroups per CU, else one
+  // block of sixteen keys per wave (measured against one block per wave: split
+  // kernel 33.5 -> 31.9 us at 8x64K, 10.6 -> 8.8 us at 512K; sixteen keys per
+  // wave at 8x64K shortened the split kernel less than the 64 splits lengthened
+  // the merge).  The workspace is sized for this split count, which is at least
+  // that of two blocks per wave.
   if (decode_mfma_path(dm))
-    return (long)dm.b * dm.hkv * ((dm.K + 4) / 4) >= 512 ? 4 : 1;
+    return (long)dm.b * dm.hkv * ((dm.K + 4) / 4) >= 512 ? 2 : 1;
   const long total = (long)dm.b * dm.hkv * (dm.K + 1);
   return total >= 2048 ? 2 : 1;
 }
@@ -856,9 +861,10 @@ hipError_t launch_decode_step(const Dims& dm, int L, const KvView& kvv, int C, i
                               void* o, float* lse, void* ws, hipStream_t st) {
   if (!decode_mfma_path(dm)) return hipErrorInvalidValue;
   // Entries split as in the separate decode: every workgroup (four waves)
-  // merges the row's chunk candidates first, then serves its entries.  One
-  // block per workgroup on small grids puts four times as many workgroups on
-  // the chip as four blocks would (measured at 512K: 16.5 -> 12.8 us).
+  // merges the row's chunk candidates first, then serves its entries.  Two
+  // waves per block, or four on small grids, put two or four times as many
+  // workgroups on the chip as one wave per block (measured: fused split kernel
+  // 36.2 -> 34.6 us at 8x64K, 16.5 -> 12.8 us at 512K).
   const int bps = kvv.table && decode_two_per_wave(dm) ? 8 : decode_blocks_per_split(dm);
   const int nsplit = (dm.K + 1 + bps - 1) / bps;
   float* part_ml = (float*)ws;

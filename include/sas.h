@@ -281,7 +281,7 @@ sas_status sas_decode_step(const sas_shape* shape, int cache_len, int K, const v
  * Nothing is allocated and nothing needs clearing: the step writes every
  * scratch byte it reads.  Returns SAS_ERR_WORKSPACE, before any device call,
  * when the step needs more scratch than that (sas_decode_step_workspace_size
- * gives the need; e.g. batch 8 x 64K tokens, 32/8 heads, K 63: 2.3 MB).  All
+ * gives the need; e.g. batch 8 x 64K tokens, 32/8 heads, K 63: 4.4 MB).  All
  * calls on one GPU share its array: calls that overlap on one GPU (two streams,
  * two threads) race and must be serialised by the caller.
  * ---------------------------------------------------------------------- */
