@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--part all|train|train32k|decode] [--decode-workloads 4,5]
     python bench.py --calibrate-copy      # plain 256 MiB device copy (counter scale)
+    python bench.py --stream-floor        # read floor of cold streams at the decode's sizes
 
 One step is one pass of the training hot path over the Qwen3-4B-shaped 8K
 workload (batch 1, 8192 tokens, 32 query / 8 KV heads, head_dim 128, bf16,
@@ -188,6 +189,32 @@ def recorded_traffic(name, workload):
         return int(float(rec["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def stream_floor():
+    """Runs the stand-alone stream probe (built next to libsas.so): a plain
+    read kernel over buffers rotated through 1 GiB, at the decode's stream
+    sizes, over grids of 256..4096 workgroups; prints its lines and the best
+    rate per size.  Returns the probe's exit status."""
+    import subprocess
+    probe = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "gated_block_sparse_scores_amd", "stream_probe")
+    if not os.path.exists(probe):
+        print("stream_probe is not built (python -m gated_block_sparse_scores_amd.build)",
+              file=sys.stderr)
+        return 1
+    res = subprocess.run([probe], capture_output=True, text=True, timeout=300)
+    sys.stdout.write(res.stdout)
+    sys.stderr.write(res.stderr)
+    if res.returncode != 0:
+        return res.returncode
+    best = {}
+    for line in res.stdout.splitlines():
+        r = json.loads(line)
+        if r["bytes"] not in best or r["us_per_launch"] < best[r["bytes"]]["us_per_launch"]:
+            best[r["bytes"]] = r
+    print(json.dumps({"stream_floor": [best[b] for b in sorted(best)]}), flush=True)
+    return 0
 
 
 def calibrate_copy(n_bytes=256 << 20, reps=5):
@@ -781,11 +808,15 @@ def main():
                     help="train32k: only the 32K-token training workload (profiling)")
     ap.add_argument("--decode-workloads", default="4,5")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--stream-floor", action="store_true",
+                    help="run the HBM stream probe (a child process) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the path is single-GPU by design "
               "(sharding across GPUs is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.stream_floor:  # before this process touches the GPU
+        sys.exit(stream_floor())
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

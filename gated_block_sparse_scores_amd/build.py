@@ -1,4 +1,5 @@
-"""Builds libsas.so (HIP, gfx950) in-tree, next to this file.
+"""Builds libsas.so (HIP, gfx950) in-tree, next to this file, and the
+stand-alone HBM stream probe that bench.py --stream-floor runs.
 
     python -m gated_block_sparse_scores_amd.build     # or build() from Python
 
@@ -17,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsas.so")
+PROBE = os.path.join(HERE, "stream_probe")  # measurement only, not linked into the library
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = [
@@ -69,8 +71,14 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"linking libsas.so failed:\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)
+    cmd = [_hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, "stream_probe.hip"), "-o",
+           PROBE + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"building stream_probe failed:\n{res.stdout}{res.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
 
 

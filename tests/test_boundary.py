@@ -27,6 +27,14 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
 
 
+def test_stream_probe_is_built_beside_the_library():
+    # bench.py --stream-floor runs it; it is a separate program, not in libsas.so
+    probe = os.path.join(os.path.dirname(L.LIB_PATH), "stream_probe")
+    assert os.path.isfile(probe) and os.access(probe, os.X_OK)
+    lib = C.CDLL(L.LIB_PATH)
+    assert not hasattr(lib, "read_kernel")
+
+
 def test_version_and_status_strings():
     assert L.sas_version() >= 100
     assert L.status_string(L.SAS_OK) == "ok"
