@@ -40,7 +40,11 @@ CASES = [
     (2, 8, 1, 64, 128, 64, 3),      # no history: current block only
     (1, 16, 2, 3000, 128, 32, 64),
     (4, 32, 8, 2049, 128, 64, 8),
-    (8, 16, 8, 1500, 128, 64, 63),  # four blocks per workgroup; C = 23 < K: empty waves
+    (8, 16, 8, 1500, 128, 64, 63),  # two blocks per workgroup; C = 23 < K: empty waves;
+                                    # current block of 28 keys: its second wave is empty
+    (8, 16, 8, 1520, 128, 64, 63),  # current block of 48 keys: its second wave has 16
+    (1, 8, 2, 660, 128, 64, 7),     # one block per workgroup, current block of 20 keys:
+                                    # the second wave has 4, the last two none
 ]
 
 

@@ -82,6 +82,7 @@ STEP_CASES = [
     (2, 8, 2, 1000, 128, 64, 5, torch.bfloat16),        # fused, one chunk
     (1, 8, 8, 64, 128, 64, 4, torch.bfloat16),          # C = 0: current block only
     (8, 16, 8, 1500, 128, 64, 63, torch.bfloat16),      # C = 23 < K
+    (8, 16, 8, 1520, 128, 64, 63, torch.bfloat16),      # 32 keys per wave, current block of 48
     (3, 5, 1, 4097, 128, 64, 64, torch.bfloat16),       # C = K = 64
     (2, 16, 2, 64 * 700 + 5, 128, 64, 31, torch.bfloat16),   # 3 chunks (odd), ragged tail
     (1, 40, 8, 64 * 2300 + 1, 128, 64, 31, torch.bfloat16),  # 9 chunks, G = 5
