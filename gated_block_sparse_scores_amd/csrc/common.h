@@ -130,6 +130,32 @@ __device__ __forceinline__ uint64_t bitonic_sort_asc64(uint64_t v, int lane) {
   else return v;
 }
 
+// Copies n 8-byte keys from global memory to LDS with all of a thread's loads
+// (up to PER per pass) issued before its first store, so a pass costs one
+// memory round trip instead of one per key; at most one key per thread is
+// copied directly (measured: the unrolled pass was slower there).
+template <int PER>
+__device__ __forceinline__ void copy_keys_to_lds(uint64_t* dst, const uint64_t* __restrict__ src,
+                                                 int n, int tid, int nth) {
+  if (n <= nth) {
+    if (tid < n) dst[tid] = src[tid];
+    return;
+  }
+  for (int base = 0; base < n; base += PER * nth) {
+    uint64_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + tid + u * nth;
+      v[u] = i < n ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + tid + u * nth;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 // Top K (K <= 64) of nl descending lists of K distinct nonzero keys held in
 // LDS, descending.  Two descending lists of 64 (zero-padded) meet by taking
 // the larger of a[i] and b[63 - i] lane by lane, which keeps the top 64 of the

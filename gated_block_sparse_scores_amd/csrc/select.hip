@@ -481,7 +481,7 @@ __global__ void __launch_bounds__(256) select_merge_kernel(
   const int ct = row_history(t, row_offset, C, rl, row / T);
   const int nc = nchunk * K;
   const uint64_t* crow = cand + row * (size_t)nc;
-  for (int i = threadIdx.x; i < nc; i += blockDim.x) lists[i] = crow[i];
+  copy_keys_to_lds<16>(lists, crow, nc, (int)threadIdx.x, (int)blockDim.x);
   // The chunks' (max, sum of exp) are combined by the last wave (nchunk <= 64,
   // lane i holds chunk i) while wave 0 folds the waves' lists: fp32 max, fp64
   // sum of the chunk sums rescaled to it, one fp32 rounding of max + log(sum).
