@@ -18,6 +18,10 @@ K/V bytes: each decode call takes a fresh query and the calls rotate over
 distinct per-layer K/V caches, so the selected blocks come from HBM rather than
 from the last-level cache.  Prints one JSON line.
 
+`ceilings` holds what the chip reaches on plain work in the same run (a large
+bf16 GEMM through the vendor BLAS, a 1 GiB device copy); each roofline's
+`frac_of_practical` divides its achieved rate by the matching ceiling.
+
 `roofline.traffic` is the HBM bytes per launch of the dominant kernel from the
 committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, scaled by the
 plain-copy calibration recorded there; it is null when that kernel's sources
@@ -215,6 +219,47 @@ def stream_floor():
             best[r["bytes"]] = r
     print(json.dumps({"stream_floor": [best[b] for b in sorted(best)]}), flush=True)
     return 0
+
+
+def practical_ceilings(n=16384, copy_bytes=1 << 30, reps=8):
+    """What the chip reaches on plain work in this run, beside the published
+    peaks: a large bf16 GEMM through the vendor BLAS (torch.matmul, n x n x n,
+    contiguous operands; the first products of a cold GPU run slower, so six
+    untimed ones come first) and a device copy of 1 GiB (read + write bytes)."""
+    import torch
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(6):
+        c = torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    x = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    del x, y
+    torch.cuda.empty_cache()
+    tflops = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
+    gbps = 2.0 * copy_bytes / (copy_ms * 1e-3) / 1e9
+    return {"bf16_gemm": {"n": n, "ms": round(gemm_ms, 4), "TFLOPs": round(tflops, 1),
+                          "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+            "device_copy": {"bytes": copy_bytes, "ms": round(copy_ms, 4), "GBps": round(gbps, 1),
+                            "frac_of_peak": round(gbps / PEAK_HBM_GBS, 4)}}
 
 
 def calibrate_copy(n_bytes=256 << 20, reps=5):
@@ -836,6 +881,8 @@ def main():
         log("32K training workload ...")
         out["train_32k"] = bench_train_32k(args)
     if args.part in ("all", "train"):
+        log("practical ceilings ...")
+        out["ceilings"] = practical_ceilings()
         log("training workload ...")
         res = bench_train(args)
         out.update({
@@ -848,7 +895,8 @@ def main():
             "selected_pairs": int(res["pairs"]),
             "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
             "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "roofline": res["roofline"],
+            "roofline": dict(res["roofline"], frac_of_practical=round(
+                res["roofline"]["achieved"] / out["ceilings"]["bf16_gemm"]["TFLOPs"], 4)),
             "kernel_rooflines": res["kernel_rooflines"],
             "kernels": res["kernels"],
             "kernels_alone": res["kernels_alone"],
@@ -864,6 +912,10 @@ def main():
         out["decode"] = [bench_decode(int(wl), steps=steps.get(int(wl), 10),
                                       cpu=int(wl) == 4 and not args.no_cpu_baseline)
                          for wl in args.decode_workloads.split(",") if wl]
+        if "ceilings" in out:
+            for dec in out["decode"]:
+                dec["roofline"]["frac_of_practical"] = round(
+                    dec["roofline"]["achieved"] / out["ceilings"]["device_copy"]["GBps"], 4)
         if not args.no_paged:
             log("paged ragged decode ...")
             out["decode_paged"] = bench_decode_paged()
