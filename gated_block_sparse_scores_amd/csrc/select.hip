@@ -153,153 +153,159 @@ template <> struct Slice8<float> {
 };
 
 // ---------------------------------------------------------------- gate LSE + Top-K
-// One 256-thread workgroup per row.  With STANDIN the row's scores are formed
-// first: s[m] = fp32((qbar . kbar[m]) * scale), the dot product in fp64 with 16
-// lanes per key-block summary (8 consecutive dims each, reduced with DPP),
-// kept in LDS and written to s_out (0 past the row's history).  The valid
-// scores are then held in LDS as order-preserving uint32 keys.  A 4-pass
-// MSB-first radix select (8 bits per pass) finds the K-th largest key v and
-// how many keys equal to v are still needed; those are taken in ascending
-// block order, which realises the "equal score -> lower block index" rule.
-// The selection is then compacted in ascending block order with two
-// workgroup scans.
-template <typename Tk, bool STANDIN>
-__global__ void __launch_bounds__(256) topk_kernel(
-    const float* __restrict__ s, const float* __restrict__ qbar, const Tk* __restrict__ kbar,
-    int kbar_ld, int d, double scale, float* __restrict__ s_out, int T, int C, int row_offset,
-    int K, int act, int32_t* __restrict__ idx, float* __restrict__ logg,
-    float* __restrict__ lse_s, RowLens rl) {
-  extern __shared__ uint32_t keys[];  // C keys (then, with STANDIN, C scores)
-  __shared__ int hist[256];
-  __shared__ int iscr[16];
-  __shared__ float fscr[16];
-  __shared__ double dscr[16];
-  __shared__ uint32_t sh_prefix;
-  __shared__ int sh_rem;
-
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const size_t row = blockIdx.x;
-  const int t = (int)(row % T);
-  const int ct = row_history(t, row_offset, C, rl, row / T);
-  const float* srow = s + row * (size_t)C;
-  if constexpr (STANDIN) {
-    float* sv = reinterpret_cast<float*>(keys + C);
-    const int sub = tid & 15, grp = tid >> 4;
-    const bool lane_on = sub * 8 < d;
-    double qv[8];
-    {
-      const float* qrow = qbar + row * (size_t)d + (lane_on ? sub * 8 : 0);
+// Rows of at most kLongHistory history blocks.  One wave selects a row: lane
+// l holds blocks l ch .. l ch + ch - 1 (ch = ceil(C_t / 64) <= 8) in
+// registers, as order-preserving uint32 keys.  The gate LSE takes wave
+// reductions; the K-th largest key v is found bit by bit from the top, each
+// step counting the keys at or above the candidate with ballots; keys above v
+// and the first (K - #above) keys equal to v in ascending block order (the
+// "equal score -> lower block index" rule) are written in ascending block
+// order from wave prefix sums.  No workgroup barrier.
+__device__ __forceinline__ void wave_select_row(const float* src, int ct, int K, int act,
+                                                int32_t* __restrict__ irow,
+                                                float* __restrict__ lrow, float* lse_out) {
+  constexpr int PER = kLongHistory / 64;
+  const int lane = threadIdx.x & 63;
+  const int ch = (ct + 63) >> 6;
+  const int mb = lane * ch;
+  float f[PER];
+  uint32_t key[PER];
+  float mxl = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = (double)qrow[e];
+  for (int i = 0; i < PER; ++i) {
+    const bool ok = i < ch && mb + i < ct;
+    f[i] = ok ? src[mb + i] : 0.0f;
+    key[i] = ok ? order_key(f[i]) : 0u;  // every valid key is above 0
+    if (ok) mxl = fmaxf(mxl, f[i]);
+  }
+  const float mx = wave_max(mxl);
+  double sl = 0.0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (i < ch && mb + i < ct) sl += (double)expf(f[i] - mx);
+  const double sum = wave_sum_d(sl);
+  const float lse = ct > 0 ? (float)((double)mx + log(sum)) : -INFINITY;
+
+  const int kk = min(K, ct);
+  const bool all = ct <= K;
+  uint32_t thr = 0u;
+  int take_eq = 0;
+  if (!all) {
+    // the largest thr with at least K keys >= thr is the K-th largest key
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= K) thr = cand;
     }
-    const Tk* kb = kbar + (row / T) * (size_t)kbar_ld * d + (lane_on ? sub * 8 : 0);
-    float* orow = s_out + row * (size_t)C;
-#pragma unroll 4
-    for (int m = grp; m < C; m += 16) {
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gt += __popcll(__ballot(key[i] > thr));
+    take_eq = K - gt;
+  }
+  int eq_cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) eq_cnt += (!all && key[i] == thr) ? 1 : 0;
+  const int eq_before = wave_incl_scan(eq_cnt) - eq_cnt;
+  bool sel[PER];
+  int sel_cnt = 0;
+  {
+    int e = eq_before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool ok = i < ch && mb + i < ct;
+      const bool eq = !all && key[i] == thr;
+      sel[i] = ok && (all || key[i] > thr || (eq && e < take_eq));
+      e += eq ? 1 : 0;
+      sel_cnt += sel[i] ? 1 : 0;
+    }
+  }
+  const int pos0 = wave_incl_scan(sel_cnt) - sel_cnt;
+  {
+    int pos = pos0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (sel[i]) {
+        irow[pos] = mb + i;
+        lrow[pos] = gate_log(f[i], lse, act);
+        ++pos;
+      }
+  }
+  for (int p = kk + lane; p < K; p += 64) {
+    irow[p] = -1;
+    lrow[p] = 0.0f;
+  }
+  if (lane == 0) *lse_out = lse;
+}
+
+// Given scores: one wave per row, four rows per workgroup.
+__global__ void __launch_bounds__(256) topk_given_kernel(const float* __restrict__ s,
+                                                         size_t rows, int T, int C,
+                                                         int row_offset, int K, int act,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ logg,
+                                                         float* __restrict__ lse_s, RowLens rl) {
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // the whole wave
+  const int ct = row_history((int)(row % T), row_offset, C, rl, row / T);
+  wave_select_row(s + row * (size_t)C, ct, K, act, idx + row * (size_t)K, logg + row * (size_t)K,
+                  lse_s + row);
+}
+
+// Stand-in scores: one 256-thread workgroup per row forms
+// s[m] = fp32((qbar . kbar[m]) * scale), the dot product in fp64 with 16 lanes
+// per key-block summary (8 consecutive dims each, reduced with DPP), into LDS
+// and s_out (0 past the row's history); then wave 0 selects.
+template <typename Tk>
+__global__ void __launch_bounds__(256) topk_standin_kernel(
+    const float* __restrict__ qbar, const Tk* __restrict__ kbar, int kbar_ld, int d,
+    double scale, float* __restrict__ s_out, int T, int C, int row_offset, int K, int act,
+    int32_t* __restrict__ idx, float* __restrict__ logg, float* __restrict__ lse_s,
+    RowLens rl) {
+  __shared__ float sv[kLongHistory];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const int ct = row_history((int)(row % T), row_offset, C, rl, row / T);
+  const int sub = tid & 15, grp = tid >> 4;
+  const bool lane_on = sub * 8 < d;
+  double qv[8];
+  {
+    const float* qrow = qbar + row * (size_t)d + (lane_on ? sub * 8 : 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = (double)qrow[e];
+  }
+  const Tk* kb = kbar + (row / T) * (size_t)kbar_ld * d + (lane_on ? sub * 8 : 0);
+  float* orow = s_out + row * (size_t)C;
+  // sixteen blocks per round (one per 16-lane group), the loads of four rounds
+  // issued before their products (the DPP reductions keep the compiler from
+  // unrolling a loop with a run-time trip count itself)
+  for (int m0 = 0; m0 < C; m0 += 64) {
+    Slice8<Tk> ks[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + 16 * u + grp;
+      if (m < ct && lane_on) ks[u].load(kb + (size_t)m * d);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + 16 * u + grp;
       double acc = 0.0;
       if (m < ct && lane_on) {
-        Slice8<Tk> ks;
-        ks.load(kb + (size_t)m * d);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += qv[e] * ks.get(e);
+        for (int e = 0; e < 8; ++e) acc += qv[e] * ks[u].get(e);
       }
       acc = row16_sum_d(acc);
       const float v = m < ct ? (float)(acc * scale) : 0.0f;
-      if (sub == 0) {
+      if (sub == 0 && m < C) {
         sv[m] = v;
         orow[m] = v;
       }
     }
-    __syncthreads();
-    srow = sv;
   }
-
-  float mx = -INFINITY;
-  for (int m = tid; m < ct; m += nth) {
-    const float f = srow[m];
-    keys[m] = order_key(f);
-    mx = fmaxf(mx, f);
-  }
-  mx = block_max(mx, fscr);  // barriers inside; keys[] visible afterwards
-  double sum = 0.0;
-  for (int m = tid; m < ct; m += nth) sum += (double)expf(srow[m] - mx);
-  sum = block_sum_d(sum, dscr);
-  const float lse = ct > 0 ? (float)((double)mx + log(sum)) : -INFINITY;
-
-  const int kk = min(K, ct);
-  uint32_t thr = 0u;
-  int take_eq = 0;
-  const bool all = ct <= K;
-  if (!all) {
-    uint32_t prefix = 0u, mask = 0u;
-    int rem = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int m = tid; m < ct; m += nth) {
-        const uint32_t key = keys[m];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      // bin = 255 - tid; "above" = number of candidates in bins > bin.
-      const int bin = 255 - tid;
-      const int cnt = hist[bin];
-      int total;
-      const int above = block_excl_scan(cnt, iscr, &total);
-      if (above < rem && rem <= above + cnt) {
-        sh_prefix = prefix | ((uint32_t)bin << shift);
-        sh_rem = rem - above;
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      rem = sh_rem;
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-    thr = prefix;
-    take_eq = rem;
-  }
-
-  // Contiguous chunk of block indices per thread, so scans follow index order.
-  const int chunk = (ct + nth - 1) / nth;
-  const int mb = min(tid * chunk, ct), me = min(mb + chunk, ct);
-  int eq_cnt = 0;
-  if (!all)
-    for (int m = mb; m < me; ++m) eq_cnt += keys[m] == thr;
-  int dummy;
-  const int eq_before = block_excl_scan(eq_cnt, iscr, &dummy);
-  int sel_cnt = 0;
-  {
-    int e = eq_before;
-    for (int m = mb; m < me; ++m) {
-      const uint32_t key = keys[m];
-      const bool eq = key == thr;
-      sel_cnt += all || key > thr || (eq && e < take_eq);
-      e += eq;
-    }
-  }
-  const int pos0 = block_excl_scan(sel_cnt, iscr, &dummy);
-  int32_t* irow = idx + row * (size_t)K;
-  float* lrow = logg + row * (size_t)K;
-  {
-    int e = eq_before, pos = pos0;
-    for (int m = mb; m < me; ++m) {
-      const uint32_t key = keys[m];
-      const bool eq = key == thr;
-      const bool sel = all || key > thr || (eq && e < take_eq);
-      e += eq;
-      if (sel) {
-        irow[pos] = m;
-        lrow[pos] = gate_log(srow[m], lse, act);
-        ++pos;
-      }
-    }
-  }
-  for (int p = kk + tid; p < K; p += nth) {
-    irow[p] = -1;
-    lrow[p] = 0.0f;
-  }
-  if (tid == 0) lse_s[row] = lse;
+  __syncthreads();
+  if (tid < 64)
+    wave_select_row(sv, ct, K, act, idx + row * (size_t)K, logg + row * (size_t)K, lse_s + row);
 }
 
 // ---------------------------------------------------------------- long histories: two stages
@@ -590,20 +596,18 @@ hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool
                        int row_offset, int K, int act, int32_t* idx, float* logg,
                        float* lse_s, hipStream_t st, const RowLens& rl) {
   const size_t rows = (size_t)rows_bk * T;
-  const size_t lds = (size_t)(C > 0 ? C : 1) * sizeof(uint32_t) * (s ? 1 : 2);
   ProfScope ps("topk", st);
   if (s)
-    hipLaunchKernelGGL((topk_kernel<float, false>), dim3((unsigned)rows), dim3(256), lds, st, s,
-                       nullptr, nullptr, 0, 0, 0.0, nullptr, T, C, row_offset, K, act, idx, logg,
-                       lse_s, rl);
+    hipLaunchKernelGGL(topk_given_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, s,
+                       rows, T, C, row_offset, K, act, idx, logg, lse_s, rl);
   else if (kbar_bf16)
-    hipLaunchKernelGGL((topk_kernel<bf16_t, true>), dim3((unsigned)rows), dim3(256), lds, st,
-                       nullptr, qbar, (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, act, idx, logg, lse_s, rl);
+    hipLaunchKernelGGL(topk_standin_kernel<bf16_t>, dim3((unsigned)rows), dim3(256), 0, st, qbar,
+                       (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C, row_offset, K, act,
+                       idx, logg, lse_s, rl);
   else
-    hipLaunchKernelGGL((topk_kernel<float, true>), dim3((unsigned)rows), dim3(256), lds, st,
-                       nullptr, qbar, (const float*)kbar, kbar_ld, d, scale, s_out, T, C,
-                       row_offset, K, act, idx, logg, lse_s, rl);
+    hipLaunchKernelGGL(topk_standin_kernel<float>, dim3((unsigned)rows), dim3(256), 0, st, qbar,
+                       (const float*)kbar, kbar_ld, d, scale, s_out, T, C, row_offset, K, act,
+                       idx, logg, lse_s, rl);
   return hipGetLastError();
 }
 
