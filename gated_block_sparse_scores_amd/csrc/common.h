@@ -206,11 +206,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // Inclusive prefix sum across a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -241,30 +236,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) 
   __syncthreads();
   *total = tot;
   return base + incl - v;
-}
-
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  v = wave_max(v);
-  if (lane == 0) scratch[wid] = v;
-  __syncthreads();
-  float r = scratch[0];
-  for (int w = 1; w < nw; ++w) r = fmaxf(r, scratch[w]);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ double block_sum_d(double v, double* scratch) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  v = wave_sum_d(v);
-  if (lane == 0) scratch[wid] = v;
-  __syncthreads();
-  double r = 0.0;
-  for (int w = 0; w < nw; ++w) r += scratch[w];
-  __syncthreads();
-  return r;
 }
 
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
