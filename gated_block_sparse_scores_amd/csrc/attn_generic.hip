@@ -251,8 +251,16 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(const T* __restrict__ o,
 }
 
 // Inverse selection map: slot[b, kv][m][t] = the Top-K slot of block m in
-// the selection of query block t (0xFF when t did not select m).  Cleared and
-// then marked from idx; the key-major kernels read the row of their key block.
+// the selection of query block t (0xFF when t did not select m); the
+// key-major kernels read the row of their key block.  One workgroup per
+// (b, kv) and kSlotRows rows m: it reads every selection row of (b, kv) (the
+// loads of eight passes issued together), marks its kSlotRows x T tile in LDS
+// over a 0xFF fill, then writes the tile, which is contiguous in the map, once.
+// For T > kSlotMaxT (tiles past 64 KB of LDS) the map is cleared, then marked
+// entry by entry.
+constexpr int kSlotRows = 16;
+constexpr int kSlotMaxT = 4096;
+
 __global__ void __launch_bounds__(256) slotmap_clear_kernel(uint4* __restrict__ sm, size_t n16) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n16) sm[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
@@ -263,11 +271,52 @@ __global__ void __launch_bounds__(256) slotmap_mark_kernel(const int32_t* __rest
                                                            uint8_t* __restrict__ sm) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= entries) return;
-  const size_t row = i / K;          // (bk, t)
+  const size_t row = i / K;  // (bk, t)
   const int t = (int)(row % T);
   const size_t bk = row / T;
   const int m = idx[i];
   if (m >= 0 && m < t) sm[(bk * T + m) * (size_t)T + t] = (uint8_t)(i % K);
+}
+
+__global__ void __launch_bounds__(256) slotmap_build_kernel(const int32_t* __restrict__ idx,
+                                                            int T, int K,
+                                                            uint8_t* __restrict__ sm) {
+  extern __shared__ __align__(16) uint32_t tile32[];  // kSlotRows * T bytes
+  uint8_t* tile = reinterpret_cast<uint8_t*>(tile32);
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * kSlotRows;
+  const size_t bk = blockIdx.y;
+  const int rows = min(kSlotRows, T - m0);
+  for (int i = tid; i < kSlotRows * T / 4; i += 256) tile32[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  const int32_t* ib = idx + bk * (size_t)T * K;
+  const int n = T * K;
+  for (int base = 0; base < n; base += 8 * 256) {
+    int mv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * 256 + tid;
+      mv[u] = e < n ? ib[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * 256 + tid;
+      const int m = mv[u];
+      if (m >= m0 && m < m0 + rows) {
+        const int t = e / K;
+        if (m < t) tile[(m - m0) * T + t] = (uint8_t)(e - t * K);
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* out = sm + (bk * T + m0) * (size_t)T;
+  const int nb = rows * T;
+  if ((T & 15) == 0) {  // the tile starts 16-byte aligned
+    for (int i = tid; i < nb / 16; i += 256)
+      reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(tile32)[i];
+  } else {
+    for (int i = tid; i < nb; i += 256) out[i] = tile[i];
+  }
 }
 
 // ---------------------------------------------------------------- backward: dq + dlogg
@@ -608,15 +657,16 @@ hipError_t launch_bwd_prep(const Dims& dm, const void* o, const void* dout, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t entries = (size_t)dm.b * dm.hkv * dm.T * dm.K;
-  {
-    ProfScope ps("slotmap_clear", st);
+  ProfScope ps("slotmap", st);
+  if (dm.T <= kSlotMaxT) {
+    const dim3 grid((unsigned)((dm.T + kSlotRows - 1) / kSlotRows), (unsigned)(dm.b * dm.hkv));
+    hipLaunchKernelGGL(slotmap_build_kernel, grid, dim3(256), (size_t)kSlotRows * dm.T, st, idx,
+                       dm.T, dm.K, ws.slotmap);
+  } else {
     const size_t n16 = ws.slotmap_bytes / 16;
+    const size_t entries = (size_t)dm.b * dm.hkv * dm.T * dm.K;
     hipLaunchKernelGGL(slotmap_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0,
                        st, (uint4*)ws.slotmap, n16);
-  }
-  {
-    ProfScope ps("slotmap_mark", st);
     hipLaunchKernelGGL(slotmap_mark_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256),
                        0, st, idx, dm.T, dm.K, entries, ws.slotmap);
   }
