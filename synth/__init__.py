@@ -135,3 +135,24 @@ def random_scores(shape, seed: int, std: float = math.sqrt(2.0), device="cpu"):
     """i.i.d. N(0, std^2) fp32 selector scores of any shape."""
     gen = _gen(seed, device)
     return _normal(shape, std, gen, device, torch.float32)
+
+
+def random_selection(b: int, hkv: int, T: int, K: int, seed: int) -> torch.Tensor:
+    """int32 [b,hkv,T,K]: for query block t, min(K, t) distinct history blocks
+    m < t drawn uniformly, in ascending order, then -1 padding (the layout of a
+    Top-K selection, without the scores behind it)."""
+    gen = _gen(seed, "cpu")
+    out = torch.full((b, hkv, T, K), -1, dtype=torch.int32)
+    for bb in range(b):
+        for kv in range(hkv):
+            for t in range(1, T):
+                k = min(K, t)
+                pick = torch.randperm(t, generator=gen)[:k].sort().values
+                out[bb, kv, t, :k] = pick.to(torch.int32)
+    return out
+
+
+def random_log_gates(shape, seed: int) -> torch.Tensor:
+    """fp32 log gates in (-4, 0]: log g of the selected blocks of any shape."""
+    gen = _gen(seed, "cpu")
+    return -4.0 * torch.rand(*shape, generator=gen, dtype=torch.float32)

@@ -66,6 +66,42 @@ def compare_full(x, r, K, bs, dtype, gated=True):
     return errs
 
 
+def test_slot_map_past_4096_query_blocks():
+    """T = 4100 query blocks: past the one-pass slot-map build (T <= 4096) the
+    map is cleared, then marked entry by entry.  dK / dV of sampled key blocks
+    and the gate gradients of the rows that selected them, against the oracle
+    (fp32, block 16, a random selection of K = 3 per row)."""
+    from gated_block_sparse_scores_amd import ops
+    bs, T, K, d = 16, 4100, 3, 64
+    say(f"slot map T={T}")
+    w = synth.workload(1, batch=1, hq=1, hkv=1, seqlen=bs * T, head_dim=d, block=bs, topk=K,
+                       dtype="f32")
+    x = synth.train_inputs(w, seed=41, poison_invalid_scores=False)
+    idx = synth.random_selection(1, 1, T, K, seed=42)
+    logg = synth.random_log_gates((1, 1, T, K), seed=43)
+    g = {k_: x[k_].to(DEV) for k_ in ("q", "k", "v", "dout")}
+    idx_g, lg_g = idx.to(DEV), logg.to(DEV)
+    o, lse = ops.attn_fwd(g["q"], g["k"], g["v"], idx_g, lg_g, bs)
+    gr = ops.attn_bwd(g["q"], g["k"], g["v"], o, g["dout"], lse, idx_g, lg_g, None, None, bs,
+                      want_ds=False)
+    torch.cuda.synchronize()
+    dk, dv, dl = gr["dk"].cpu(), gr["dv"].cpu(), gr["dlogg"].cpu()
+    scale = 1.0 / math.sqrt(d)
+    oi, ol = idx.numpy(), logg.numpy()
+    counts = np.bincount(oi[0, 0][oi[0, 0] >= 0], minlength=T)
+    _, rtol = tols(torch.float32)
+    for m in sorted({int(np.argmax(counts)), T // 2, T - 2}):
+        dkb, dvb = O.bwd_key_block(x["q"], x["k"], x["v"], x["dout"], oi, ol, bs, scale, 0, 0, m)
+        lo, hi = O.block_span(m, bs, w.seqlen)
+        ek, ev = rel_l2(np64(dk[0, 0, lo:hi]), dkb), rel_l2(np64(dv[0, 0, lo:hi]), dvb)
+        say(f"  key block {m} ({int(counts[m])} selecting rows): dk {ek:.2e} dv {ev:.2e}")
+        assert ek <= rtol and ev <= rtol, m
+        for t in np.nonzero((oi[0, 0] == m).any(axis=1))[0][:4]:
+            _, dlb, _ = O.bwd_row_block(x["q"], x["k"], x["v"], x["dout"], oi, ol, bs, scale, 0,
+                                        0, int(t))
+            assert rel_l2(np64(dl[0, 0, int(t)]), dlb) <= rtol, (m, int(t))
+
+
 CASES = [
     # b, hq, hkv, n,   d,  bs, K
     (1, 1, 1, 256, 64, 16, 4),
