@@ -845,6 +845,8 @@ def main():
     # ramping); 25 untimed steps of the 8K workload cover about 40 ms
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the GEMM / copy ceilings (profiling runs)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged ragged decode")
     ap.add_argument("--no-variants", action="store_true",
@@ -881,8 +883,9 @@ def main():
         log("32K training workload ...")
         out["train_32k"] = bench_train_32k(args)
     if args.part in ("all", "train"):
-        log("practical ceilings ...")
-        out["ceilings"] = practical_ceilings()
+        if not args.no_ceilings:
+            log("practical ceilings ...")
+            out["ceilings"] = practical_ceilings()
         log("training workload ...")
         res = bench_train(args)
         out.update({
@@ -895,8 +898,9 @@ def main():
             "selected_pairs": int(res["pairs"]),
             "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 2),
             "frac_of_bf16_peak": round(res["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "roofline": dict(res["roofline"], frac_of_practical=round(
-                res["roofline"]["achieved"] / out["ceilings"]["bf16_gemm"]["TFLOPs"], 4)),
+            "roofline": res["roofline"] if "ceilings" not in out else dict(
+                res["roofline"], frac_of_practical=round(
+                    res["roofline"]["achieved"] / out["ceilings"]["bf16_gemm"]["TFLOPs"], 4)),
             "kernel_rooflines": res["kernel_rooflines"],
             "kernels": res["kernels"],
             "kernels_alone": res["kernels_alone"],
