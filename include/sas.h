@@ -48,8 +48,10 @@
  *   - Calls are thread-safe.  Calls that share output buffers must not
  *     overlap.  Every call is ordered on the caller's stream; sas_attn_bwd may
  *     fork part of its work onto a second stream of the library's own (one per
- *     host thread and device, default priority, created on first use) and
- *     joins it back to the caller's stream with events before returning.
+ *     device for the whole process, default priority, created on first use,
+ *     shared by threads under a lock held while a call enqueues its fork,
+ *     kernels and join) and joins it back to the caller's stream with events
+ *     before returning.
  *   - No call allocates device memory, records a memset or synchronises, so
  *     every call can be captured in a HIP graph on a capturing stream (make
  *     one eager sas_attn_bwd call first, so that its second stream exists
