@@ -32,7 +32,7 @@ def test_select_tiny_fp32_workload():
 
 
 @pytest.mark.parametrize("T,K", [(1, 4), (5, 4), (16, 16), (33, 7), (130, 31), (200, 64),
-                                 (700, 31), (1100, 64)])
+                                 (512, 15), (300, 200), (255, 254), (700, 31), (1100, 64)])
 def test_select_shapes(T, K):
     s = synth.random_scores((2, 3, T, T), seed=T * 100 + K)
     s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
@@ -46,6 +46,16 @@ def test_select_ties_lowest_index_and_signed_zero():
     s = torch.round(synth.random_scores((1, 4, T, T), seed=5) * 2) / 2
     s[0, 1] = 0.0
     s[0, 2, :, ::2] = -0.0
+    s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
+    check_select(s, K)
+
+
+def test_select_ties_with_several_keys_per_lane():
+    """Rows of up to 399 history blocks (up to seven keys per lane of the
+    one-wave selection), scores quantised so that the K-th largest value is
+    shared by many blocks: the lower indices among them are kept."""
+    T, K = 400, 50
+    s = torch.round(synth.random_scores((1, 2, T, T), seed=11) * 4) / 4
     s[..., torch.ones(T, T, dtype=torch.bool).triu()] = float("nan")
     check_select(s, K)
 
