@@ -75,3 +75,25 @@ def test_noalloc_step_equals_allocated_step_twice():
             assert max_abs(a["logg"].cpu(), ol[:, :, 0]) <= GATE_ATOL
             oo, olse = O.decode(x["q"], x["kcache"], x["vcache"], L, oi[:, :, 0], ol[:, :, 0], 64)
             assert max_abs(a["o"].cpu(), oo) <= 2e-2 and max_abs(a["lse"].cpu(), olse) <= 2e-2
+
+
+def test_noalloc_step_at_the_batched_decode_size():
+    """Batch 8 x 64K tokens, 32 / 8 heads, K 63 (the batched-decode workload,
+    4.4 MB of the 16 MiB scratch): the no-alloc step equals the allocated one
+    bitwise.  Library against library, so the caches and the pooled-key cache
+    are drawn on the device."""
+    from gated_block_sparse_scores_amd import _lib as Lb
+    b, hq, hkv, L, K = 8, 32, 8, 65536, 63
+    say(f"decode_step_noalloc b={b} hq={hq} hkv={hkv} L={L} K={K}")
+    sh = Lb.Shape(b, hq, hkv, L, 128, 64, Lb.SAS_DTYPE_BF16)
+    assert Lb.sas_decode_step_workspace_size(sh, K) <= Lb.SAS_STATIC_SCRATCH_BYTES
+    w = synth.workload(4, batch=b, hq=hq, hkv=hkv, seqlen=L, head_dim=128, block=64, topk=K)
+    x = synth.decode_inputs(w, seed=9, device=DEV)
+    C = (L - 1) // 64
+    kbar = synth.random_scores((b, hkv, C, 128), seed=10, std=0.1, device=DEV).to(torch.bfloat16)
+    a = _run(x, kbar, L, K, noalloc=True)
+    r = _run(x, kbar, L, K, noalloc=False)
+    for key in a:
+        assert torch.equal(a[key], r[key]), key
+    del x
+    torch.cuda.empty_cache()
