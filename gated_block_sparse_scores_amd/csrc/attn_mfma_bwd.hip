@@ -370,8 +370,12 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  tile_load_lds<DQ_NW>(K0, kbase + (size_t)blist[0] * BS * D);
-  tile_load_lds<DQ_NW>(V0, vbase + (size_t)blist[0] * BS * D);
+  const TileOffsets<DQ_NW> toff;
+  {
+    const int m0 = __builtin_amdgcn_readfirstlane(blist[0]);
+    tile_copy_lds<DQ_NW>(K0, kbase + (size_t)m0 * BS * D, toff);
+    tile_copy_lds<DQ_NW>(V0, vbase + (size_t)m0 * BS * D, toff);
+  }
   wait_all_loads();
   __syncthreads();
   // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
@@ -381,8 +385,9 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
     const float gain = OUTER ? bbias[bi] : 1.0f;
     const bool diag = m == t;
     if (bi + 1 < nb) {
-      tile_load_lds<DQ_NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
-      tile_load_lds<DQ_NW>(Vn, vbase + (size_t)blist[bi + 1] * BS * D);
+      const int mn = __builtin_amdgcn_readfirstlane(blist[bi + 1]);
+      tile_copy_lds<DQ_NW>(Kn, kbase + (size_t)mn * BS * D, toff);
+      tile_copy_lds<DQ_NW>(Vn, vbase + (size_t)mn * BS * D, toff);
     }
 
     // Per 32-key tile: S^T, dP^T (keys x this wave's 32 queries), then dS^T

@@ -160,8 +160,12 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   const int nb = nblk;
   const bf16_t* kbase = k + ((size_t)b * dm.hkv + kv) * dm.n * D;
   const bf16_t* vbase = v + ((size_t)b * dm.hkv + kv) * dm.n * D;
-  tile_load_lds<NW>(K0, kbase + (size_t)blist[0] * BS * D);
-  tile_load_lds<NW>(V0, vbase + (size_t)blist[0] * BS * D);
+  const TileOffsets<NW> toff;
+  {
+    const int m0 = __builtin_amdgcn_readfirstlane(blist[0]);
+    tile_copy_lds<NW>(K0, kbase + (size_t)m0 * BS * D, toff);
+    tile_copy_lds<NW>(V0, vbase + (size_t)m0 * BS * D, toff);
+  }
   wait_all_loads();
   __syncthreads();
 
@@ -171,8 +175,9 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     const float bias2 = OUTER ? 0.0f : bbias[bi];
     const bool diag = m == t;
     if (bi + 1 < nb) {
-      tile_load_lds<NW>(Kn, kbase + (size_t)blist[bi + 1] * BS * D);
-      tile_load_lds<NW>(Vn, vbase + (size_t)blist[bi + 1] * BS * D);
+      const int mn = __builtin_amdgcn_readfirstlane(blist[bi + 1]);
+      tile_copy_lds<NW>(Kn, kbase + (size_t)mn * BS * D, toff);
+      tile_copy_lds<NW>(Vn, vbase + (size_t)mn * BS * D, toff);
     }
 
     // S^T[key][query]: 64 keys x the wave's 32 queries.

@@ -107,6 +107,38 @@ __device__ __forceinline__ void tile_load_lds(bf16_t* tile, const bf16_t* __rest
   }
 }
 
+// The same copy with the lanes' byte offsets formed once: they depend only on
+// the lane and the wave, so a copy then takes a wave-uniform block address (a
+// scalar base) plus a precomputed 32-bit offset per load, with no per-copy
+// address arithmetic.
+template <int NW>
+struct TileOffsets {
+  uint32_t off[16 / NW];
+  __device__ __forceinline__ TileOffsets() {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < 16 / NW; ++i) {
+      const int row = (wave + i * NW) * 4 + (lane >> 4);
+      const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+      off[i] = (uint32_t)((row * TILE_LD + (((lane & 15) ^ f) << 3)) * sizeof(bf16_t));
+    }
+  }
+};
+
+// src must be uniform over the wave (a block's first row).
+template <int NW>
+__device__ __forceinline__ void tile_copy_lds(bf16_t* tile, const bf16_t* __restrict__ src,
+                                              const TileOffsets<NW>& to) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int i = 0; i < 16 / NW; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)src + to.off[i]),
+                                     (lds_void*)(tile + (wave + i * NW) * 4 * TILE_LD), 16, 0,
+                                     0);
+}
+
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace sas
