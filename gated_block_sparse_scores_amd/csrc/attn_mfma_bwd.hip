@@ -403,10 +403,16 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
         sa = mfma32(row_frag(Kc, kt * 32 + c, kc * 16 + g * 8), qf[kc], sa);
         pa = mfma32(row_frag(Vc, kt * 32 + c, kc * 16 + g * 8), of[kc], pa);
       }
+      // the diagonal block's keys past the row: logit -inf, so P = 0 (a
+      // uniform branch, taken for one block of the row)
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + acc_row(r, g) > qi) sa[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(sa[r], sc2, off2));
-        if (diag && kt * 32 + acc_row(r, g) > qi) p = 0.0f;
+        const float p = fast_exp2(fmaf(sa[r], sc2, off2));
         pa[r] = p * ((OUTER ? pa[r] * gain : pa[r]) - dval);
       }
       db[2 * kt] = pack8(pa, 0);
