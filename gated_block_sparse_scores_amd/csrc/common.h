@@ -130,6 +130,19 @@ __device__ __forceinline__ uint64_t bitonic_sort_asc64(uint64_t v, int lane) {
   else return v;
 }
 
+// The same network into descending lane order (the larger key goes where
+// the ascending sort puts the smaller).
+template <int KK = 2, int J = 1>
+__device__ __forceinline__ uint64_t bitonic_sort_desc64(uint64_t v, int lane) {
+  const uint64_t o = ((uint64_t)xor_lane<J>((uint32_t)(v >> 32)) << 32) |
+                     xor_lane<J>((uint32_t)v);
+  const bool lower = (lane & J) == 0, up = (lane & KK) == 0 || KK == 64;
+  v = (lower == up) ? (v > o ? v : o) : (v > o ? o : v);
+  if constexpr (J > 1) return bitonic_sort_desc64<KK, J / 2>(v, lane);
+  else if constexpr (KK < 64) return bitonic_sort_desc64<KK * 2, KK>(v, lane);
+  else return v;
+}
+
 // Copies n 8-byte keys from global memory to LDS with all of a thread's loads
 // (up to PER per pass) issued before its first store, so a pass costs one
 // memory round trip instead of one per key; at most one key per thread is
@@ -191,20 +204,27 @@ __device__ __forceinline__ uint64_t merge_top64(const uint64_t* lists, int nl, i
   return acc;
 }
 
+// Butterfly reductions over the wave (lane distances 32, 16, ..., 1, the
+// lane exchanges of xor_lane): every lane ends with the result.
+template <int J = 32>
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, __uint_as_float(xor_lane<J>(__float_as_uint(v))));
+  if constexpr (J > 1) return wave_max<J / 2>(v);
+  else return v;
 }
+template <int J = 32>
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += __uint_as_float(xor_lane<J>(__float_as_uint(v)));
+  if constexpr (J > 1) return wave_sum<J / 2>(v);
+  else return v;
 }
+template <int J = 32>
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t o = ((uint64_t)xor_lane<J>((uint32_t)(b >> 32)) << 32) | xor_lane<J>((uint32_t)b);
+  v += __longlong_as_double((long long)o);
+  if constexpr (J > 1) return wave_sum_d<J / 2>(v);
+  else return v;
 }
 
 // Inclusive prefix sum across a wave.

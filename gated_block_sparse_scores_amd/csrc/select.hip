@@ -417,18 +417,7 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
   // position in its wave plus, for each other wave, how many of that wave's
   // sorted keys exceed it (binary search in LDS).
   const int lane = tid & 63, wave = tid >> 6;
-  uint64_t v = mykey;
-#pragma unroll
-  for (int kk = 2; kk <= 64; kk <<= 1) {
-#pragma unroll
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, j);
-      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j);
-      const uint64_t o = ((uint64_t)ohi << 32) | olo;
-      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
-      v = keep_max ? (v > o ? v : o) : (v > o ? o : v);
-    }
-  }
+  const uint64_t v = bitonic_sort_desc64(mykey, lane);  // lane exchanges by DPP / row swaps
   srt[wave][lane] = v;
   // Chunk statistics: one barrier publishes the sorted lists and the wave
   // maxima together; the waves' fp64 sums of exp are combined, in wave order,
