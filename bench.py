@@ -480,8 +480,8 @@ def bench_selector_bwd(args, w, gr, qb, kb):
     kt = L.sas_profiler_read()
     esz = 2 if w.dtype == "bf16" else 4
     spread_bytes = 2 * esz * w.batch * (w.hq + w.hkv) * w.seqlen * w.head_dim
-    n_sp, t_sp = kt.get("pool_spread", (1, 0.0))
-    spread_us = t_sp / n_sp * 1e3 * 2          # two launches (dq, dk) per call
+    _, t_sp = kt.get("pool_spread", (1, 0.0))
+    spread_us = t_sp * 1e3 / args.steps        # the spread into dq and dk, per call
     n_sb, t_sb = kt.get("selector_bwd", (1, 0.0))
     sb_us = t_sb / n_sb * 1e3
     gbs = spread_bytes / (spread_us * 1e-6) / 1e9 if spread_us > 0 else None

@@ -84,10 +84,13 @@ __global__ void __launch_bounds__(256) selector_bwd_kernel(const float* __restri
   }
 }
 
-// x[b][h][i][c] += xbar[b][h / group][i / bs][c] / (group * n_t).  Grid
-// (ceil(n d / (8 * 256 * kSpreadVec)), b * heads): a workgroup covers a span of
+// x[b][h][i][c] += xbar[b][h / group][i / bs][c] / (group * n_t), for dq
+// (its b * hq planes) and dk (b * hkv planes) in one launch.  Grid
+// (ceil(n d / (8 * 256 * kSpreadVec)), planes): a workgroup covers a span of
 // one (b, h) plane, each lane kSpreadVec 8-value vectors (16 bytes of bf16, 32
-// of fp32) 2048 values apart, all loads issued before the arithmetic.
+// of fp32) 2048 values apart, all loads issued before the arithmetic; the
+// division is one reciprocal per vector (exact for the power-of-two counts of
+// whole blocks).
 constexpr int kSpreadVec = 4;
 
 template <typename Tx>
@@ -121,20 +124,29 @@ __device__ __forceinline__ void store8(Tx* p, const float (&v)[8]) {
   }
 }
 
+template <typename Tx>
+struct SpreadPlanes {
+  Tx* x[2];              // dq, dk (either may be absent: then it has no planes)
+  const float* xbar[2];  // dqbar, dkbar
+  int heads[2], group[2];
+  int planes0;           // planes of the first tensor (b * heads[0], or 0)
+};
+
 template <typename Tx, int D>
-__global__ void __launch_bounds__(256) pool_spread_kernel(Tx* __restrict__ x,
-                                                          const float* __restrict__ xbar,
-                                                          int heads, int group, int n, int bs,
+__global__ void __launch_bounds__(256) pool_spread_kernel(SpreadPlanes<Tx> sp, int n, int bs,
                                                           const int32_t* __restrict__ lens) {
   constexpr int VPR = D / 8;  // vectors per row
-  const int bh = blockIdx.y;
+  const int which = (int)blockIdx.y >= sp.planes0 ? 1 : 0;
+  const int bh = (int)blockIdx.y - (which ? sp.planes0 : 0);
+  const int heads = sp.heads[which], group = sp.group[which];
   const int h = bh % heads, b = bh / heads;
   const int T = (n + bs - 1) / bs;
   // ragged batch: only this sequence's own rows, n_t counted within them
   const int nlen = lens ? min(max(lens[b], 0), n) : n;
   const int nvec = nlen * VPR;
-  Tx* plane = x + (size_t)bh * n * D;
-  const float* sbase = xbar + ((size_t)b * (heads / group) + h / group) * (size_t)T * D;
+  Tx* plane = sp.x[which] + (size_t)bh * n * D;
+  const float* sbase =
+      sp.xbar[which] + ((size_t)b * (heads / group) + h / group) * (size_t)T * D;
   float v[kSpreadVec][8], a[kSpreadVec][8];
   int ev[kSpreadVec];
 #pragma unroll
@@ -157,9 +169,9 @@ __global__ void __launch_bounds__(256) pool_spread_kernel(Tx* __restrict__ x,
     if (e < nvec) {
       const int i = e / VPR, c = (e % VPR) * 8;
       const int t = i / bs;
-      const float den = (float)(group * min(bs, nlen - t * bs));
+      const float rden = 1.0f / (float)(group * min(bs, nlen - t * bs));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[k][q] += a[k][q] / den;
+      for (int q = 0; q < 8; ++q) v[k][q] += a[k][q] * rden;
       store8(plane + (size_t)i * D + c, v[k]);
     }
   }
@@ -180,32 +192,37 @@ hipError_t launch_selector_bwd(const Dims& dm, const float* ds, const float* qba
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  for (int which = 0; which < 2; ++which) {
-    void* x = which ? dk : dq;
-    if (!x) continue;
-    const int heads = which ? dm.hkv : dm.hq, group = which ? 1 : dm.g;
-    const long nvec = (long)dm.n * dm.d / 8;
-    if (nvec == 0) continue;
-    ProfScope ps("pool_spread", st);
-    const dim3 grid((unsigned)((nvec + 256 * kSpreadVec - 1) / (256 * kSpreadVec)),
-                    (unsigned)(dm.b * heads));
-    const float* xb = which ? dkbar : dqbar;
+  const long nvec = (long)dm.n * dm.d / 8;
+  const int pq = dq ? dm.b * dm.hq : 0, pk = dk ? dm.b * dm.hkv : 0;
+  if (nvec == 0 || pq + pk == 0) return hipSuccess;
+  ProfScope ps("pool_spread", st);
+  const dim3 grid((unsigned)((nvec + 256 * kSpreadVec - 1) / (256 * kSpreadVec)),
+                  (unsigned)(pq + pk));
 #define SAS_SPREAD(TX, DD)                                                                    \
-  hipLaunchKernelGGL((pool_spread_kernel<TX, DD>), grid, dim3(256), 0, st, (TX*)x, xb, heads, \
-                     group, dm.n, dm.bs, dm.seq_lens)
-    if (dm.bf16 && dm.d == 128)
-      SAS_SPREAD(bf16_t, 128);
-    else if (dm.bf16)
-      SAS_SPREAD(bf16_t, 64);
-    else if (dm.d == 128)
-      SAS_SPREAD(float, 128);
-    else
-      SAS_SPREAD(float, 64);
-#undef SAS_SPREAD
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  {                                                                                           \
+    SpreadPlanes<TX> sp;                                                                      \
+    sp.x[0] = dq ? (TX*)dq : (TX*)dk;                                                         \
+    sp.xbar[0] = dq ? dqbar : dkbar;                                                          \
+    sp.heads[0] = dq ? dm.hq : dm.hkv;                                                        \
+    sp.group[0] = dq ? dm.g : 1;                                                              \
+    sp.x[1] = (TX*)dk;                                                                        \
+    sp.xbar[1] = dkbar;                                                                       \
+    sp.heads[1] = dm.hkv;                                                                     \
+    sp.group[1] = 1;                                                                          \
+    sp.planes0 = dq ? pq : pk;                                                                \
+    hipLaunchKernelGGL((pool_spread_kernel<TX, DD>), grid, dim3(256), 0, st, sp, dm.n, dm.bs, \
+                       dm.seq_lens);                                                          \
   }
-  return hipSuccess;
+  if (dm.bf16 && dm.d == 128)
+    SAS_SPREAD(bf16_t, 128)
+  else if (dm.bf16)
+    SAS_SPREAD(bf16_t, 64)
+  else if (dm.d == 128)
+    SAS_SPREAD(float, 128)
+  else
+    SAS_SPREAD(float, 64)
+#undef SAS_SPREAD
+  return hipGetLastError();
 }
 
 }  // namespace sas
