@@ -354,11 +354,15 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     const int nsl = d / 8;  // lanes carrying 8 dims each (16 for d = 128, 8 for d = 64)
     // The summary rows' loads go out first: nothing in their addresses waits on
     // the query, so their latency overlaps the query's.
+    // Rows past the history and lanes past d read an in-bounds row (clamped)
+    // and weight it 0 (or discard it), so no row needs a branch and the rows'
+    // products interleave.
+    const int cmax = max(ct - 1, 0), subc = sub < nsl ? sub : 0;
     Slice8<Tk> sl[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int mm = m0 + grp + 16 * i;
-      if (sub < nsl && mm < ct) sl[i].load(kbar + (bk * kbar_ld + mm) * (size_t)d + sub * 8);
+      const int mm = min(m0 + grp + 16 * i, cmax);
+      sl[i].load(kbar + (bk * kbar_ld + mm) * (size_t)d + subc * 8);
     }
     double qd[8];
     if (qraw) {
@@ -398,10 +402,8 @@ __global__ void __launch_bounds__(256) select_chunk_kernel(
     for (int i = 0; i < 16; ++i) {
       const int mm = m0 + grp + 16 * i;
       double a = 0.0;
-      if (sub < nsl && mm < ct) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a += qd[e] * sl[i].get(e);
-      }
+      for (int e = 0; e < 8; ++e) a += qd[e] * sl[i].get(e);  // qd = 0 past d
       a = row16_sum_d(a);
       if (sub == 0) sval[grp + 16 * i] = mm < ct ? (float)(a * scale) : 0.0f;
     }
