@@ -179,3 +179,79 @@ def test_full_lengths_equal_dense_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for key in ("dq", "dk", "dv", "dlogg", "ds"):
         assert torch.equal(g1[key], g2[key]), key
+
+
+@pytest.mark.timeout(300)
+def test_ragged_batch_of_the_benchmark():
+    """The ragged training batch the benchmark times: sequences of 8192, 6177,
+    3077 and 1024 tokens padded to 8192, 32/8 heads, d 128, block 64, Top-31,
+    stand-in selector.  Per sequence (the oracle on that sequence's own tokens):
+    its pooled scores (fp64 dot products rounded once, so equal but for an
+    fp32 rounding boundary), the Top-K of the device's scores, and for two KV
+    heads the o, LSE, dq, dlogg and ds of sampled query blocks (the last one
+    partial) and the dk, dv of the key block with the longest inverse list;
+    padding rows stay zero."""
+    from gated_block_sparse_scores_amd import ops
+    lens = [8192, 6177, 3077, 1024]
+    w = synth.workload(2, batch=len(lens))
+    x = synth.train_inputs(w, seed=77)
+    for bb, nb in enumerate(lens):
+        for key in ("q", "k", "v", "dout"):
+            x[key][bb, :, nb:] = JUNK
+    say(f"ragged batch {lens}")
+    xd = {k_: x[k_].to(DEV) for k_ in ("q", "k", "v", "dout")}
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    T, bs, K, g = w.nblocks, w.block, w.topk, w.group
+    qb = ops.block_pool(xd["q"], bs, g, seq_lens=sl)
+    kb = ops.block_pool(xd["k"], bs, 1, seq_lens=sl)
+    idx, logg, lse_s, s = ops.select_topk(w.batch, w.hkv, T, T, K, qbar=qb, kbar=kb, seq_lens=sl,
+                                          seqlen=w.seqlen, block=bs)
+    o, lse = ops.attn_fwd(xd["q"], xd["k"], xd["v"], idx, logg, bs, seq_lens=sl)
+    gr = ops.attn_bwd(xd["q"], xd["k"], xd["v"], o, xd["dout"], lse, idx, logg, s, lse_s, bs,
+                      seq_lens=sl)
+    torch.cuda.synchronize()
+    scale = O.default_scale(w.head_dim)
+    s_c, idx_c, logg_c = s.cpu().numpy(), idx.cpu().numpy(), logg.cpu().numpy()
+    o_c, lse_c, dq_c = o.cpu(), lse.cpu(), gr["dq"].cpu()
+    dl_c, ds_c = gr["dlogg"].cpu().numpy(), gr["ds"].cpu().numpy()
+    dk_c, dv_c = gr["dk"].cpu(), gr["dv"].cpu()
+    worst = {}
+    for bb, nb in enumerate(lens):
+        Tb = O.n_blocks(nb, bs)
+        xb = {k_: x[k_][bb:bb + 1, :, :nb] for k_ in ("q", "k", "v", "dout")}
+        qo = O.to_f32(O.pool_queries(xb["q"], w.hkv, bs))
+        ko = O.to_f32(O.pool_keys(xb["k"], bs))
+        so = O.standin_scores(qo, ko, scale, Tb)
+        valid = np.tril(np.ones((Tb, Tb), dtype=bool), -1)
+        assert np.sum((s_c[bb:bb + 1, :, :Tb, :Tb] != so) & valid) <= 2, bb
+        oi, ol, ols = O.select_topk(s_c[bb:bb + 1, :, :Tb, :Tb], K)
+        np.testing.assert_array_equal(idx_c[bb:bb + 1, :, :Tb], oi)
+        assert max_abs(logg_c[bb:bb + 1, :, :Tb], ol) <= GATE_ATOL
+        assert torch.all(o_c[bb, :, nb:] == 0) and torch.all(dq_c[bb, :, nb:] == 0)
+        assert torch.all(dk_c[bb, :, nb:] == 0) and torch.all(dv_c[bb, :, nb:] == 0)
+        for kv in (0, w.hkv - 1):
+            hs = slice(kv * g, (kv + 1) * g)
+            for t in sorted({1, Tb // 2, Tb - 1}):
+                lo, hi = O.block_span(t, bs, nb)
+                ob, lb, _, _ = O.fwd_row_block(xb["q"], xb["k"], xb["v"], oi, ol, bs, scale, 0,
+                                               kv, t)
+                dqb, dlb, _ = O.bwd_row_block(xb["q"], xb["k"], xb["v"], xb["dout"], oi, ol, bs,
+                                              scale, 0, kv, t)
+                dsr = O.ds_row(s_c[bb, kv, t, :t], ols[0, kv, t], oi[0, kv, t], dlb)
+                e = {"o": max_abs(o_c[bb, hs, lo:hi], ob), "lse": max_abs(lse_c[bb, hs, lo:hi], lb),
+                     "dq": rel_l2(dq_c[bb, hs, lo:hi], dqb),
+                     "dlogg": max_abs(dl_c[bb, kv, t], dlb) / max(np.abs(dlb).max(), 1e-3),
+                     "ds": max_abs(ds_c[bb, kv, t, :t], dsr) / max(np.abs(dsr).max(), 1e-3)}
+                for k_, v_ in e.items():
+                    worst[k_] = max(worst.get(k_, 0.0), v_)
+            counts = np.bincount(oi[0, kv][oi[0, kv] >= 0], minlength=Tb)
+            m = int(np.argmax(counts))
+            dkb, dvb = O.bwd_key_block(xb["q"], xb["k"], xb["v"], xb["dout"], oi, ol, bs, scale,
+                                       0, kv, m)
+            lo, hi = O.block_span(m, bs, nb)
+            worst["dk"] = max(worst.get("dk", 0.0), rel_l2(dk_c[bb, kv, lo:hi], dkb))
+            worst["dv"] = max(worst.get("dv", 0.0), rel_l2(dv_c[bb, kv, lo:hi], dvb))
+    say("  worst: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in worst.items()))
+    assert worst["o"] <= 2e-2 and worst["lse"] <= 2e-2
+    for k_ in ("dq", "dlogg", "ds", "dk", "dv"):
+        assert worst[k_] <= 3e-2, k_
