@@ -175,23 +175,24 @@ def _block_err(got, ref, rms):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("variant", [("sigmoid", True, False), ("softmax", False, True),
-                                     ("raw", False, False)],
-                         ids=["sigmoid-outer", "softmax-ste", "raw"])
+@pytest.mark.parametrize("variant", [("sigmoid", True, False, 31), ("softmax", False, True, 31),
+                                     ("raw", False, False, 31), ("softmax", False, False, 127)],
+                         ids=["sigmoid-outer", "softmax-ste", "raw", "dense-scope"])
 def test_gate_variant_at_the_8k_workload(variant):
-    """The 8K-token training workload (32/8 heads, d 128, block 64, Top-31,
-    stand-in selector) under a gate variant, in the launch configuration the
-    benchmark times: the device's selection against the oracle's Top-K of the
-    same fp32 scores with the variant's activation, then for two KV heads the
-    oracle recomputes sampled query blocks (o, LSE, dq, dlogg, ds) and the key
-    block with that head's longest inverse list (dk, dv), each held to the
-    tolerance on its own."""
+    """The 8K-token training workload (32/8 heads, d 128, block 64, stand-in
+    selector; Top-31, or every history block for the dense scope) under a gate
+    variant, in the launch configuration the benchmark times: the device's
+    selection against the oracle's Top-K of the same fp32 scores with the
+    variant's activation, then for two KV heads the oracle recomputes sampled
+    query blocks (o, LSE, dq, dlogg, ds) and the key block with that head's
+    longest inverse list (dk, dv), each held to the tolerance on its own."""
     from gated_block_sparse_scores_amd import _lib as L
     from gated_block_sparse_scores_amd import ops
-    act, outer, ste = variant
+    act, outer, ste, topk = variant
+    variant = variant[:3]
     gate = L.gate_code(act, outer, ste)
-    say(f"8K workload, gates {vid(variant)}")
-    w = synth.workload(2)
+    say(f"8K workload, gates {vid(variant)}, K {topk}")
+    w = synth.workload(2, topk=topk)
     x = synth.train_inputs(w, device=DEV)
     T = w.nblocks
     qb = ops.block_pool(x["q"], w.block, w.group)
