@@ -46,6 +46,8 @@ namespace sas {
 
 namespace {
 
+template <bool B> struct DiagTag { static constexpr bool value = B; };
+
 constexpr int D = 128;
 constexpr int BS = 64;
 // q / dout / K / V tiles: 64 x 128 bf16, swizzled (see mfma.h)
@@ -171,12 +173,14 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
   wait_all_loads();
   __syncthreads();
   float dlsum = 0.0f;
-  for (int it = 0; it < items; ++it) {
+  // The list opens with the diagonal block (t = m, one item per head): those
+  // items mask the keys past each row; the loop over the rest has no mask.
+  auto item = [&](int it, auto diagc) __attribute__((always_inline)) {
     const int e = it / dm.g;
     const uint32_t ent = lst[e];
     const int t = (int)(ent & 0xFFFF);
     const int slot = (int)(ent >> 16);
-    const bool diag = t == m;
+    constexpr bool diag = decltype(diagc)::value;
     const float bias2 = OUTER ? 0.0f : cur_bias * LOG2E;
     const float gain = OUTER ? expf(cur_bias) : 1.0f;
 
@@ -244,7 +248,10 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     if (it + 1 < items) fetch(it + 1);
     wait_all_loads();
     __syncthreads();  // item it + 1 is in the tiles
-  }
+  };
+  const int ndiag = min(dm.g, items);
+  for (int it = 0; it < ndiag; ++it) item(it, DiagTag<true>());
+  for (int it = ndiag; it < items; ++it) item(it, DiagTag<false>());
 
   // dK = scale * (dK^T)^T, dV: lane holds key `key`, dims 64 qh + 32 dt + acc_row(r, g).
   bf16_t* dkp = dk + kvrow;
