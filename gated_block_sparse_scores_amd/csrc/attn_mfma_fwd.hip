@@ -39,6 +39,8 @@ namespace sas {
 
 namespace {
 
+template <bool B> struct DiagTag { static constexpr bool value = B; };
+
 constexpr int D = 128;
 constexpr int BS = 64;
 // K and V tiles: 64 x 128 bf16 each, swizzled (see mfma.h)
@@ -170,10 +172,10 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   __syncthreads();
 
   // Block bi from (Kc, Vc) while block bi + 1 is copied into (Kn, Vn).
-  auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
-    const int m = blist[bi];
+  auto step = [&](int bi, const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn,
+                  auto diagc) __attribute__((always_inline)) {
     const float bias2 = OUTER ? 0.0f : bbias[bi];
-    const bool diag = m == t;
+    constexpr bool diag = decltype(diagc)::value;  // the last block is the diagonal one
     if (bi + 1 < nb) {
       const int mn = __builtin_amdgcn_readfirstlane(blist[bi + 1]);
       tile_copy_lds<NW>(Kn, kbase + (size_t)mn * BS * D, toff);
@@ -237,9 +239,18 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
     wait_all_loads();   // this wave's copies of the next block
     __syncthreads();    // everyone's copies landed; everyone is done with (Kc, Vc)
   };
-  for (int bi = 0; bi < nb; bi += 2) {
-    step(bi, K0, V0, K1, V1);
-    if (bi + 1 < nb) step(bi + 1, K1, V1, K0, V0);
+  // history blocks in pairs (the tiles alternate), then the diagonal block
+  // last, the only one that masks keys past its rows
+  int bi = 0;
+  for (; bi + 2 < nb; bi += 2) {
+    step(bi, K0, V0, K1, V1, DiagTag<false>());
+    step(bi + 1, K1, V1, K0, V0, DiagTag<false>());
+  }
+  if (bi + 1 < nb) {
+    step(bi, K0, V0, K1, V1, DiagTag<false>());
+    step(bi + 1, K1, V1, K0, V0, DiagTag<true>());
+  } else {
+    step(bi, K0, V0, K1, V1, DiagTag<true>());
   }
 
   // Normalise and store o (bf16) and LSE (natural log); padding rows: 0, +inf.
