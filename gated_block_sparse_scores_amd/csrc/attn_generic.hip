@@ -632,6 +632,10 @@ BwdWorkspace bwd_workspace_layout(const Dims& dm, void* base) {
   w.dlogg_part = (float*)take(rows * (size_t)bwd_dlogg_chunks(dm) * dm.K * sizeof(float));
   w.slotmap_bytes = align256(rows * (size_t)dm.T);
   w.slotmap = (uint8_t*)take(w.slotmap_bytes);
+  const int nparts = mfma_bwd_supported(dm) ? dkdv_split_plan(dm).nparts : 0;
+  w.dkdv_part =
+      nparts ? (float*)take((size_t)nparts * dm.b * dm.hkv * kDkdvPartFloats * sizeof(float))
+             : nullptr;
   w.bytes = off;
   return w;
 }

@@ -24,7 +24,10 @@
 //    heads, 64 rows, 64 keys) directly.  The q / dout tiles are single-buffered:
 //    the next item is copied (direct-to-LDS loads) after every wave is done
 //    with the current one, and the second workgroup on the CU computes
-//    meanwhile.
+//    meanwhile.  When the grid is small enough that the longest lists (the
+//    lowest key blocks) would outlast the rest, those blocks are split: several
+//    workgroups take contiguous shares of one list and store fp32 partials,
+//    which a small kernel sums in share order (the sums stay repeatable).
 //  * dQ (query-major): the forward's tiling (2 heads x 64 rows per workgroup,
 //    four waves of 32 rows), recomputing S^T = K Q^T and dP^T = V dO^T per
 //    selected block and accumulating dQ^T += K^T dS^T, with K and V staged
@@ -36,7 +39,10 @@
 // gradient of a block is the sum of P dP instead of dS.
 #include <math.h>
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -72,7 +78,8 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ Dv,
     const float* __restrict__ logg, const uint8_t* __restrict__ slotmap,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg) {
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ dlogg,
+    const DkdvSplit sp, float* __restrict__ part) {
   // q and dout tiles in one array: they are only read after every copy into
   // them has landed, and one base register with constant offsets addresses both
   __shared__ __align__(16) bf16_t QO[2 * BS * TILE_LD];
@@ -87,13 +94,18 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
   __shared__ uint32_t lst[DKV_MAXT];
   __shared__ int scan_scr[16];
 
-  // key blocks ascending (low blocks are selected by the most query blocks, so
-  // the longest inverse lists go first), KV head fastest
-  int tile = blockIdx.x;
-  const int kv = tile % dm.hkv;
-  tile /= dm.hkv;
-  const int b = tile % dm.b;
-  const int m = tile / dm.b;
+  // The parts of the split key blocks first, then the other key blocks
+  // ascending (low blocks are selected by the most query blocks, so the longest
+  // inverse lists go first); KV head fastest.  A part's partial sums go to slot
+  // blockIdx.x of `part`.
+  const int kv = blockIdx.x % dm.hkv;
+  const int b = (blockIdx.x / dm.hkv) % dm.b;
+  const int j = blockIdx.x / (dm.hkv * dm.b);
+  const bool split = j < sp.nparts;
+  const int m = split ? sp.part_m[j] : sp.nsplit + (j - sp.nparts);
+  const int share = split ? sp.part_p[j] : 0;
+  const int nshares = split ? sp.first[m + 1] - sp.first[m] : 1;
+  float* const partp = split ? part + (size_t)blockIdx.x * kDkdvPartFloats : nullptr;
   const size_t bk = (size_t)b * dm.hkv + kv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, c = lane & 31;
@@ -103,6 +115,13 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
   // ragged batch: a key block past the sequence's end is selected by no row and
   // its diagonal rows are padding, so dK = dV = 0 (uniform over the workgroup)
   if (dm.seq_lens && m * BS >= min(max(dm.seq_lens[b], 0), dm.n)) {
+    if (split) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *reinterpret_cast<float4*>(partp + (i * DKV_NT + threadIdx.x) * 4) =
+            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -144,7 +163,9 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
   }
   __syncthreads();
 
-  const int items = ne * dm.g;
+  // this workgroup's share of the list: entries [elo, ehi), G items each
+  const int elo = ne * share / nshares, ehi = ne * (share + 1) / nshares;
+  const int ilo = elo * dm.g, ihi = ehi * dm.g;
   typedef __attribute__((address_space(3))) void lds_void;
   // Copies item `it` into the tiles: q and dout rows by all waves, LSE and D
   // by wave 0, the log gate by lane 0 of wave 1 (or a 0 when ungated).
@@ -169,7 +190,7 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
       }
     }
   };
-  if (items > 0) fetch(0);
+  if (ilo < ihi) fetch(ilo);
   wait_all_loads();
   __syncthreads();
   float dlsum = 0.0f;
@@ -245,13 +266,31 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
       }
     }
     __syncthreads();  // everyone is done with the tiles and the exchange
-    if (it + 1 < items) fetch(it + 1);
+    if (it + 1 < ihi) fetch(it + 1);
     wait_all_loads();
     __syncthreads();  // item it + 1 is in the tiles
   };
-  const int ndiag = min(dm.g, items);
-  for (int it = 0; it < ndiag; ++it) item(it, DiagTag<true>());
-  for (int it = ndiag; it < items; ++it) item(it, DiagTag<false>());
+  // the diagonal's items exist in the first share only
+  const int idiag = elo == 0 ? min(dm.g, ihi) : ilo;
+  for (int it = ilo; it < idiag; ++it) item(it, DiagTag<true>());
+  for (int it = idiag; it < ihi; ++it) item(it, DiagTag<false>());
+
+  if (split) {
+    // fp32 partials, float4 i of thread x at (i * 256 + x) * 4: dK^T (unscaled)
+    // then dV^T, in the order of the stores below
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        *reinterpret_cast<float4*>(partp + ((dt * 4 + r4) * DKV_NT + threadIdx.x) * 4) =
+            make_float4(dka[dt][r4 * 4], dka[dt][r4 * 4 + 1], dka[dt][r4 * 4 + 2],
+                        dka[dt][r4 * 4 + 3]);
+        *reinterpret_cast<float4*>(partp + ((8 + dt * 4 + r4) * DKV_NT + threadIdx.x) * 4) =
+            make_float4(dva[dt][r4 * 4], dva[dt][r4 * 4 + 1], dva[dt][r4 * 4 + 2],
+                        dva[dt][r4 * 4 + 3]);
+      }
+    return;
+  }
 
   // dK = scale * (dK^T)^T, dV: lane holds key `key`, dims 64 qh + 32 dt + acc_row(r, g).
   bf16_t* dkp = dk + kvrow;
@@ -268,6 +307,56 @@ __global__ void __launch_bounds__(DKV_NT, 2) bwd_dkdv_mfma_kernel(
       wv.y = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
       *reinterpret_cast<uint2*>(dkp + dd) = wk;
       *reinterpret_cast<uint2*>(dvp + dd) = wv;
+    }
+}
+
+// Sums the parts of every split key block, in part order, and stores dK
+// (scaled) and dV in bf16, each thread the values the dK/dV kernel's own
+// epilogue would store.  One workgroup per (split key block, batch, KV head).
+__global__ void __launch_bounds__(DKV_NT) bwd_dkdv_combine_kernel(
+    Dims dm, const DkdvSplit sp, const float* __restrict__ part, bf16_t* __restrict__ dk,
+    bf16_t* __restrict__ dv) {
+  const int kv = blockIdx.x % dm.hkv;
+  const int b = (blockIdx.x / dm.hkv) % dm.b;
+  const int m = blockIdx.x / (dm.hkv * dm.b);
+  const size_t bk = (size_t)b * dm.hkv + kv;
+  const size_t rows = (size_t)dm.b * dm.hkv;
+  const int j0 = sp.first[m], j1 = sp.first[m + 1];
+  float4 acc[16];
+  {
+    const float4* src = reinterpret_cast<const float4*>(part + (j0 * rows + bk) * kDkdvPartFloats);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = src[i * DKV_NT + threadIdx.x];
+  }
+  for (int j = j0 + 1; j < j1; ++j) {
+    const float4* src = reinterpret_cast<const float4*>(part + (j * rows + bk) * kDkdvPartFloats);
+    float4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = src[i * DKV_NT + threadIdx.x];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[i].x += x[i].x;
+      acc[i].y += x[i].y;
+      acc[i].z += x[i].z;
+      acc[i].w += x[i].w;
+    }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, kt = wave & 1, qh = wave >> 1;
+  const size_t kvrow = (bk * dm.n + (size_t)m * BS + kt * 32 + (lane & 31)) * D;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dd = qh * 64 + dt * 32 + r4 * 8 + g * 4;
+      const float4 a = acc[dt * 4 + r4], c = acc[8 + dt * 4 + r4];
+      uint2 wk, wv;
+      wk.x = pack_bf16x2(a.x * dm.scale, a.y * dm.scale);
+      wk.y = pack_bf16x2(a.z * dm.scale, a.w * dm.scale);
+      wv.x = pack_bf16x2(c.x, c.y);
+      wv.y = pack_bf16x2(c.z, c.w);
+      *reinterpret_cast<uint2*>(dk + kvrow + dd) = wk;
+      *reinterpret_cast<uint2*>(dv + kvrow + dd) = wv;
     }
 }
 
@@ -540,15 +629,61 @@ void launch_dq(const Dims& dm, const void* q, const void* k, const void* v, cons
 void launch_dkdv(const Dims& dm, const void* q, const void* k, const void* v, const void* dout,
                  const float* lse, const float* logg, const BwdWorkspace& ws, void* dk,
                  void* dv, hipStream_t st) {
-  const size_t wgs = (size_t)dm.b * dm.hkv * dm.T;
+  const DkdvSplit sp = dkdv_split_plan(dm);
+  const size_t rows = (size_t)dm.b * dm.hkv;
+  const size_t wgs = rows * (sp.nparts + dm.T - sp.nsplit);
+  // one timing scope over both kernels: the dK/dV work includes the sums
   ProfScope ps("bwd_dkdv_mfma", st);
   auto kern = dm.outer ? bwd_dkdv_mfma_kernel<true> : bwd_dkdv_mfma_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(DKV_NT), 0, st, dm, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout, lse, ws.D, logg,
-                     ws.slotmap, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part);
+                     ws.slotmap, (bf16_t*)dk, (bf16_t*)dv, ws.dlogg_part, sp, ws.dkdv_part);
+  if (sp.nparts > 0)
+    hipLaunchKernelGGL(bwd_dkdv_combine_kernel, dim3((unsigned)(rows * sp.nsplit)),
+                       dim3(DKV_NT), 0, st, dm, sp, (const float*)ws.dkdv_part, (bf16_t*)dk,
+                       (bf16_t*)dv);
 }
 
 }  // namespace
+
+DkdvSplit dkdv_split_plan(const Dims& dm) {
+  DkdvSplit sp{};
+  const int T = dm.T;
+  if (T < 2 || dm.K <= 0) return sp;
+  int cus = 256, dev = 0, c = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      c > 0)
+    cus = c;
+  // Expected list length of key block m when every query block t selects K of
+  // its t history blocks evenly: the diagonal plus the sum over t > m of
+  // min(1, K / t).  Non-increasing in m, so the split blocks are a prefix.
+  std::vector<double> e(T);
+  double tail = 0.0, total = 0.0;
+  for (int m = T - 1; m >= 0; --m) {
+    e[m] = 1.0 + tail;
+    total += e[m];
+    tail += std::min(1.0, (double)dm.K / std::max(m, 1));
+  }
+  // a part's share: at most an even share of all lists over the grid's
+  // workgroup slots (two per CU)
+  const double cap = total * dm.b * dm.hkv / (2.0 * cus);
+  int parts = 0, m = 0;
+  for (; m < T && m < kDkdvMaxSplit; ++m) {
+    const int P = (int)std::min((double)kDkdvMaxPartsPerBlock, std::ceil(e[m] / cap));
+    if (P < 2 || parts + P > kDkdvMaxParts) break;
+    sp.first[m] = (uint16_t)parts;
+    for (int p = 0; p < P; ++p) {
+      sp.part_m[parts + p] = (uint8_t)m;
+      sp.part_p[parts + p] = (uint8_t)p;
+    }
+    parts += P;
+  }
+  sp.first[m] = (uint16_t)parts;
+  sp.nsplit = m;
+  sp.nparts = parts;
+  return sp;
+}
 
 // Inner and outer gating (templated kernels).
 bool mfma_bwd_supported(const Dims& dm) {

@@ -75,11 +75,34 @@ hipError_t launch_select_long(const float* s, const float* qbar, const void* kba
 hipError_t launch_fwd_generic(const Dims& dm, const void* q, const void* k, const void* v,
                               const int32_t* idx, const float* logg, void* o, float* lse,
                               hipStream_t st);
+// Work split of the MFMA dK/dV kernel (attn_mfma_bwd.hip).  Key block m is
+// visited by the query blocks whose selection holds it, so low blocks have the
+// longest lists; when one such list alone outlasts an even share of the grid's
+// work, the key blocks m < nsplit are each taken by several workgroups
+// ("parts", contiguous shares of the list), which store fp32 partial dK, dV
+// that a small kernel sums in part order.  The plan depends only on the shape,
+// K and the device's CU count.
+constexpr int kDkdvMaxSplit = 64;   // split key blocks
+constexpr int kDkdvMaxParts = 256;  // their parts, summed (per (batch, KV head))
+constexpr int kDkdvMaxPartsPerBlock = 4;
+struct DkdvSplit {
+  int nsplit;                         // key blocks m < nsplit are split
+  int nparts;                         // parts over them
+  uint16_t first[kDkdvMaxSplit + 1];  // block m's parts are first[m] .. first[m + 1] - 1
+  uint8_t part_m[kDkdvMaxParts];      // part j covers block part_m[j] ...
+  uint8_t part_p[kDkdvMaxParts];      // ... as its share part_p[j]
+};
+bool mfma_bwd_supported(const Dims& dm);
+DkdvSplit dkdv_split_plan(const Dims& dm);
+// fp32 per part: 64 keys x 128 dims for dK and for dV
+constexpr size_t kDkdvPartFloats = 2 * 64 * 128;
+
 // Workspace layout helpers for the backward.
 struct BwdWorkspace {
   float* D;            // [b, hq, n]          dout . o per query row
   float* dlogg_part;   // [b*hkv*T, nchunk, K] per-chunk gate-gradient partials
   uint8_t* slotmap;    // [b*hkv, T (m), T (t)] Top-K slot of block m in row t, 0xFF = none
+  float* dkdv_part;    // [nparts, b, hkv, kDkdvPartFloats] split dK/dV partials (MFMA path)
   size_t slotmap_bytes;
   size_t bytes;
 };

@@ -19,7 +19,6 @@ bool mfma_fwd_supported(const Dims& dm);
 hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const int32_t* idx, const float* logg, void* o, float* lse,
                            hipStream_t st);
-bool mfma_bwd_supported(const Dims& dm);
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
                            const int32_t* idx, const float* logg, void* dq, void* dk, void* dv,
