@@ -215,6 +215,9 @@ sas_status sas_attn_fwd(const sas_shape* shape, int K, const void* q, const void
  *                     sas_select_topk.
  * o and lse are the forward's outputs.  With logg == NULL (ungated) dlogg,
  * ds, s and lse_s must be NULL.  dq/dk/dv are overwritten.
+ * The workspace size depends on the shape, K and the CU count of the current
+ * device (small grids split the longest dK/dV lists and keep fp32 partials
+ * there): query it with the device that runs the call current.
  * ---------------------------------------------------------------------- */
 size_t sas_attn_bwd_workspace_size(const sas_shape* shape, int K);
 sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void* k,
