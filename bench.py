@@ -198,8 +198,9 @@ def recorded_traffic(name, workload):
 def stream_floor():
     """Runs the stand-alone stream probe (built next to libsas.so): a plain
     read kernel over buffers rotated through 1 GiB, at the decode's stream
-    sizes, over grids of 256..4096 workgroups; prints its lines and the best
-    rate per size.  Returns the probe's exit status."""
+    sizes, over grids of 256..4096 workgroups, then the 8 x 64K decode's gather
+    pattern without its arithmetic; prints its lines, the best rate per size
+    and the gather rates.  Returns the first failing probe's exit status."""
     import subprocess
     probe = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                          "gated_block_sparse_scores_amd", "stream_probe")
@@ -217,7 +218,16 @@ def stream_floor():
         r = json.loads(line)
         if r["bytes"] not in best or r["us_per_launch"] < best[r["bytes"]]["us_per_launch"]:
             best[r["bytes"]] = r
-    print(json.dumps({"stream_floor": [best[b] for b in sorted(best)]}), flush=True)
+    # the 8 x 64K decode's gather pattern (random 16 KiB K and V blocks) against
+    # adjacent blocks through the same kernel
+    res = subprocess.run([probe, "--gather"], capture_output=True, text=True, timeout=300)
+    sys.stdout.write(res.stdout)
+    sys.stderr.write(res.stderr)
+    if res.returncode != 0:
+        return res.returncode
+    gather = [json.loads(line) for line in res.stdout.splitlines()]
+    print(json.dumps({"stream_floor": [best[b] for b in sorted(best)], "gather_floor": gather}),
+          flush=True)
     return 0
 
 
