@@ -88,7 +88,8 @@ def train_step_fn(w, x, ws, gate=0, K=None, seq_lens=None):
 def bench_gate_variants(args, w, x):
     """The same training step under each gate variant (sas_shape.gate) and under
     the dense scope (K = T - 1: every history block selected and gated); a few
-    steps each.  Outer gating runs the portable kernels."""
+    steps each, every variant through the same MFMA kernels (outer gating as
+    their OUTER instantiation)."""
     import torch
     from gated_block_sparse_scores_amd import _lib as L
     from gated_block_sparse_scores_amd import ops
