@@ -41,6 +41,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -409,22 +410,7 @@ __global__ void __launch_bounds__(DQ_NT, 2) bwd_dq_mfma_kernel(
   }
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
-  if (threadIdx.x == 0) {
-    int cnt = 0;
-    const int32_t* ir = idx + rowbk * dm.K;
-    for (int s = 0; s < dm.K; ++s) {
-      const int mm = ir[s];
-      if (mm >= 0 && mm < t) {
-        const float lg = logg ? logg[rowbk * dm.K + s] : 0.0f;
-        blist[cnt] = mm;
-        bbias[cnt] = OUTER ? expf(lg) : lg * LOG2E;  // gate (OUTER) or log2 gate
-        ++cnt;
-      }
-    }
-    blist[cnt] = t;
-    bbias[cnt] = OUTER ? 1.0f : 0.0f;
-    nblk = cnt + 1;
-  }
+  if (wave == 0) wave_block_list<OUTER>(idx, logg, rowbk, dm.K, t, lane, blist, bbias, &nblk);
 
   const size_t row = ((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qi;
   bf16x8 qf[8], of[8];
@@ -569,7 +555,7 @@ __global__ void __launch_bounds__(256) bwd_dval_kernel(const bf16_t* __restrict_
 // The dQ kernel's second stream and its fork / join events, one set per
 // device for the whole process (created on first use, default priority, never
 // destroyed).  Callers on different threads share it: a backward holds `mu`
-// while it enqueues its fork, its two kernels and its join, so the events
+// while it enqueues its fork, its kernels and its join, so the events
 // always order the right pair of streams; the dQ kernels of concurrent
 // backwards then run one after another on the side stream.
 struct SideStream {
@@ -694,41 +680,51 @@ bool mfma_bwd_supported(const Dims& dm) {
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
                            const int32_t* idx, const float* logg, void* dq, void* dk, void* dv,
-                           const BwdWorkspace& ws, int* nchunk_out, hipStream_t st) {
-  // dlogg is written whole by the dK/dV kernel (one partial per row).
-  *nchunk_out = 1;
+                           const BwdWorkspace& ws, const std::function<hipError_t()>& tail,
+                           hipStream_t st) {
   // When the dK/dV grid is at most two rounds of its two-per-CU occupancy, its
-  // last workgroups (the longest inverse lists) leave CUs idle: D is then
-  // formed by a small kernel and dQ runs beside dK/dV on a second stream.
-  // Larger grids have no such tail and run dQ (which forms D) first.
+  // last workgroups (the longest inverse lists) leave CUs idle: dQ then runs
+  // beside dK/dV on a second stream.  Larger grids have no such tail and run
+  // dQ (which forms D) first.
   SideStream* ss = nullptr;
   const size_t dkdv_wgs = (size_t)dm.b * dm.hkv * dm.T;
   if (!dm.seq_lens) {
     ss = side_stream();
     if (ss && dkdv_wgs > (size_t)4 * ss->cus) ss = nullptr;
   }
+  hipError_t e;
   if (!ss) {
+    if ((e = launch_bwd_prep(dm, o, dout, idx, ws, false, st)) != hipSuccess) return e;
     launch_dq(dm, q, k, v, o, dout, lse, ws.D, nullptr, idx, logg, dq, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return tail();
   }
   const size_t rows = (size_t)dm.b * dm.hq * dm.n;
+  // The side stream forks before anything of the backward: dQ needs none of
+  // its intermediates (it forms D from o with the same sums as bwd_dval_kernel
+  // and stores none), so it starts at once while the slot map, D and dK/dV
+  // follow on st.  The selector gradient needs only dK/dV's dlogg and runs on
+  // st before the join; dQ is the longer of the two, so the join comes last.
+  // (Measured at 8K against forking after D and joining before the selector
+  // gradient: 1.170 against 1.187 ms per training step, bitwise the same.)
+  std::lock_guard<std::mutex> lk(ss->mu);
+  if ((e = hipEventRecord(ss->fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+  launch_dq(dm, q, k, v, o, dout, lse, nullptr, nullptr, idx, logg, dq, ss->s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+  if ((e = launch_bwd_prep(dm, o, dout, idx, ws, false, st)) != hipSuccess) return e;
   {
     ProfScope ps("bwd_dot", st);
     hipLaunchKernelGGL(bwd_dval_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
                        (const bf16_t*)o, (const bf16_t*)dout, ws.D, rows);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(ss->mu);
-  if ((e = hipEventRecord(ss->fork, st)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
-  launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
-  launch_dq(dm, q, k, v, o, dout, lse, nullptr, ws.D, idx, logg, dq, ss->s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+  launch_dkdv(dm, q, k, v, dout, lse, logg, ws, dk, dv, st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tail()) != hipSuccess) return e;
   return hipStreamWaitEvent(st, ss->join, 0);
 }
 

@@ -125,22 +125,7 @@ __global__ void __launch_bounds__(64 * NW, 2) fwd_mfma_kernel(
   }
 
   const size_t rowbk = ((size_t)b * dm.hkv + kv) * dm.T + t;
-  if (threadIdx.x == 0) {
-    int cnt = 0;
-    const int32_t* ir = idx + rowbk * dm.K;
-    for (int s = 0; s < dm.K; ++s) {
-      const int m = ir[s];
-      if (m >= 0 && m < t) {
-        const float lg = logg ? logg[rowbk * dm.K + s] : 0.0f;
-        blist[cnt] = m;
-        bbias[cnt] = OUTER ? expf(lg) : lg * LOG2E;
-        ++cnt;
-      }
-    }
-    blist[cnt] = t;
-    bbias[cnt] = OUTER ? 1.0f : 0.0f;
-    nblk = cnt + 1;
-  }
+  if (wave == 0) wave_block_list<OUTER>(idx, logg, rowbk, dm.K, t, lane, blist, bbias, &nblk);
 
   // Q^T fragments (B operand): query qt*32 + c, dims kc*16 + g*8 .. +8.
   const bf16_t* qrow = q + (((size_t)b * dm.hq + h) * dm.n + (size_t)t * BS + qt * 32) * D;

@@ -141,4 +141,38 @@ __device__ __forceinline__ void tile_copy_lds(bf16_t* tile, const bf16_t* __rest
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// The attended blocks of query block t of selection row `rowbk`: the valid
+// history blocks of its selection (0 <= m < t) in slot order, then t itself,
+// each with its bias, the log2 gate (inner gating) or the gate (OUTER).  Called
+// by one whole wave: lane s takes slot s0 + s of each pass of 64 slots, and the
+// valid entries are placed with a ballot's prefix counts (all of a pass's
+// loads in flight at once, instead of one thread reading the slots in turn).
+template <bool OUTER>
+__device__ __forceinline__ void wave_block_list(const int32_t* __restrict__ idx,
+                                                const float* __restrict__ logg, size_t rowbk,
+                                                int K, int t, int lane, int* blist, float* bbias,
+                                                int* nblk) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int32_t* ir = idx + rowbk * K;
+  int cnt = 0;
+  for (int s0 = 0; s0 < K; s0 += 64) {
+    const int s = s0 + lane;
+    const int m = s < K ? ir[s] : -1;
+    const bool ok = m >= 0 && m < t;
+    const float lg = (ok && logg) ? logg[rowbk * K + s] : 0.0f;
+    const unsigned long long bal = __ballot(ok);
+    if (ok) {
+      const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      blist[pos] = m;
+      bbias[pos] = OUTER ? expf(lg) : lg * kLog2e;
+    }
+    cnt += __popcll(bal);
+  }
+  if (lane == 0) {
+    blist[cnt] = t;
+    bbias[cnt] = OUTER ? 1.0f : 0.0f;
+    *nblk = cnt + 1;
+  }
+}
+
 }  // namespace sas

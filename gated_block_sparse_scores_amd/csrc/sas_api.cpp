@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <functional>
 #include <map>
 #include <mutex>
 #include <string>
@@ -19,10 +20,13 @@ bool mfma_fwd_supported(const Dims& dm);
 hipError_t launch_fwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const int32_t* idx, const float* logg, void* o, float* lse,
                            hipStream_t st);
+// Slot map, D, dQ and dK/dV; `tail` enqueues the work that needs only dK/dV's
+// outputs (the selector gradient) on st before the backward joins its streams.
 hipError_t launch_bwd_mfma(const Dims& dm, const void* q, const void* k, const void* v,
                            const void* o, const void* dout, const float* lse,
                            const int32_t* idx, const float* logg, void* dq, void* dk, void* dv,
-                           const BwdWorkspace& ws, int* nchunk_out, hipStream_t st);
+                           const BwdWorkspace& ws, const std::function<hipError_t()>& tail,
+                           hipStream_t st);
 }  // namespace sas
 
 namespace {
@@ -296,14 +300,19 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
   const hipStream_t st = (hipStream_t)stream;
   const bool mfma = sas::mfma_bwd_supported(dm);
   const float* lg = dm.ste ? nullptr : logg;  // hard gating: the attention is ungated
-  SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, !mfma, st));
+  if (mfma) {
+    // dlogg is written whole by the dK/dV kernel (one partial per row)
+    const auto tail = [&]() -> hipError_t {
+      return (dlogg || ds) ? sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, 1, dlogg, ds, st)
+                           : hipSuccess;
+    };
+    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, lg, dq, dk, dv, ws, tail, st));
+    return SAS_OK;
+  }
+  SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, true, st));
   int nchunk = 0;
-  if (mfma)
-    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, lg, dq, dk, dv, ws,
-                                    &nchunk, st));
-  else
-    SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, lg, dq, dk, dv, ws,
-                                       &nchunk, st));
+  SAS_LAUNCH(sas::launch_bwd_generic(dm, q, k, v, dout, lse, idx, lg, dq, dk, dv, ws, &nchunk,
+                                     st));
   if (dlogg || ds)
     SAS_LAUNCH(sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, nchunk, dlogg, ds, st));
   return SAS_OK;
