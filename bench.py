@@ -159,7 +159,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv_mfma": ["attn_mfma_bwd.hip", "mfma.h", "common.h", "internal.h"],
     "bwd_dq_mfma": ["attn_mfma_bwd.hip", "mfma.h", "common.h", "internal.h"],
     "fwd_mfma": ["attn_mfma_fwd.hip", "mfma.h", "common.h", "internal.h"],
-    "decode_split": ["decode.hip", "mfma.h", "common.h", "internal.h"],
+    "decode_split": ["decode.hip", "common.h", "internal.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
