@@ -46,6 +46,24 @@ def max_abs(a, b):
     return float(np.max(np.abs(a - b)))
 
 
+def block_err(got, ref, rms):
+    """L2 error of one sampled block over the larger of its own norm and the
+    RMS norm of that quantity's sampled blocks: a dlogg row (or ds row) can be
+    a near-zero sum of cancelling terms, whose own norm says nothing about the
+    size of the rounding it carries."""
+    got, ref = _arr(got), _arr(ref)
+    return float(np.sqrt(np.sum((got - ref) ** 2)) / max(np.sqrt(np.sum(ref ** 2)), rms))
+
+
+def worst_block_errs(rows):
+    """{name: [(got, ref), ...]} -> {name: largest block_err over its blocks}."""
+    out = {}
+    for name, pairs in rows.items():
+        rms = float(np.sqrt(sum(float(np.sum(_arr(r_) ** 2)) for _, r_ in pairs) / len(pairs)))
+        out[name] = max(block_err(got, ref, rms) for got, ref in pairs)
+    return out
+
+
 def tols(dtype):
     return (ATOL_F32, REL_F32) if dtype == torch.float32 else (ATOL_BF16, REL_BF16)
 

@@ -3,7 +3,6 @@ activations, outer gating, straight-through hard gating) against the oracle:
 selection, forward, backward (dq, dk, dv, dlogg, ds), decode and the fused
 decode step, on the portable fp32 kernels and the bf16 MFMA shapes, and
 sampled blocks of the 8K-token workload."""
-import math
 
 import numpy as np
 import pytest
@@ -11,7 +10,7 @@ import torch
 
 import synth
 from oracle import sas_oracle as O
-from tests._gpu_helpers import GATE_ATOL, max_abs, np64, rel_l2, say, tols
+from tests._gpu_helpers import GATE_ATOL, max_abs, np64, rel_l2, say, tols, worst_block_errs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -170,10 +169,6 @@ def test_dense_scope(shape):
         assert v_ <= rtol, k_
 
 
-def _block_err(got, ref, rms):
-    return float(np.sqrt(np.sum((got - ref) ** 2)) / max(np.sqrt(np.sum(ref ** 2)), rms))
-
-
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("variant", [("sigmoid", True, False, 31), ("softmax", False, True, 31),
                                      ("raw", False, False, 31), ("softmax", False, False, 127)],
@@ -237,10 +232,7 @@ def test_gate_variant_at_the_8k_workload(variant):
         lo, hi = O.block_span(m, w.block, w.seqlen)
         rows["dk"].append((np64(dk_c[0, kv, lo:hi]), dkb))
         rows["dv"].append((np64(dv_c[0, kv, lo:hi]), dvb))
-    errs = {}
-    for name, pairs in rows.items():
-        rms = math.sqrt(sum(float(np.sum(r_ ** 2)) for _, r_ in pairs) / len(pairs))
-        errs[name] = max(_block_err(got, ref, rms) for got, ref in pairs)
+    errs = worst_block_errs(rows)
     say(f"  o {eo:.2e} lse {el:.2e} " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
     assert eo <= 2e-2 and el <= 2e-2
     for name, e in errs.items():

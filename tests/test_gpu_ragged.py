@@ -8,7 +8,7 @@ import torch
 
 import synth
 from oracle import sas_oracle as O
-from tests._gpu_helpers import GATE_ATOL, max_abs, rel_l2, say, tols
+from tests._gpu_helpers import GATE_ATOL, max_abs, rel_l2, say, tols, worst_block_errs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -215,7 +215,8 @@ def test_ragged_batch_of_the_benchmark():
     o_c, lse_c, dq_c = o.cpu(), lse.cpu(), gr["dq"].cpu()
     dl_c, ds_c = gr["dlogg"].cpu().numpy(), gr["ds"].cpu().numpy()
     dk_c, dv_c = gr["dk"].cpu(), gr["dv"].cpu()
-    worst = {}
+    worst = {"o": 0.0, "lse": 0.0}
+    rows = {k_: [] for k_ in ("dq", "dlogg", "ds", "dk", "dv")}
     for bb, nb in enumerate(lens):
         Tb = O.n_blocks(nb, bs)
         xb = {k_: x[k_][bb:bb + 1, :, :nb] for k_ in ("q", "k", "v", "dout")}
@@ -238,19 +239,22 @@ def test_ragged_batch_of_the_benchmark():
                 dqb, dlb, _ = O.bwd_row_block(xb["q"], xb["k"], xb["v"], xb["dout"], oi, ol, bs,
                                               scale, 0, kv, t)
                 dsr = O.ds_row(s_c[bb, kv, t, :t], ols[0, kv, t], oi[0, kv, t], dlb)
-                e = {"o": max_abs(o_c[bb, hs, lo:hi], ob), "lse": max_abs(lse_c[bb, hs, lo:hi], lb),
-                     "dq": rel_l2(dq_c[bb, hs, lo:hi], dqb),
-                     "dlogg": max_abs(dl_c[bb, kv, t], dlb) / max(np.abs(dlb).max(), 1e-3),
-                     "ds": max_abs(ds_c[bb, kv, t, :t], dsr) / max(np.abs(dsr).max(), 1e-3)}
-                for k_, v_ in e.items():
-                    worst[k_] = max(worst.get(k_, 0.0), v_)
+                worst["o"] = max(worst["o"], max_abs(o_c[bb, hs, lo:hi], ob))
+                worst["lse"] = max(worst["lse"], max_abs(lse_c[bb, hs, lo:hi], lb))
+                rows["dq"].append((dq_c[bb, hs, lo:hi], dqb))
+                rows["dlogg"].append((dl_c[bb, kv, t], dlb))
+                rows["ds"].append((ds_c[bb, kv, t, :t], dsr))
             counts = np.bincount(oi[0, kv][oi[0, kv] >= 0], minlength=Tb)
             m = int(np.argmax(counts))
             dkb, dvb = O.bwd_key_block(xb["q"], xb["k"], xb["v"], xb["dout"], oi, ol, bs, scale,
                                        0, kv, m)
             lo, hi = O.block_span(m, bs, nb)
-            worst["dk"] = max(worst.get("dk", 0.0), rel_l2(dk_c[bb, kv, lo:hi], dkb))
-            worst["dv"] = max(worst.get("dv", 0.0), rel_l2(dv_c[bb, kv, lo:hi], dvb))
+            rows["dk"].append((dk_c[bb, kv, lo:hi], dkb))
+            rows["dv"].append((dv_c[bb, kv, lo:hi], dvb))
+    # gradients: relative L2 per sampled block, over the larger of the block's
+    # own norm and the RMS block norm (a one-block dlogg row can be a near-zero
+    # sum of cancelling terms)
+    worst.update(worst_block_errs(rows))
     say("  worst: " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in worst.items()))
     assert worst["o"] <= 2e-2 and worst["lse"] <= 2e-2
     for k_ in ("dq", "dlogg", "ds", "dk", "dv"):
