@@ -5,6 +5,8 @@
 // evolve.pub review FAQ (pooling-based block summaries feed the selector).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -161,10 +163,13 @@ template <> struct Slice8<float> {
 // and the first (K - #above) keys equal to v in ascending block order (the
 // "equal score -> lower block index" rule) are written in ascending block
 // order from wave prefix sums.  No workgroup barrier.
+// PER >= ceil(C_t / 64) keys per lane (the register arrays and every ballot
+// pass are sized by it).
+template <int PER>
 __device__ __forceinline__ void wave_select_row(const float* src, int ct, int K, int act,
                                                 int32_t* __restrict__ irow,
                                                 float* __restrict__ lrow, float* lse_out) {
-  constexpr int PER = kLongHistory / 64;
+  static_assert(PER * 64 <= kLongHistory, "row longer than the one-wave select");
   const int lane = threadIdx.x & 63;
   const int ch = (ct + 63) >> 6;
   const int mb = lane * ch;
@@ -240,6 +245,7 @@ __device__ __forceinline__ void wave_select_row(const float* src, int ct, int K,
 }
 
 // Given scores: one wave per row, four rows per workgroup.
+template <int PER>
 __global__ void __launch_bounds__(256) topk_given_kernel(const float* __restrict__ s,
                                                          size_t rows, int T, int C,
                                                          int row_offset, int K, int act,
@@ -249,15 +255,15 @@ __global__ void __launch_bounds__(256) topk_given_kernel(const float* __restrict
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // the whole wave
   const int ct = row_history((int)(row % T), row_offset, C, rl, row / T);
-  wave_select_row(s + row * (size_t)C, ct, K, act, idx + row * (size_t)K, logg + row * (size_t)K,
-                  lse_s + row);
+  wave_select_row<PER>(s + row * (size_t)C, ct, K, act, idx + row * (size_t)K,
+                       logg + row * (size_t)K, lse_s + row);
 }
 
 // Stand-in scores: one 256-thread workgroup per row forms
 // s[m] = fp32((qbar . kbar[m]) * scale), the dot product in fp64 with 16 lanes
 // per key-block summary (8 consecutive dims each, reduced with DPP), into LDS
 // and s_out (0 past the row's history); then wave 0 selects.
-template <typename Tk>
+template <typename Tk, int PER>
 __global__ void __launch_bounds__(256) topk_standin_kernel(
     const float* __restrict__ qbar, const Tk* __restrict__ kbar, int kbar_ld, int d,
     double scale, float* __restrict__ s_out, int T, int C, int row_offset, int K, int act,
@@ -277,18 +283,20 @@ __global__ void __launch_bounds__(256) topk_standin_kernel(
   }
   const Tk* kb = kbar + (row / T) * (size_t)kbar_ld * d + (lane_on ? sub * 8 : 0);
   float* orow = s_out + row * (size_t)C;
-  // sixteen blocks per round (one per 16-lane group), the loads of four rounds
+  // sixteen blocks per round (one per 16-lane group), the loads of RB rounds
   // issued before their products (the DPP reductions keep the compiler from
-  // unrolling a loop with a run-time trip count itself)
-  for (int m0 = 0; m0 < C; m0 += 64) {
-    Slice8<Tk> ks[4];
+  // unrolling a loop with a run-time trip count itself); rows of at most 128
+  // blocks issue all their loads at once
+  constexpr int RB = PER <= 2 ? 8 : 4;
+  for (int m0 = 0; m0 < C; m0 += 16 * RB) {
+    Slice8<Tk> ks[RB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RB; ++u) {
       const int m = m0 + 16 * u + grp;
       if (m < ct && lane_on) ks[u].load(kb + (size_t)m * d);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RB; ++u) {
       const int m = m0 + 16 * u + grp;
       double acc = 0.0;
       if (m < ct && lane_on) {
@@ -305,7 +313,8 @@ __global__ void __launch_bounds__(256) topk_standin_kernel(
   }
   __syncthreads();
   if (tid < 64)
-    wave_select_row(sv, ct, K, act, idx + row * (size_t)K, logg + row * (size_t)K, lse_s + row);
+    wave_select_row<PER>(sv, ct, K, act, idx + row * (size_t)K, logg + row * (size_t)K,
+                         lse_s + row);
 }
 
 // ---------------------------------------------------------------- long histories: two stages
@@ -588,17 +597,27 @@ hipError_t launch_topk(const float* s, const float* qbar, const void* kbar, bool
                        float* lse_s, hipStream_t st, const RowLens& rl) {
   const size_t rows = (size_t)rows_bk * T;
   ProfScope ps("topk", st);
-  if (s)
-    hipLaunchKernelGGL(topk_given_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, s,
-                       rows, T, C, row_offset, K, act, idx, logg, lse_s, rl);
-  else if (kbar_bf16)
-    hipLaunchKernelGGL(topk_standin_kernel<bf16_t>, dim3((unsigned)rows), dim3(256), 0, st, qbar,
-                       (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C, row_offset, K, act,
-                       idx, logg, lse_s, rl);
+  // keys per lane sized to the longest row (C <= kLongHistory here)
+  auto go = [&](auto per) {
+    constexpr int PER = decltype(per)::value;
+    if (s)
+      hipLaunchKernelGGL((topk_given_kernel<PER>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                         0, st, s, rows, T, C, row_offset, K, act, idx, logg, lse_s, rl);
+    else if (kbar_bf16)
+      hipLaunchKernelGGL((topk_standin_kernel<bf16_t, PER>), dim3((unsigned)rows), dim3(256), 0,
+                         st, qbar, (const bf16_t*)kbar, kbar_ld, d, scale, s_out, T, C,
+                         row_offset, K, act, idx, logg, lse_s, rl);
+    else
+      hipLaunchKernelGGL((topk_standin_kernel<float, PER>), dim3((unsigned)rows), dim3(256), 0,
+                         st, qbar, (const float*)kbar, kbar_ld, d, scale, s_out, T, C,
+                         row_offset, K, act, idx, logg, lse_s, rl);
+  };
+  if (C <= 128)
+    go(std::integral_constant<int, 2>());
+  else if (C <= 256)
+    go(std::integral_constant<int, 4>());
   else
-    hipLaunchKernelGGL(topk_standin_kernel<float>, dim3((unsigned)rows), dim3(256), 0, st, qbar,
-                       (const float*)kbar, kbar_ld, d, scale, s_out, T, C, row_offset, K, act,
-                       idx, logg, lse_s, rl);
+    go(std::integral_constant<int, kLongHistory / 64>());
   return hipGetLastError();
 }
 
