@@ -303,10 +303,11 @@ sas_status sas_attn_bwd(const sas_shape* shape, int K, const void* q, const void
   if (mfma) {
     // dlogg is written whole by the dK/dV kernel (one partial per row)
     const auto tail = [&]() -> hipError_t {
-      return (dlogg || ds) ? sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, 1, dlogg, ds, st)
-                           : hipSuccess;
+      if (!dlogg && !ds) return hipSuccess;
+      return sas::launch_bwd_ds(dm, idx, s, lse_s, ws.dlogg_part, 1, dlogg, ds, st);
     };
-    SAS_LAUNCH(sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, lg, dq, dk, dv, ws, tail, st));
+    SAS_LAUNCH(
+        sas::launch_bwd_mfma(dm, q, k, v, o, dout, lse, idx, lg, dq, dk, dv, ws, tail, st));
     return SAS_OK;
   }
   SAS_LAUNCH(sas::launch_bwd_prep(dm, o, dout, idx, ws, true, st));
